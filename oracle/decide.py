@@ -1,0 +1,133 @@
+"""Per-position decision rules and the accepted prefix per candidate (oracle).
+
+Test infrastructure: see the package docstring for who may import this.
+
+Decision codes: 0 NONE (row not decided), 1 KEEP, 2 REPLACE, 3 REMASK.
+Rule codes: 0 TRUST, 1 KL, 2 CONF, 3 KL_OR_CONF, 4 COVER, 5 COUPLED_ACCEPT.
+
+Sources and readings:
+
+* TRUST, [DualDiffusion] §2 "Verification algorithms" item 1: every drafted
+  token is accepted unchanged -> KEEP.
+* KL, item 2: a token is remasked when KL(p_v || p_d) exceeds tau. The page
+  also mentions remasking when the divergence is "probabilistically" high;
+  that clause is not specified and is not part of this rule. REMASK iff
+  kl > tau (strict), else KEEP.
+* CONF, item 3: low verifier confidence leads to remasking. REMASK iff
+  conf < theta, else KEEP.
+* KL_OR_CONF: REMASK iff either of the two conditions holds.
+* COVER, [COVER] §3 "Adaptive revision outcomes": when the re-predicted token
+  equals the current assignment the token is kept; when it differs and the
+  verifier is confident it is replaced in place; it is remasked only when it
+  is uncertain and likely wrong. Reading: re-predicted token = tok_v (the
+  verifier's token; equal to argmax_v at T = 0); KEEP if tok_v == current;
+  else REPLACE (with tok_v) if conf >= theta; else REMASK.
+* COUPLED_ACCEPT, [SPOT] §1/§3 coupled-noise verification of candidate block
+  states: a drafted token is accepted when the target, under the shared
+  noise, draws the same token. Rows are grouped into candidates of
+  ``group_len`` consecutive rows, in the candidate's commit order. Reading:
+  the accepted prefix of a candidate is the number of leading decided rows
+  whose tokens agree; the first disagreeing row takes the target's own token
+  (REPLACE with tok_v, a valid draw of the target given the accepted
+  prefix); decided rows after it are REMASKed.
+
+"Current token" is ``cur_tok`` when given, else the drafter's token tok_d.
+Rows with subject == 0 are not decided: NONE, and their output token is the
+current token. REMASKed rows output ``mask_token``; REPLACEd rows output
+tok_v; KEEP rows output the current token.
+
+Accepted prefix of group c (any rule): the offset of the first decided row
+in the group whose decision is not KEEP, or group_len if there is none.
+Best group: the largest prefix, lowest group index on ties.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+NONE, KEEP, REPLACE, REMASK = 0, 1, 2, 3
+TRUST, KL, CONF, KL_OR_CONF, COVER, COUPLED_ACCEPT = 0, 1, 2, 3, 4, 5
+
+__all__ = ["NONE", "KEEP", "REPLACE", "REMASK", "TRUST", "KL", "CONF", "KL_OR_CONF",
+           "COVER", "COUPLED_ACCEPT", "decide", "accepted_prefix", "best_group"]
+
+
+def decide(rule: int, stats: dict, *, tau_kl: float = 0.0, conf_thr: float = 0.0,
+           mask_token: int = -1, subject=None, cur_tok=None, group_len: int = 0):
+    """Apply ``rule`` to every row. Returns (decision uint8, out_tok int32).
+
+    ``stats`` holds the row statistics needed by the rule (kl, conf, tok_v,
+    tok_d), as float64 / int arrays of length R.
+    """
+    rule = int(rule)
+    cur = np.asarray(stats["tok_d"] if cur_tok is None else cur_tok).astype(np.int32)
+    n = cur.shape[0]
+    subj = np.ones(n, bool) if subject is None else (np.asarray(subject) != 0)
+    dec = np.full(n, NONE, np.uint8)
+    if rule == TRUST:
+        dec[subj] = KEEP
+    elif rule in (KL, CONF, KL_OR_CONF):
+        remask = np.zeros(n, bool)
+        if rule in (KL, KL_OR_CONF):
+            remask |= np.asarray(stats["kl"], dtype=np.float64) > tau_kl
+        if rule in (CONF, KL_OR_CONF):
+            remask |= np.asarray(stats["conf"], dtype=np.float64) < conf_thr
+        dec[subj] = np.where(remask[subj], REMASK, KEEP)
+    elif rule == COVER:
+        tok_v = np.asarray(stats["tok_v"]).astype(np.int32)
+        conf = np.asarray(stats["conf"], dtype=np.float64)
+        d = np.where(tok_v == cur, KEEP, np.where(conf >= conf_thr, REPLACE, REMASK))
+        dec[subj] = d[subj]
+    elif rule == COUPLED_ACCEPT:
+        if group_len <= 0 or n % group_len:
+            raise ValueError("COUPLED_ACCEPT needs group_len > 0 dividing the row count")
+        tok_v = np.asarray(stats["tok_v"]).astype(np.int32)
+        agree = tok_v == cur
+        for c in range(n // group_len):
+            rejected = False
+            for j in range(group_len):
+                r = c * group_len + j
+                if not subj[r]:
+                    continue
+                if rejected:
+                    dec[r] = REMASK
+                elif agree[r]:
+                    dec[r] = KEEP
+                else:
+                    dec[r] = REPLACE
+                    rejected = True
+    else:
+        raise ValueError(f"unknown rule {rule}")
+    out = cur.copy()
+    tok_v = stats.get("tok_v")
+    if (dec == REPLACE).any():
+        out[dec == REPLACE] = np.asarray(tok_v).astype(np.int32)[dec == REPLACE]
+    out[dec == REMASK] = np.int32(mask_token)
+    return dec, out
+
+
+def accepted_prefix(decision, group_len: int, subject=None) -> np.ndarray:
+    """Per group: offset of the first decided, non-KEEP row (group_len if none)."""
+    decision = np.asarray(decision)
+    n = decision.shape[0]
+    if group_len <= 0 or n % group_len:
+        raise ValueError("group_len must be positive and divide the row count")
+    subj = np.ones(n, bool) if subject is None else (np.asarray(subject) != 0)
+    out = np.empty(n // group_len, np.int32)
+    for c in range(n // group_len):
+        p = group_len
+        for j in range(group_len):
+            r = c * group_len + j
+            if subj[r] and decision[r] != KEEP:
+                p = j
+                break
+        out[c] = p
+    return out
+
+
+def best_group(prefix) -> int:
+    """Group with the longest accepted prefix; lowest index on ties (-1 if none)."""
+    prefix = np.asarray(prefix)
+    if prefix.size == 0:
+        return -1
+    return int(np.argmax(prefix))

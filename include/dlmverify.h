@@ -1,0 +1,226 @@
+/*
+ * libdlmverify: the per-position verification pass of masked diffusion
+ * language-model decoding, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   [DualDiffusion] "DualDiffusion: A Speculative Decoding Strategy for Masked
+ *       Diffusion Models" (gist.science summary of arXiv 2604.05250).
+ *   [SPOT] "On the SPOT: Enhancing Speculative Decoding for Diffusion Language
+ *       Models via Commit-Order Prediction" (paper review, blog.secrett2633.cloud).
+ *   [COVER] "Stop the Flip-Flop: Context-Preserving Verification for Fast
+ *       Revocable Diffusion Decoding" (gist.science summary of arXiv 2602.06161).
+ *
+ * Conventions shared by every call:
+ *   - Every array pointer is a caller-owned DEVICE pointer (hipMalloc'd or a
+ *     torch tensor's data_ptr()). The library allocates nothing and keeps no
+ *     state between calls; scratch memory, where a call needs it, is passed in.
+ *   - Calls validate their arguments on the host first. An invalid argument
+ *     returns a status != DV_OK synchronously, before any HIP call, with no
+ *     side effect. Valid calls enqueue kernels on `stream` and return without
+ *     waiting: inputs must stay alive and outputs are valid only once the
+ *     stream has reached that point. A launch failure returns DV_ERR_HIP.
+ *   - dv_last_error() gives a message for the last failing call of the calling
+ *     thread. Nothing throws across this interface and nothing aborts.
+ *   - Rows are independent; indices are int32, so rows and vocab are < 2^31.
+ *   - Calls on one stream run in order; calls on different streams that share
+ *     output buffers race, as with any kernel.
+ */
+#ifndef DLMVERIFY_H
+#define DLMVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DV_VERSION 1
+
+typedef enum dv_status {
+  DV_OK = 0,
+  DV_ERR_NULL = 1,        /* a required pointer is NULL */
+  DV_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  DV_ERR_DTYPE = 3,       /* unknown element type */
+  DV_ERR_ALIGN = 4,       /* a pointer or row pitch is not 16-byte aligned */
+  DV_ERR_ARG = 5,         /* a scalar argument is out of range (T, tau, theta, k, rule, ...) */
+  DV_ERR_WORKSPACE = 6,   /* workspace missing or too small */
+  DV_ERR_UNSUPPORTED = 7, /* valid request this build cannot serve (e.g. seq_len too long) */
+  DV_ERR_HIP = 8          /* a HIP launch or runtime call failed */
+} dv_status;
+
+typedef enum dv_dtype { DV_FP32 = 0, DV_BF16 = 1 } dv_dtype;
+
+/* Decision codes written by dv_decide. */
+typedef enum dv_decision { DV_NONE = 0, DV_KEEP = 1, DV_REPLACE = 2, DV_REMASK = 3 } dv_decision;
+
+/* Verifier and drafter logits of `rows` positions over a vocabulary of `vocab`.
+ * Layout: row-major [rows][ld] elements of `dtype` (fp32 values or bfloat16
+ * bit patterns); element (r, i) sits at base + r*ld + i, and each buffer spans
+ * rows*ld elements. Only the first `vocab` entries of a row are read as
+ * logits; the padding up to the next 16-byte boundary is read and ignored.
+ * Requirements: both base pointers 16-byte aligned, ld*elt a multiple of 16,
+ * vocab <= ld, all logits finite. */
+typedef struct dv_logits {
+  const void *verifier;
+  const void *drafter;
+  int32_t dtype;   /* dv_dtype */
+  int32_t reserved;
+  int64_t rows;
+  int64_t vocab;
+  int64_t ld;
+} dv_logits;
+
+/* Shared Gumbel noise ([SPOT] §1 and §3, coupled-noise verification): at
+ * temperature > 0 both models draw token argmax_i(x_i / T + g_i) with the SAME
+ * standard Gumbel g_i, which depends only on (seed, position, vocabulary index).
+ * temperature == 0 means greedy decoding (token = argmax, no noise).
+ * Position of row r: pos[r] when pos != NULL (device int32 [rows]); else
+ * r % pos_period when pos_period > 0; else r. Rows with equal positions see
+ * equal noise (e.g. the candidates of one tree level). */
+typedef struct dv_noise {
+  float temperature;
+  int32_t reserved;
+  uint64_t seed;
+  const int32_t *pos;
+  int64_t pos_period;
+} dv_noise;
+
+/* Per-row statistics, structure of arrays of length rows (device). Any member
+ * may be NULL to skip that output. Definitions ([DualDiffusion] §2,
+ * "Verification algorithms" items 2-3; [COVER] §2, uncertainty u):
+ *   lse_v, lse_d   log sum_i exp(x_i) of the verifier / drafter logits
+ *   kl             KL(p_verifier || p_drafter), nats
+ *   entropy        -sum_i p_v,i ln p_v,i, nats
+ *   conf           max_i p_v,i
+ *   argmax_v/_d    lowest index of the row maximum
+ *   tok_v/_d       Gumbel-max token under the shared noise (argmax at T = 0) */
+typedef struct dv_row_stats {
+  float *lse_v;
+  float *lse_d;
+  float *kl;
+  float *entropy;
+  float *conf;
+  int32_t *argmax_v;
+  int32_t *argmax_d;
+  int32_t *tok_v;
+  int32_t *tok_d;
+} dv_row_stats;
+
+/* Optional launch-shape override for dv_verify_rows (NULL = automatic). A
+ * zero field keeps its automatic value. Results do not depend on it beyond
+ * float rounding: integer outputs are identical for every shape.
+ *   split         vocabulary slices per row (1..64)
+ *   block         threads per workgroup of the shared-noise kernel (256 or
+ *                 512; the per-row kernel always uses 256)
+ *   shared_noise  1: compute the noise once per (position, slice) in LDS and
+ *                 reuse it for every row at that position (needs pos == NULL
+ *                 and pos_period > 0); 0: compute it per row; -1: automatic */
+typedef struct dv_tuning {
+  int32_t split;
+  int32_t block;
+  int32_t shared_noise;
+  int32_t reserved;
+} dv_tuning;
+
+/* Bytes of device workspace dv_verify_rows needs for these arguments (may be
+ * 0). Validates like dv_verify_rows does, but does not look at pointers. */
+dv_status dv_verify_workspace_bytes(const dv_logits *logits, const dv_noise *noise,
+                                    const dv_tuning *tuning, size_t *bytes);
+
+/* One fused pass over both logit matrices ([DualDiffusion] §2 "Core process":
+ * the verifier's distributions are compared with the drafter's predictions;
+ * [SPOT] §3: all candidate states are verified in one batched pass). Writes
+ * the non-NULL members of `out`. `workspace` (device, 256-byte aligned) must
+ * hold dv_verify_workspace_bytes() bytes; it may be NULL when that is 0.
+ * Errors: DV_ERR_NULL (logits, noise or out NULL; verifier/drafter NULL),
+ * DV_ERR_SHAPE (rows < 0, vocab < 1, vocab > ld, sizes >= 2^31, pos_period < 0),
+ * DV_ERR_DTYPE, DV_ERR_ALIGN, DV_ERR_ARG (temperature < 0 or not finite, bad
+ * tuning), DV_ERR_WORKSPACE, DV_ERR_HIP. rows == 0 is a no-op. */
+dv_status dv_verify_rows(const dv_logits *logits, const dv_noise *noise, const dv_tuning *tuning,
+                         const dv_row_stats *out, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+typedef enum dv_rule {
+  DV_RULE_TRUST = 0,          /* [DualDiffusion] §2 verification item 1: accept all */
+  DV_RULE_KL = 1,             /* item 2: REMASK iff kl > tau_kl */
+  DV_RULE_CONF = 2,           /* item 3: REMASK iff conf < conf_thr */
+  DV_RULE_KL_OR_CONF = 3,     /* REMASK iff either holds */
+  DV_RULE_COVER = 4,          /* [COVER] §3: KEEP if tok_v == current; else REPLACE if
+                                 conf >= conf_thr; else REMASK */
+  DV_RULE_COUPLED_ACCEPT = 5  /* [SPOT] §1/§3: per candidate of group_len rows, KEEP the
+                                 leading rows whose tok_v equals the current token,
+                                 REPLACE the first disagreeing row with tok_v, REMASK
+                                 the rows after it */
+} dv_rule;
+
+typedef struct dv_decide_args {
+  int32_t rule;        /* dv_rule */
+  float tau_kl;        /* finite */
+  float conf_thr;      /* finite */
+  int32_t mask_token;  /* token id written for REMASK rows ([COVER] problem statement:
+                          a remasked position holds [MASK]) */
+  int64_t rows;
+  int64_t group_len;   /* rows per candidate (consecutive rows, commit order); 0 = none.
+                          Required (> 0, dividing rows) for COUPLED_ACCEPT and for
+                          prefix_len / best_group. */
+} dv_decide_args;
+
+/* Per-position decision ([DualDiffusion] §2 verification items 1-3;
+ * [COVER] §3 adaptive revision outcomes; [SPOT] §1/§3 coupled-noise check).
+ * Reads from `stats` only the members the rule needs (kl; conf; tok_v), plus
+ * tok_d when cur_tok is NULL. subject: device uint8 [rows] or NULL (all
+ * rows); rows with subject == 0 get DV_NONE and keep their current token.
+ * cur_tok: device int32 [rows], the current token assignment, or NULL to use
+ * tok_d. Outputs: decision uint8 [rows], out_tok int32 [rows] (current token
+ * for KEEP/NONE, tok_v for REPLACE, mask_token for REMASK); prefix_len int32
+ * [rows/group_len] (offset of the first decided row of each group that is not
+ * KEEP, group_len if none) or NULL; best_group int32 [1] (group with the
+ * longest prefix, lowest index on ties) or NULL; best_group requires
+ * prefix_len. decision and out_tok may be NULL to skip them.
+ * Errors: DV_ERR_NULL, DV_ERR_SHAPE (rows < 0, group_len < 0, group_len not
+ * dividing rows), DV_ERR_ARG (unknown rule, non-finite thresholds). */
+dv_status dv_decide(const dv_decide_args *args, const dv_row_stats *stats, const uint8_t *subject,
+                    const int32_t *cur_tok, uint8_t *decision, int32_t *out_tok,
+                    int32_t *prefix_len, int32_t *best_group, hipStream_t stream);
+
+/* COVER stability-aware seed score ([COVER] §2, the Score equation):
+ * score = u * (1 + d_in) / (1 + d_out) where eligible (or everywhere when
+ * eligible is NULL), -inf elsewhere. All arrays device [rows]; u, d_in, d_out
+ * float32 (u is normally the verifier entropy from dv_verify_rows).
+ * Errors: DV_ERR_NULL, DV_ERR_SHAPE (rows < 0). */
+dv_status dv_seed_score(int64_t rows, const float *u, const float *d_in, const float *d_out,
+                        const uint8_t *eligible, float *score, hipStream_t stream);
+
+/* Per-sequence selection ([COVER] §2: a small set of top-scoring positions
+ * becomes the seeds; [SPOT] §3: threshold decoding with SPOT-Sets).
+ * score: device float32 [nseq][seq_len]; eligible: uint8 [nseq][seq_len] or
+ * NULL. Picks, per sequence, the k eligible positions with the largest
+ * (largest != 0) or smallest scores, equal scores to the lower index, sorted;
+ * with use_thr != 0 keeps of those only score > thr (largest) or score < thr
+ * (smallest). Outputs: out_idx int32 [nseq][k] and out_val float32 [nseq][k]
+ * (padded with -1 / NaN after the count), out_count int32 [nseq], out_mask
+ * uint8 [nseq][seq_len] (1 at kept positions) — each may be NULL. Scores must
+ * not be NaN. Errors: DV_ERR_NULL, DV_ERR_SHAPE (nseq < 0, seq_len < 1),
+ * DV_ERR_ARG (k < 1 or k > seq_len, thr not finite), DV_ERR_UNSUPPORTED
+ * (seq_len > 16384). */
+dv_status dv_select_topk(int64_t nseq, int64_t seq_len, const float *score, const uint8_t *eligible,
+                         int32_t k, int32_t largest, int32_t use_thr, float thr, int32_t *out_idx,
+                         float *out_val, int32_t *out_count, uint8_t *out_mask, hipStream_t stream);
+
+/* The noise hash words h[r][i] (uint32, device [rows][vocab]) for the
+ * positions described as in dv_noise. For testing the noise generator bit
+ * for bit. Errors: DV_ERR_NULL, DV_ERR_SHAPE. */
+dv_status dv_debug_hash(uint64_t seed, const int32_t *pos, int64_t pos_period, int64_t rows,
+                        int64_t vocab, uint32_t *out, hipStream_t stream);
+
+const char *dv_status_str(dv_status status);
+const char *dv_last_error(void);
+int dv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DLMVERIFY_H */

@@ -1,0 +1,161 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, and rejects bad arguments synchronously (validation runs before any
+HIP call, so none of these touches a device)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from token_verification_row_amd import dlmverify as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dlmverify.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libdlmverify.so is not built (run __graft_entry__.build())")
+    return B.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dv_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = _declared_functions()
+    assert names == sorted(["dv_verify_workspace_bytes", "dv_verify_rows", "dv_decide", "dv_seed_score",
+                           "dv_select_topk", "dv_debug_hash", "dv_status_str", "dv_last_error", "dv_version"])
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.dv_version() == 1
+
+
+def test_status_strings(lib):
+    for code, name in enumerate(["DV_OK", "DV_ERR_NULL", "DV_ERR_SHAPE", "DV_ERR_DTYPE", "DV_ERR_ALIGN",
+                                 "DV_ERR_ARG", "DV_ERR_WORKSPACE", "DV_ERR_UNSUPPORTED", "DV_ERR_HIP"]):
+        assert lib.dv_status_str(code).decode() == name
+
+
+FAKE = 1 << 20  # a non-null, 16-byte aligned address that is never dereferenced
+
+
+def _logits(rows=4, vocab=64, ld=64, dtype=B.DV_BF16, va=FAKE, vb=FAKE):
+    return B.dv_logits(verifier=va, drafter=vb, dtype=dtype, reserved=0, rows=rows, vocab=vocab, ld=ld)
+
+
+def _noise(T=0.0, period=0, pos=None):
+    return B.dv_noise(temperature=T, reserved=0, seed=0, pos=pos, pos_period=period)
+
+
+def _verify(lib, lg, nz, tuning=None, out=True, ws=None, ws_bytes=0):
+    st = B.dv_row_stats(kl=FAKE)
+    return lib.dv_verify_rows(ctypes.byref(lg), ctypes.byref(nz), None if tuning is None else ctypes.byref(tuning),
+                              ctypes.byref(st) if out else None, ws, ws_bytes, None)
+
+
+def test_verify_validation(lib):
+    assert lib.dv_verify_rows(None, ctypes.byref(_noise()), None, ctypes.byref(B.dv_row_stats()), None, 0,
+                              None) == B.DV_ERR_NULL
+    assert _verify(lib, _logits(), _noise(), out=False) == B.DV_ERR_NULL
+    assert _verify(lib, _logits(dtype=7), _noise()) == B.DV_ERR_DTYPE
+    assert _verify(lib, _logits(rows=-1), _noise()) == B.DV_ERR_SHAPE
+    assert _verify(lib, _logits(vocab=0), _noise()) == B.DV_ERR_SHAPE
+    assert _verify(lib, _logits(vocab=65, ld=64), _noise()) == B.DV_ERR_SHAPE
+    assert _verify(lib, _logits(rows=1 << 31), _noise()) == B.DV_ERR_SHAPE
+    assert _verify(lib, _logits(ld=68), _noise()) == B.DV_ERR_ALIGN          # 136 bytes per row
+    assert _verify(lib, _logits(va=FAKE + 8), _noise()) == B.DV_ERR_ALIGN
+    assert _verify(lib, _logits(vb=0), _noise()) == B.DV_ERR_NULL
+    assert _verify(lib, _logits(), _noise(T=-1.0)) == B.DV_ERR_ARG
+    assert _verify(lib, _logits(), _noise(T=float("nan"))) == B.DV_ERR_ARG
+    assert _verify(lib, _logits(), _noise(T=float("inf"))) == B.DV_ERR_ARG
+    assert _verify(lib, _logits(), _noise(period=-3)) == B.DV_ERR_SHAPE
+    bad = B.dv_tuning(split=65, block=0, shared_noise=-1, reserved=0)
+    assert _verify(lib, _logits(), _noise(), tuning=bad) == B.DV_ERR_ARG
+    bad = B.dv_tuning(split=0, block=300, shared_noise=-1, reserved=0)
+    assert _verify(lib, _logits(), _noise(), tuning=bad) == B.DV_ERR_ARG
+    bad = B.dv_tuning(split=0, block=0, shared_noise=1, reserved=0)   # greedy cannot share noise
+    assert _verify(lib, _logits(), _noise(), tuning=bad) == B.DV_ERR_ARG
+    assert "shared noise" in lib.dv_last_error().decode()
+    # a split that needs a workspace must get one
+    t = B.dv_tuning(split=4, block=0, shared_noise=0, reserved=0)
+    assert _verify(lib, _logits(vocab=4096, ld=4096), _noise(), tuning=t) == B.DV_ERR_WORKSPACE
+    assert _verify(lib, _logits(vocab=4096, ld=4096), _noise(), tuning=t, ws=FAKE, ws_bytes=100) == B.DV_ERR_WORKSPACE
+    assert _verify(lib, _logits(vocab=4096, ld=4096), _noise(), tuning=t, ws=FAKE + 16,
+                   ws_bytes=1 << 20) == B.DV_ERR_ALIGN
+
+
+def test_verify_empty_rows_is_a_noop(lib):
+    assert _verify(lib, _logits(rows=0, va=0, vb=0), _noise()) == B.DV_OK
+
+
+def test_workspace_query(lib):
+    out = ctypes.c_size_t(123)
+    lg, nz = _logits(rows=4, vocab=4096, ld=4096), _noise()
+    t = B.dv_tuning(split=4, block=0, shared_noise=0, reserved=0)
+    assert lib.dv_verify_workspace_bytes(ctypes.byref(lg), ctypes.byref(nz), ctypes.byref(t),
+                                         ctypes.byref(out)) == B.DV_OK
+    assert out.value == 4 * 4 * 64
+    t = B.dv_tuning(split=1, block=0, shared_noise=0, reserved=0)
+    assert lib.dv_verify_workspace_bytes(ctypes.byref(lg), ctypes.byref(nz), ctypes.byref(t),
+                                         ctypes.byref(out)) == B.DV_OK
+    assert out.value == 0
+    assert lib.dv_verify_workspace_bytes(ctypes.byref(lg), ctypes.byref(nz), None, None) == B.DV_ERR_NULL
+    # shared noise: one workgroup per (position, slice); slices keep the LDS copy of the noise small
+    lg = _logits(rows=2048, vocab=151936, ld=151936)
+    nz = _noise(T=1.0, period=32)
+    assert lib.dv_verify_workspace_bytes(ctypes.byref(lg), ctypes.byref(nz), None, ctypes.byref(out)) == B.DV_OK
+    assert out.value == 2048 * 16 * 64
+
+
+def _decide(lib, rule=B.DV_RULE_KL, rows=8, group_len=0, tau=0.1, thr=0.9, stats=None, subject=None, cur=None,
+            decision=FAKE, out_tok=FAKE, prefix=None, best=None):
+    a = B.dv_decide_args(rule=rule, tau_kl=tau, conf_thr=thr, mask_token=0, rows=rows, group_len=group_len)
+    st = stats if stats is not None else B.dv_row_stats(kl=FAKE, conf=FAKE, tok_v=FAKE, tok_d=FAKE)
+    return lib.dv_decide(ctypes.byref(a), ctypes.byref(st), subject, cur, decision, out_tok, prefix, best, None)
+
+
+def test_decide_validation(lib):
+    assert lib.dv_decide(None, None, None, None, None, None, None, None, None) == B.DV_ERR_NULL
+    assert _decide(lib, rule=9) == B.DV_ERR_ARG
+    assert _decide(lib, rows=-1) == B.DV_ERR_SHAPE
+    assert _decide(lib, tau=float("nan")) == B.DV_ERR_ARG
+    assert _decide(lib, rule=B.DV_RULE_COUPLED_ACCEPT, group_len=0) == B.DV_ERR_SHAPE
+    assert _decide(lib, rule=B.DV_RULE_COUPLED_ACCEPT, group_len=3) == B.DV_ERR_SHAPE   # 3 does not divide 8
+    assert _decide(lib, group_len=4, best=FAKE) == B.DV_ERR_NULL                      # best needs prefix
+    assert _decide(lib, stats=B.dv_row_stats(conf=FAKE, tok_d=FAKE)) == B.DV_ERR_NULL  # KL needs kl
+    assert _decide(lib, rule=B.DV_RULE_COVER, stats=B.dv_row_stats(conf=FAKE, tok_d=FAKE)) == B.DV_ERR_NULL
+    assert _decide(lib, stats=B.dv_row_stats(kl=FAKE)) == B.DV_ERR_NULL                # no current token
+    assert _decide(lib, rows=0) == B.DV_OK
+
+
+def test_seed_score_select_hash_validation(lib):
+    assert lib.dv_seed_score(-1, None, None, None, None, None, None) == B.DV_ERR_SHAPE
+    assert lib.dv_seed_score(4, FAKE, None, FAKE, None, FAKE, None) == B.DV_ERR_NULL
+    assert lib.dv_seed_score(0, None, None, None, None, None, None) == B.DV_OK
+    sel = lib.dv_select_topk
+    assert sel(1, 0, FAKE, None, 1, 1, 0, 0.0, None, None, None, None, None) == B.DV_ERR_SHAPE
+    assert sel(1, 10, FAKE, None, 0, 1, 0, 0.0, None, None, None, None, None) == B.DV_ERR_ARG
+    assert sel(1, 10, FAKE, None, 11, 1, 0, 0.0, None, None, None, None, None) == B.DV_ERR_ARG
+    assert sel(1, 10, FAKE, None, 3, 1, 1, float("inf"), None, None, None, None, None) == B.DV_ERR_ARG
+    assert sel(1, 16385, FAKE, None, 3, 1, 0, 0.0, None, None, None, None, None) == B.DV_ERR_UNSUPPORTED
+    assert sel(1, 10, None, None, 3, 1, 0, 0.0, None, None, None, None, None) == B.DV_ERR_NULL
+    assert sel(0, 10, None, None, 3, 1, 0, 0.0, None, None, None, None, None) == B.DV_OK
+    assert lib.dv_debug_hash(0, None, 0, -1, 4, FAKE, None) == B.DV_ERR_SHAPE
+    assert lib.dv_debug_hash(0, None, -1, 1, 4, FAKE, None) == B.DV_ERR_SHAPE
+    assert lib.dv_debug_hash(0, None, 0, 2, 4, None, None) == B.DV_ERR_NULL
+    assert lib.dv_debug_hash(0, None, 0, 0, 4, None, None) == B.DV_OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    a = torch.zeros((2, 8), dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        B.dv_verify_rows(a, a)
+    with pytest.raises(TypeError):
+        B.dv_seed_score(torch.zeros(3), torch.zeros(3), torch.zeros(3))

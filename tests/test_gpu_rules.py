@@ -1,0 +1,299 @@
+"""GPU parity of dv_decide, dv_seed_score and dv_select_topk, alone (fed the
+same fp32 inputs as the oracle: exact) and chained after dv_verify_rows on the
+workloads (against the oracle's own statistics: exact outside the near-tie
+bands)."""
+
+import numpy as np
+import pytest
+import torch
+
+import token_verification_row_amd as dv
+import workloads as W
+from oracle import decide as odecide
+from oracle import rowstats
+from oracle import select as oselect
+from parity_util import BAND, ATOL, RTOL, decisions_in_band, oracle_rows, to_numpy
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    return torch.device("cuda:0")
+
+
+def _t(x, dev):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+
+def _oracle_decide(rule, st, tau, theta, mask, subject=None, cur=None, group_len=0):
+    st64 = {k: (np.asarray(v, np.float64) if k in ("kl", "conf") else np.asarray(v)) for k, v in st.items()
+            if v is not None}
+    return odecide.decide(rule, st64, tau_kl=np.float32(tau), conf_thr=np.float32(theta), mask_token=mask,
+                          subject=subject, cur_tok=cur, group_len=group_len)
+
+
+@pytest.mark.parametrize("rows,group_len", [(1, 0), (7, 0), (64, 1), (1000, 0), (960, 4), (960, 32), (960, 96),
+                                            (2048, 32), (3000, 1000)])
+def test_decide_exact(rows, group_len):
+    print(f"case: decide rows={rows} group_len={group_len}", flush=True)
+    dev = _dev()
+    rng = np.random.default_rng(rows + group_len)
+    st = dict(kl=rng.uniform(0, 0.2, rows).astype(np.float32), conf=rng.uniform(0, 1, rows).astype(np.float32),
+              tok_v=rng.integers(0, 3, rows).astype(np.int32), tok_d=rng.integers(0, 3, rows).astype(np.int32))
+    st["kl"][::17] = np.float32(0.1)          # exactly at the thresholds
+    st["conf"][::13] = np.float32(0.9)
+    subject = (rng.random(rows) < 0.8).astype(np.uint8)
+    cur = rng.integers(0, 3, rows).astype(np.int32)
+    gst = {k: _t(v, dev) for k, v in st.items()}
+    rules = ["TRUST", "KL", "CONF", "KL_OR_CONF", "COVER"] + (["COUPLED_ACCEPT"] if group_len else [])
+    for rule in rules:
+        for use_subject in (False, True):
+            for use_cur in (False, True):
+                subj = subject if use_subject else None
+                c = cur if use_cur else None
+                d, o, pre, best = dv.dv_decide(rule, gst, tau_kl=0.1, conf_thr=0.9, mask_token=-9,
+                                               subject=None if subj is None else _t(subj, dev),
+                                               cur_tok=None if c is None else _t(c, dev), group_len=group_len,
+                                               want_prefix=group_len > 0, want_best=group_len > 0)
+                rd, ro = _oracle_decide(dv.RULES[rule], st, 0.1, 0.9, -9, subj, c, group_len)
+                np.testing.assert_array_equal(d.cpu().numpy(), rd, err_msg=f"{rule} decisions")
+                np.testing.assert_array_equal(o.cpu().numpy(), ro, err_msg=f"{rule} out_tok")
+                if group_len:
+                    rp = odecide.accepted_prefix(rd, group_len, subj)
+                    np.testing.assert_array_equal(pre.cpu().numpy(), rp, err_msg=f"{rule} prefix")
+                    assert int(best.cpu()[0]) == odecide.best_group(rp)
+
+
+def test_decide_empty_best_group():
+    print("case: decide empty", flush=True)
+    dev = _dev()
+    st = {"tok_v": torch.zeros(0, dtype=torch.int32, device=dev), "tok_d": torch.zeros(0, dtype=torch.int32, device=dev)}
+    d, o, pre, best = dv.dv_decide("COUPLED_ACCEPT", st, rows=0, group_len=4, want_prefix=True, want_best=True)
+    assert int(best.cpu()[0]) == -1 and d.numel() == 0
+
+
+def test_seed_score():
+    print("case: seed score", flush=True)
+    dev = _dev()
+    rng = np.random.default_rng(0)
+    n = 100003
+    u = rng.uniform(0, 12, n).astype(np.float32)
+    d_in = rng.uniform(0, 1, n).astype(np.float32)
+    d_out = rng.uniform(0, 1, n).astype(np.float32)
+    el = (rng.random(n) < 0.5).astype(np.uint8)
+    for e in (None, el):
+        got = dv.dv_seed_score(_t(u, dev), _t(d_in, dev), _t(d_out, dev), None if e is None else _t(e, dev))
+        ref = oselect.seed_score(u, d_in, d_out, e)
+        g = got.cpu().numpy().astype(np.float64)
+        fin = np.isfinite(ref)
+        np.testing.assert_array_equal(np.isfinite(g), fin)
+        assert np.all(g[~fin] == -np.inf)
+        np.testing.assert_allclose(g[fin], ref[fin], rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 17, 64, 1000, 1024, 2048, 5000, 16384])
+def test_select_topk_exact(L):
+    print(f"case: select L={L}", flush=True)
+    dev = _dev()
+    rng = np.random.default_rng(L)
+    nseq = 5 if L <= 5000 else 2
+    score = (rng.standard_normal((nseq, L)) * 3).round(1).astype(np.float32)   # many ties
+    score[0, : min(L, 5)] = -np.inf
+    score[-1, :: 7] = 0.0
+    score[-1, 1::7] = -0.0
+    el = (rng.random((nseq, L)) < 0.7).astype(np.uint8)
+    el[1] = 0                                                                 # a sequence with nothing eligible
+    for k in sorted({1, min(L, 3), min(L, 32), min(L, 64), L}):
+        for largest in (True, False):
+            for use_thr, thr in ((False, 0.0), (True, 0.5), (True, -100.0)):
+                for e in (None, el):
+                    idx, val, cnt, mask = dv.dv_select_topk(_t(score, dev), k, eligible=None if e is None else _t(e, dev),
+                                                            largest=largest, use_thr=use_thr, thr=thr, want_mask=True)
+                    ri, rv, rc = oselect.select_topk(score, k, eligible=e, largest=largest, use_thr=use_thr,
+                                                     thr=np.float32(thr))
+                    ctx = f"L={L} k={k} largest={largest} thr={use_thr, thr} elig={e is not None}"
+                    np.testing.assert_array_equal(cnt.cpu().numpy(), rc, err_msg=ctx)
+                    np.testing.assert_array_equal(idx.cpu().numpy(), ri, err_msg=ctx)
+                    gv = val.cpu().numpy().astype(np.float64)
+                    np.testing.assert_array_equal(np.isnan(gv), np.isnan(rv), err_msg=ctx)
+                    ok = ~np.isnan(rv)
+                    np.testing.assert_array_equal(gv[ok], rv[ok], err_msg=ctx)
+                    m = np.zeros((nseq, L), np.uint8)
+                    for s in range(nseq):
+                        m[s, ri[s, :rc[s]]] = 1
+                    np.testing.assert_array_equal(mask.cpu().numpy(), m, err_msg=ctx)
+
+
+# ---------------------------------------------------------------- chains ----
+
+def _upload_bf16(x, dev):
+    return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def test_workload_tiny_rules_chain():
+    w = W.workload(1)
+    print(f"case: workload 1 chain ({w.name})", flush=True)
+    dev = _dev()
+    a_np, b_np = W.make_logits_numpy(w)
+    got = dv.dv_verify_rows(_t(a_np, dev), _t(b_np, dev), temperature=w.temperature, seed=w.seed)
+    ref = oracle_rows(a_np, b_np, "fp32", 0.0, w.seed, W.positions(w))
+    subject = W.subject_rows(w)
+    g = to_numpy(got)
+    for rule in ("TRUST", "KL", "CONF", "KL_OR_CONF", "COVER"):
+        d, o, _, _ = dv.dv_decide(rule, got, tau_kl=w.tau_kl, conf_thr=w.conf_thr, mask_token=-1,
+                                  subject=_t(subject, dev))
+        rd, ro = odecide.decide(dv.RULES[rule], ref, tau_kl=w.tau_kl, conf_thr=w.conf_thr, mask_token=-1,
+                                subject=subject)
+        band = decisions_in_band(dv.RULES[rule], ref["kl"], ref["conf"], w.tau_kl, w.conf_thr)
+        bad = (d.cpu().numpy() != rd) & ~band
+        assert not bad.any(), (rule, np.nonzero(bad))
+        # on the GPU's own statistics the rules agree exactly
+        gd, go = _oracle_decide(dv.RULES[rule], g, w.tau_kl, w.conf_thr, -1, subject)
+        np.testing.assert_array_equal(d.cpu().numpy(), gd, err_msg=rule)
+        np.testing.assert_array_equal(o.cpu().numpy(), go, err_msg=rule)
+
+
+def test_workload_remask_chain_full_size():
+    w = W.workload(2)
+    print(f"case: workload 2 chain ({w.name})", flush=True)
+    dev = _dev()
+    a_np, b_np = W.make_logits_numpy(w)
+    got = dv.dv_verify_rows(_upload_bf16(a_np, dev), _upload_bf16(b_np, dev), temperature=0.0, seed=w.seed)
+    g = to_numpy(got)
+    rows = np.arange(0, w.rows, 9)
+    ref = oracle_rows(a_np[rows], b_np[rows], "bf16", 0.0, w.seed, W.positions(w)[rows])
+    counts = {}
+    for rule in w.rules:
+        d, o, _, _ = dv.dv_decide(rule, got, tau_kl=w.tau_kl, conf_thr=w.conf_thr, mask_token=-1)
+        dn = d.cpu().numpy()
+        gd, go = _oracle_decide(dv.RULES[rule], g, w.tau_kl, w.conf_thr, -1)
+        np.testing.assert_array_equal(dn, gd, err_msg=rule)
+        rd, _ = odecide.decide(dv.RULES[rule], ref, tau_kl=w.tau_kl, conf_thr=w.conf_thr, mask_token=-1)
+        band = decisions_in_band(dv.RULES[rule], ref["kl"], ref["conf"], w.tau_kl, w.conf_thr)
+        assert not ((dn[rows] != rd) & ~band).any(), rule
+        counts[rule] = {int(c): int((dn == c).sum()) for c in np.unique(dn)}
+    print("decision counts", counts, flush=True)
+
+
+def _oracle_stats_blocks(a_np, b_np, dtype, block=32):
+    out = {}
+    for s in range(0, a_np.shape[0], block):
+        st = rowstats.row_stats(rowstats.as_float64(a_np[s:s + block], dtype), rowstats.as_float64(b_np[s:s + block], dtype))
+        for k, v in st.items():
+            out.setdefault(k, []).append(v)
+    return {k: np.concatenate(v) for k, v in out.items()}
+
+
+def test_workload_cover_chain_full_size():
+    w = W.workload(3)
+    print(f"case: workload 3 chain ({w.name})", flush=True)
+    dev = _dev()
+    a_np, b_np = W.make_logits_numpy(w)
+    got = dv.dv_verify_rows(_upload_bf16(a_np, dev), _upload_bf16(b_np, dev), temperature=0.0, seed=w.seed)
+    committed = W.committed_rows(w)
+    d_in, d_out = W.diffusion_inputs(w)
+    score = dv.dv_seed_score(got["entropy"], _t(d_in, dev), _t(d_out, dev), _t(committed, dev))
+    idx, val, cnt, mask = dv.dv_select_topk(score.view(w.B, w.L), w.topk, eligible=_t(committed, dev).view(w.B, w.L),
+                                            want_mask=True)
+    d, o, _, _ = dv.dv_decide("COVER", got, conf_thr=w.conf_thr, mask_token=-1, subject=mask.view(-1))
+    g = to_numpy(got)
+    # exact on the GPU's own intermediate values
+    gs = score.cpu().numpy()
+    ri, rv, rc = oselect.select_topk(gs.reshape(w.B, w.L), w.topk, eligible=committed.reshape(w.B, w.L))
+    np.testing.assert_array_equal(idx.cpu().numpy(), ri)
+    m = np.zeros(w.rows, np.uint8)
+    m[ri[0, :rc[0]]] = 1
+    np.testing.assert_array_equal(mask.cpu().numpy().ravel(), m)
+    gd, go = _oracle_decide(dv.RULES["COVER"], g, 0.0, w.conf_thr, -1, m)
+    np.testing.assert_array_equal(d.cpu().numpy(), gd)
+    np.testing.assert_array_equal(o.cpu().numpy(), go)
+    # against the oracle's own chain: seed score within tolerance, selection exact unless a near-tie
+    ost = _oracle_stats_blocks(a_np, b_np, "bf16")
+    np.testing.assert_allclose(g["entropy"], ost["entropy"], rtol=RTOL, atol=ATOL)
+    osc = oselect.seed_score(ost["entropy"], d_in, d_out, committed)
+    fin = np.isfinite(osc)
+    np.testing.assert_allclose(gs[fin], osc[fin], rtol=RTOL, atol=ATOL)
+    oi, ov, oc = oselect.select_topk(osc.reshape(w.B, w.L), w.topk, eligible=committed.reshape(w.B, w.L))
+    srt = np.sort(osc[fin])[::-1]
+    kth_gap = srt[w.topk - 1] - srt[w.topk]
+    if kth_gap > BAND:
+        assert set(oi[0].tolist()) == set(idx.cpu().numpy()[0].tolist())
+    counts = {int(c): int((d.cpu().numpy() == c).sum()) for c in range(4)}
+    print("k-th score gap", kth_gap, "decision counts", counts, flush=True)
+
+
+def test_workload_spot_tree_chain_full_size():
+    w = W.workload(4)
+    print(f"case: workload 4 chain ({w.name})", flush=True)
+    dev = _dev()
+    a, b = W.make_logits_torch(w, dev)
+    got = dv.dv_verify_rows(a, b, temperature=w.temperature, seed=w.seed, pos_period=w.pos_period)
+    d, o, pre, best = dv.dv_decide("COUPLED_ACCEPT", got, mask_token=-1, group_len=w.group_len, want_prefix=True,
+                                   want_best=True)
+    g = to_numpy(got)
+    gd, go = _oracle_decide(dv.RULES["COUPLED_ACCEPT"], g, 0.0, 0.0, -1, group_len=w.group_len)
+    np.testing.assert_array_equal(d.cpu().numpy(), gd)
+    np.testing.assert_array_equal(o.cpu().numpy(), go)
+    rp = odecide.accepted_prefix(gd, w.group_len)
+    np.testing.assert_array_equal(pre.cpu().numpy(), rp)
+    assert int(best.cpu()[0]) == odecide.best_group(rp)
+    # oracle tokens for three whole candidates give the same prefixes (unless a token is a near-tie)
+    for c in (0, 17, 63):
+        rows = np.arange(c * w.group_len, (c + 1) * w.group_len)
+        an = a[c * w.group_len:(c + 1) * w.group_len].view(torch.int16).cpu().numpy().view(np.uint16)
+        bn = b[c * w.group_len:(c + 1) * w.group_len].view(torch.int16).cpu().numpy().view(np.uint16)
+        ref = oracle_rows(an, bn, "bf16", w.temperature, w.seed, W.positions(w)[rows])
+        od, _ = odecide.decide(odecide.COUPLED_ACCEPT, ref, mask_token=-1, group_len=w.group_len)
+        op = odecide.accepted_prefix(od, w.group_len)[0]
+        near = (ref["margin_v"] <= BAND) | (ref["margin_d"] <= BAND)
+        if not near[: min(op, rp[c]) + 1].any():
+            assert op == rp[c], (c, op, rp[c])
+    print("mean accepted prefix", float(rp.mean()), "best", int(best.cpu()[0]),
+          "accept rate", float((g["tok_v"] == g["tok_d"]).mean()), flush=True)
+
+
+def test_workload_throughput_topk_chain():
+    w = W.workload(5)
+    print(f"case: workload 5 chain ({w.name})", flush=True)
+    dev = _dev()
+    a, b = W.make_logits_torch(w, dev)
+    got = dv.dv_verify_rows(a, b, temperature=w.temperature, seed=w.seed)
+    idx, val, cnt, _ = dv.dv_select_topk(got["kl"].view(w.B, w.L), w.topk)
+    kl = got["kl"].cpu().numpy().reshape(w.B, w.L)
+    ri, rv, rc = oselect.select_topk(kl, w.topk)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ri)
+    np.testing.assert_array_equal(cnt.cpu().numpy(), rc)
+    del a, b, got
+    torch.cuda.empty_cache()
+
+
+def test_band_set_decisions():
+    """Rows calibrated so that confidence and KL straddle the thresholds."""
+    print("case: band set", flush=True)
+    dev = _dev()
+    rng = np.random.default_rng(2024)
+    rows, V = 512, 8192
+    a = rng.standard_normal((rows, V)).astype(np.float32)
+    spike = rng.uniform(7.0, 13.0, rows).astype(np.float32)        # conf spans roughly [0.5, 1)
+    tok = rng.integers(0, V, rows)
+    a[np.arange(rows), tok] += spike
+    b = a + rng.standard_normal((rows, V)).astype(np.float32) * rng.uniform(0.0, 0.6, (rows, 1)).astype(np.float32)
+    a16, b16 = W.round_bf16_bits(a), W.round_bf16_bits(b)
+    ref = oracle_rows(a16, b16, "bf16", 0.0, 0, np.arange(rows))
+    tau = float(np.median(ref["kl"]))
+    theta = float(np.median(ref["conf"]))
+    got = dv.dv_verify_rows(_upload_bf16(a16, dev), _upload_bf16(b16, dev))
+    inband = {}
+    for rule in ("KL", "CONF", "KL_OR_CONF", "COVER"):
+        d, _, _, _ = dv.dv_decide(rule, got, tau_kl=tau, conf_thr=theta, mask_token=-1)
+        rd, _ = odecide.decide(dv.RULES[rule], ref, tau_kl=np.float32(tau), conf_thr=np.float32(theta), mask_token=-1)
+        band = decisions_in_band(dv.RULES[rule], ref["kl"], ref["conf"], np.float32(tau), np.float32(theta))
+        bad = (d.cpu().numpy() != rd) & ~band
+        assert not bad.any(), (rule, np.nonzero(bad))
+        inband[rule] = int(band.sum())
+        counts = np.bincount(d.cpu().numpy(), minlength=4)
+        if rule != "COVER":
+            assert counts[dv.DV_REMASK] > 50 and counts[dv.DV_KEEP] > 50, (rule, counts)
+    print("in-band rows", inband, flush=True)

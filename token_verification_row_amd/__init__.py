@@ -1,0 +1,14 @@
+"""MI355X (gfx950) library for the per-position verification pass of masked
+diffusion language-model decoding.
+
+``libdlmverify.so`` (C ABI, ``include/dlmverify.h``) holds every kernel; the
+``dlmverify`` module is its Python binding with the same function names. The
+library is loaded on first use, and a missing library is an error, never a
+silent fallback.
+"""
+
+from .dlmverify import (  # noqa: F401
+    DVError, LIB_PATH, RULES, STAT_FIELDS, load_library, dv_verify_workspace_bytes, dv_verify_rows, dv_decide,
+    dv_seed_score, dv_select_topk, dv_debug_hash, dv_status_str, dv_last_error, dv_version,
+    DV_NONE, DV_KEEP, DV_REPLACE, DV_REMASK,
+)

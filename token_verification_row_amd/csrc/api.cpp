@@ -1,0 +1,309 @@
+// Host side of libdlmverify: argument validation, launch geometry, status
+// codes and error text. Every check runs before any HIP call, so a rejected
+// call has no side effect.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "dv_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dv_status fail(dv_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+dv_status ok() {
+  g_err[0] = '\0';
+  return DV_OK;
+}
+
+dv_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ok();
+  return fail(DV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxIndex = (int64_t(1) << 31) - 1;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Launch shape of dv_verify_rows, decided from the sizes alone.
+struct Geometry {
+  int32_t split = 1;
+  int32_t block = 256;
+  int32_t shared = 0;
+  int32_t slice_chunks = 0;
+  size_t workspace = 0;
+};
+
+constexpr size_t kMaxSharedLds = 160 * 1024;
+
+dv_status check_logits(const dv_logits *x, bool need_ptrs) {
+  if (!x) return fail(DV_ERR_NULL, "logits descriptor is NULL");
+  if (x->dtype != DV_FP32 && x->dtype != DV_BF16) return fail(DV_ERR_DTYPE, "unknown dtype %d", x->dtype);
+  if (x->rows < 0 || x->rows > kMaxIndex) return fail(DV_ERR_SHAPE, "rows %lld out of range", (long long)x->rows);
+  if (x->vocab < 1 || x->vocab > kMaxIndex) return fail(DV_ERR_SHAPE, "vocab %lld out of range", (long long)x->vocab);
+  if (x->ld < x->vocab) return fail(DV_ERR_SHAPE, "ld %lld < vocab %lld", (long long)x->ld, (long long)x->vocab);
+  const int64_t elt = x->dtype == DV_BF16 ? 2 : 4;
+  if (x->ld > (int64_t(1) << 40) / elt) return fail(DV_ERR_SHAPE, "ld %lld too large", (long long)x->ld);
+  if ((x->ld * elt) % 16 != 0) return fail(DV_ERR_ALIGN, "row pitch ld*elt = %lld bytes is not a multiple of 16", (long long)(x->ld * elt));
+  if (need_ptrs && x->rows > 0) {
+    if (!x->verifier || !x->drafter) return fail(DV_ERR_NULL, "verifier or drafter pointer is NULL");
+    if (!aligned16(x->verifier) || !aligned16(x->drafter)) return fail(DV_ERR_ALIGN, "logit pointers must be 16-byte aligned");
+  }
+  return DV_OK;
+}
+
+dv_status check_noise(const dv_noise *n) {
+  if (!n) return fail(DV_ERR_NULL, "noise descriptor is NULL");
+  if (!std::isfinite(n->temperature) || n->temperature < 0.0f)
+    return fail(DV_ERR_ARG, "temperature must be finite and >= 0");
+  if (n->pos_period < 0 || n->pos_period > kMaxIndex) return fail(DV_ERR_SHAPE, "pos_period out of range");
+  return DV_OK;
+}
+
+dv_status choose_geometry(const dv_logits *x, const dv_noise *n, const dv_tuning *t, Geometry &g) {
+  const int64_t N = x->dtype == DV_BF16 ? 8 : 4;  // elements per 16-byte chunk
+  const int64_t nch = (x->vocab + N - 1) / N;
+  const bool greedy = n->temperature == 0.0f;
+  const bool can_share = !greedy && n->pos == nullptr && n->pos_period > 0;
+  const int32_t want_shared = t ? t->shared_noise : -1;
+  if (t) {
+    if (t->split < 0 || t->split > 64) return fail(DV_ERR_ARG, "tuning.split must be 0..64");
+    if (t->block != 0 && t->block != 256 && t->block != 512 && t->block != 1024)
+      return fail(DV_ERR_ARG, "tuning.block must be 0, 256, 512 or 1024");
+    if (want_shared < -1 || want_shared > 1) return fail(DV_ERR_ARG, "tuning.shared_noise must be -1, 0 or 1");
+    if (want_shared == 1 && !can_share)
+      return fail(DV_ERR_ARG, "shared noise needs temperature > 0, pos == NULL and pos_period > 0");
+  }
+  if (want_shared == 1) {
+    g.shared = 1;
+  } else if (want_shared == 0) {
+    g.shared = 0;
+  } else {
+    // share when each position carries several rows
+    g.shared = can_share && x->rows >= 2 * n->pos_period ? 1 : 0;
+  }
+  int64_t split;
+  if (g.shared) {
+    const int64_t groups = n->pos_period < x->rows ? n->pos_period : x->rows;
+    // aim for ~2 workgroups per CU, and a slice whose noise fits 64 KiB of LDS
+    split = (512 + groups - 1) / (groups > 0 ? groups : 1);
+    const int64_t min_split = (nch * N * 4 + 65535) / 65536;
+    if (split < min_split) split = min_split;
+    g.block = 512;
+  } else {
+    // aim for ~8192 waves in flight, each slice at least 256 chunks
+    split = x->rows > 0 ? (8192 + x->rows - 1) / x->rows : 1;
+    const int64_t max_by_len = nch / 256 > 0 ? nch / 256 : 1;
+    if (split > max_by_len) split = max_by_len;
+    g.block = 256;
+  }
+  if (t && t->split > 0) split = t->split;
+  if (t && t->block > 0 && g.shared) {
+    if (t->block > 512) return fail(DV_ERR_ARG, "tuning.block must be 256 or 512 with shared noise");
+    g.block = t->block;
+  }
+  if (split > 64) split = 64;
+  if (split > nch) split = nch;
+  if (split < 1) split = 1;
+  g.split = static_cast<int32_t>(split);
+  g.slice_chunks = static_cast<int32_t>((nch + split - 1) / split);
+  if (g.shared && static_cast<size_t>(g.slice_chunks) * N * 4 > kMaxSharedLds)
+    return fail(DV_ERR_ARG, "tuning.split %d leaves a slice too long for LDS", g.split);
+  const int64_t waves = x->rows * split;
+  if (!g.shared && (waves + 3) / 4 > kMaxIndex) return fail(DV_ERR_UNSUPPORTED, "too many rows for one launch");
+  g.workspace = split > 1 ? static_cast<size_t>(x->rows) * split * sizeof(dv::Partial) : 0;
+  return DV_OK;
+}
+
+bool finite(float v) { return std::isfinite(v); }
+
+}  // namespace
+
+extern "C" {
+
+dv_status dv_verify_workspace_bytes(const dv_logits *logits, const dv_noise *noise, const dv_tuning *tuning,
+                                    size_t *bytes) {
+  if (!bytes) return fail(DV_ERR_NULL, "bytes is NULL");
+  dv_status s = check_logits(logits, false);
+  if (s != DV_OK) return s;
+  if ((s = check_noise(noise)) != DV_OK) return s;
+  Geometry g;
+  if ((s = choose_geometry(logits, noise, tuning, g)) != DV_OK) return s;
+  *bytes = g.workspace;
+  return ok();
+}
+
+dv_status dv_verify_rows(const dv_logits *logits, const dv_noise *noise, const dv_tuning *tuning,
+                         const dv_row_stats *out, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  dv_status s = check_logits(logits, true);
+  if (s != DV_OK) return s;
+  if ((s = check_noise(noise)) != DV_OK) return s;
+  if (!out) return fail(DV_ERR_NULL, "output descriptor is NULL");
+  Geometry g;
+  if ((s = choose_geometry(logits, noise, tuning, g)) != DV_OK) return s;
+  if (g.workspace > 0) {
+    if (!workspace) return fail(DV_ERR_WORKSPACE, "workspace of %zu bytes required", g.workspace);
+    if (workspace_bytes < g.workspace)
+      return fail(DV_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", g.workspace, workspace_bytes);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(DV_ERR_ALIGN, "workspace must be 256-byte aligned");
+  }
+  if (logits->rows == 0) return ok();
+  dv::VerifyLaunch p{};
+  p.va = logits->verifier;
+  p.vb = logits->drafter;
+  p.rows = logits->rows;
+  p.vocab = logits->vocab;
+  p.ld = logits->ld;
+  p.bf16 = logits->dtype == DV_BF16;
+  p.greedy = noise->temperature == 0.0f;
+  p.cT = p.greedy ? 0.0f : 1.44269504088896340736f / noise->temperature;
+  if (!p.greedy && !std::isfinite(p.cT)) return fail(DV_ERR_ARG, "temperature too small");
+  p.seed_b = dv::seed_word(noise->seed);
+  p.pos = noise->pos;
+  p.pos_period = noise->pos_period;
+  p.split = g.split;
+  p.block = g.block;
+  p.shared = g.shared;
+  p.slice_chunks = g.slice_chunks;
+  p.ws = static_cast<dv::Partial *>(workspace);
+  p.out = *out;
+  return hip_status(dv::launch_verify(p, stream), "dv_verify_rows launch");
+}
+
+dv_status dv_decide(const dv_decide_args *a, const dv_row_stats *stats, const uint8_t *subject, const int32_t *cur_tok,
+                    uint8_t *decision, int32_t *out_tok, int32_t *prefix_len, int32_t *best_group, hipStream_t stream) {
+  if (!a || !stats) return fail(DV_ERR_NULL, "args or stats is NULL");
+  if (a->rows < 0 || a->rows > kMaxIndex) return fail(DV_ERR_SHAPE, "rows out of range");
+  if (a->group_len < 0 || a->group_len > kMaxIndex) return fail(DV_ERR_SHAPE, "group_len out of range");
+  if (a->rule < DV_RULE_TRUST || a->rule > DV_RULE_COUPLED_ACCEPT) return fail(DV_ERR_ARG, "unknown rule %d", a->rule);
+  if (!finite(a->tau_kl) || !finite(a->conf_thr)) return fail(DV_ERR_ARG, "thresholds must be finite");
+  const bool need_groups = a->rule == DV_RULE_COUPLED_ACCEPT || prefix_len || best_group;
+  if (need_groups) {
+    if (a->group_len <= 0) return fail(DV_ERR_SHAPE, "group_len must be > 0 for this request");
+    if (a->rows % a->group_len != 0) return fail(DV_ERR_SHAPE, "group_len must divide rows");
+  }
+  if (best_group && !prefix_len) return fail(DV_ERR_NULL, "best_group needs prefix_len");
+  if (a->rows > 0) {
+    if (!cur_tok && !stats->tok_d) return fail(DV_ERR_NULL, "cur_tok and stats.tok_d are both NULL");
+    switch (a->rule) {
+      case DV_RULE_KL:
+        if (!stats->kl) return fail(DV_ERR_NULL, "rule KL needs stats.kl");
+        break;
+      case DV_RULE_CONF:
+        if (!stats->conf) return fail(DV_ERR_NULL, "rule CONF needs stats.conf");
+        break;
+      case DV_RULE_KL_OR_CONF:
+        if (!stats->kl || !stats->conf) return fail(DV_ERR_NULL, "rule KL_OR_CONF needs stats.kl and stats.conf");
+        break;
+      case DV_RULE_COVER:
+        if (!stats->conf || !stats->tok_v) return fail(DV_ERR_NULL, "rule COVER needs stats.conf and stats.tok_v");
+        break;
+      case DV_RULE_COUPLED_ACCEPT:
+        if (!stats->tok_v) return fail(DV_ERR_NULL, "rule COUPLED_ACCEPT needs stats.tok_v");
+        break;
+      default:
+        break;
+    }
+  }
+  if (a->rows == 0) {
+    if (best_group) {
+      // no groups: the answer is -1, written by the reduction kernel
+      dv::DecideLaunch p{};
+      p.rows = 0;
+      p.best_group = best_group;
+      p.prefix_len = prefix_len;
+      return hip_status(dv::launch_decide(p, stream), "dv_decide launch");
+    }
+    return ok();
+  }
+  dv::DecideLaunch p{};
+  p.rule = a->rule;
+  p.tau_kl = a->tau_kl;
+  p.conf_thr = a->conf_thr;
+  p.mask_token = a->mask_token;
+  p.rows = a->rows;
+  p.group_len = a->group_len;
+  p.kl = stats->kl;
+  p.conf = stats->conf;
+  p.tok_v = stats->tok_v;
+  p.tok_d = stats->tok_d;
+  p.subject = subject;
+  p.cur_tok = cur_tok;
+  p.decision = decision;
+  p.out_tok = out_tok;
+  p.prefix_len = prefix_len;
+  p.best_group = best_group;
+  return hip_status(dv::launch_decide(p, stream), "dv_decide launch");
+}
+
+dv_status dv_seed_score(int64_t rows, const float *u, const float *d_in, const float *d_out, const uint8_t *eligible,
+                        float *score, hipStream_t stream) {
+  if (rows < 0 || rows > kMaxIndex) return fail(DV_ERR_SHAPE, "rows out of range");
+  if (rows > 0 && (!u || !d_in || !d_out || !score)) return fail(DV_ERR_NULL, "u, d_in, d_out and score are required");
+  return hip_status(dv::launch_seed_score(rows, u, d_in, d_out, eligible, score, stream), "dv_seed_score launch");
+}
+
+dv_status dv_select_topk(int64_t nseq, int64_t seq_len, const float *score, const uint8_t *eligible, int32_t k,
+                         int32_t largest, int32_t use_thr, float thr, int32_t *out_idx, float *out_val,
+                         int32_t *out_count, uint8_t *out_mask, hipStream_t stream) {
+  if (nseq < 0 || nseq > kMaxIndex) return fail(DV_ERR_SHAPE, "nseq out of range");
+  if (seq_len < 1) return fail(DV_ERR_SHAPE, "seq_len must be >= 1");
+  if (seq_len > dv::kMaxSelectLen)
+    return fail(DV_ERR_UNSUPPORTED, "seq_len %lld exceeds %lld", (long long)seq_len, (long long)dv::kMaxSelectLen);
+  if (k < 1 || k > seq_len) return fail(DV_ERR_ARG, "k must be in [1, seq_len]");
+  if (use_thr && !finite(thr)) return fail(DV_ERR_ARG, "thr must be finite");
+  if (nseq > 0 && !score) return fail(DV_ERR_NULL, "score is NULL");
+  dv::SelectLaunch p{};
+  p.nseq = nseq;
+  p.seq_len = seq_len;
+  p.score = score;
+  p.eligible = eligible;
+  p.k = k;
+  p.largest = largest != 0;
+  p.use_thr = use_thr != 0;
+  p.thr = thr;
+  p.out_idx = out_idx;
+  p.out_val = out_val;
+  p.out_count = out_count;
+  p.out_mask = out_mask;
+  return hip_status(dv::launch_select_topk(p, stream), "dv_select_topk launch");
+}
+
+dv_status dv_debug_hash(uint64_t seed, const int32_t *pos, int64_t pos_period, int64_t rows, int64_t vocab,
+                        uint32_t *out, hipStream_t stream) {
+  if (rows < 0 || rows > kMaxIndex || vocab < 0 || vocab > kMaxIndex) return fail(DV_ERR_SHAPE, "size out of range");
+  if (pos_period < 0 || pos_period > kMaxIndex) return fail(DV_ERR_SHAPE, "pos_period out of range");
+  if (rows > 0 && vocab > 0 && !out) return fail(DV_ERR_NULL, "out is NULL");
+  return hip_status(dv::launch_debug_hash(dv::seed_word(seed), pos, pos_period, rows, vocab, out, stream),
+                    "dv_debug_hash launch");
+}
+
+const char *dv_status_str(dv_status s) {
+  switch (s) {
+    case DV_OK: return "DV_OK";
+    case DV_ERR_NULL: return "DV_ERR_NULL";
+    case DV_ERR_SHAPE: return "DV_ERR_SHAPE";
+    case DV_ERR_DTYPE: return "DV_ERR_DTYPE";
+    case DV_ERR_ALIGN: return "DV_ERR_ALIGN";
+    case DV_ERR_ARG: return "DV_ERR_ARG";
+    case DV_ERR_WORKSPACE: return "DV_ERR_WORKSPACE";
+    case DV_ERR_UNSUPPORTED: return "DV_ERR_UNSUPPORTED";
+    case DV_ERR_HIP: return "DV_ERR_HIP";
+  }
+  return "DV_UNKNOWN_STATUS";
+}
+
+const char *dv_last_error(void) { return g_err; }
+
+int dv_version(void) { return DV_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+// Internal declarations shared by the host API (api.cpp) and the HIP kernels.
+// Not part of the public interface (include/dlmverify.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dlmverify.h"
+
+namespace dv {
+
+// ---- noise hash: 32-bit finalizer of MurmurHash3 (Appleby, public domain) ----
+// The noise word for (seed, position, vocabulary index) is built from it as
+// follows (the generator behind [SPOT]'s shared Gumbel noise; the review does
+// not say how the noise is drawn, so this keying is this library's choice):
+//   A = mix32(seed_hi ^ kSeedSalt), B = mix32(A ^ seed_lo)
+//   key(pos) = mix32(B ^ mix32(pos ^ kPosSalt))
+//   word(pos, i) = mix32(key(pos) ^ (i * kIndexStep))
+constexpr uint32_t kSeedSalt = 0x243F6A88u;
+constexpr uint32_t kPosSalt = 0x85A308D3u;
+constexpr uint32_t kIndexStep = 0x9E3779B9u;
+
+__host__ __device__ __forceinline__ uint32_t mix32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x85EBCA6Bu;
+  x ^= x >> 13;
+  x *= 0xC2B2AE35u;
+  x ^= x >> 16;
+  return x;
+}
+
+inline uint32_t seed_word(uint64_t seed) {
+  uint32_t a = mix32(static_cast<uint32_t>(seed >> 32) ^ kSeedSalt);
+  return mix32(a ^ static_cast<uint32_t>(seed));
+}
+
+// ---- per-(row, slice) partial state written to the workspace: 64 bytes ----
+// rho: reference (log2 units) the exponentials were taken against, i.e.
+//      e_i = 2^(x_i * log2e - rho); S = sum e_i; W = sum e_i * (x_i*log2e - rho);
+//      D = sum e_v,i * (a_i - b_i) (nats).
+// m: running maximum logit, cm: 16-byte chunk holding its first occurrence.
+// s: best perturbed score (log2 units), cs: its chunk.
+struct alignas(16) Partial {
+  float rho_v, S_v, W_v, D_v;
+  float rho_d, S_d, m_v, m_d;
+  float s_v, s_d;
+  int32_t cm_v, cm_d;
+  int32_t cs_v, cs_d;
+  int32_t pad0, pad1;
+};
+static_assert(sizeof(Partial) == 64, "partial state must be 64 bytes");
+
+struct VerifyLaunch {
+  const void *va;
+  const void *vb;
+  int64_t rows;
+  int64_t vocab;
+  int64_t ld;          // elements
+  int32_t bf16;
+  int32_t greedy;      // temperature == 0
+  float cT;            // log2(e) / temperature (0 when greedy)
+  uint32_t seed_b;     // seed word B
+  const int32_t *pos;  // device or NULL
+  int64_t pos_period;
+  int32_t split;       // vocabulary slices per row
+  int32_t block;       // threads per workgroup
+  int32_t shared;      // 1: noise computed once per (position, slice) in LDS
+  int32_t slice_chunks;  // 16-byte chunks per slice
+  Partial *ws;         // [rows][split] when split > 1
+  dv_row_stats out;
+};
+
+hipError_t launch_verify(const VerifyLaunch &p, hipStream_t stream);
+
+struct DecideLaunch {
+  int32_t rule;
+  float tau_kl, conf_thr;
+  int32_t mask_token;
+  int64_t rows, group_len;
+  const float *kl, *conf;
+  const int32_t *tok_v, *tok_d;
+  const uint8_t *subject;
+  const int32_t *cur_tok;
+  uint8_t *decision;
+  int32_t *out_tok, *prefix_len, *best_group;
+};
+hipError_t launch_decide(const DecideLaunch &p, hipStream_t stream);
+
+hipError_t launch_seed_score(int64_t rows, const float *u, const float *d_in, const float *d_out,
+                             const uint8_t *eligible, float *score, hipStream_t stream);
+
+struct SelectLaunch {
+  int64_t nseq, seq_len;
+  const float *score;
+  const uint8_t *eligible;
+  int32_t k, largest, use_thr;
+  float thr;
+  int32_t *out_idx;
+  float *out_val;
+  int32_t *out_count;
+  uint8_t *out_mask;
+};
+constexpr int64_t kMaxSelectLen = 16384;
+hipError_t launch_select_topk(const SelectLaunch &p, hipStream_t stream);
+
+hipError_t launch_debug_hash(uint32_t seed_b, const int32_t *pos, int64_t pos_period, int64_t rows,
+                             int64_t vocab, uint32_t *out, hipStream_t stream);
+
+}  // namespace dv

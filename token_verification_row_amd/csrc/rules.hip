@@ -1,0 +1,265 @@
+// Per-position decisions, COVER seed score, per-sequence top-k selection and
+// the noise-hash dump (gfx950). All are light next to the verification pass:
+// they touch tens of bytes per row.
+#include <climits>
+#include <cmath>
+
+#include "dv_internal.h"
+
+namespace dv {
+namespace {
+
+// ---------------------------------------------------------------- decide ----
+// Rule for one row in isolation ([DualDiffusion] §2 "Verification algorithms"
+// items 1-3; [COVER] §3 "Adaptive revision outcomes").
+__device__ __forceinline__ uint8_t rule_of_row(const DecideLaunch &p, int64_t r, int32_t cur) {
+  switch (p.rule) {
+    case DV_RULE_TRUST:
+      return DV_KEEP;
+    case DV_RULE_KL:
+      return p.kl[r] > p.tau_kl ? DV_REMASK : DV_KEEP;
+    case DV_RULE_CONF:
+      return p.conf[r] < p.conf_thr ? DV_REMASK : DV_KEEP;
+    case DV_RULE_KL_OR_CONF:
+      return (p.kl[r] > p.tau_kl || p.conf[r] < p.conf_thr) ? DV_REMASK : DV_KEEP;
+    case DV_RULE_COVER:
+      if (p.tok_v[r] == cur) return DV_KEEP;
+      return p.conf[r] >= p.conf_thr ? DV_REPLACE : DV_REMASK;
+    default:
+      return DV_NONE;
+  }
+}
+
+__device__ __forceinline__ int32_t current_token(const DecideLaunch &p, int64_t r) {
+  return p.cur_tok ? p.cur_tok[r] : p.tok_d[r];
+}
+
+__device__ __forceinline__ bool is_subject(const DecideLaunch &p, int64_t r) {
+  return p.subject == nullptr || p.subject[r] != 0;
+}
+
+__device__ __forceinline__ void emit(const DecideLaunch &p, int64_t r, uint8_t d, int32_t cur) {
+  if (p.decision) p.decision[r] = d;
+  if (p.out_tok) {
+    int32_t t = cur;
+    if (d == DV_REPLACE) t = p.tok_v[r];
+    if (d == DV_REMASK) t = p.mask_token;
+    p.out_tok[r] = t;
+  }
+}
+
+// One wave per group of group_len consecutive rows (a candidate). Pass 1 finds
+// the first decided row that breaks the group (coupled acceptance: tokens
+// disagree; other rules: decision is not KEEP); pass 2 writes the decisions.
+// With group_len == 0 the rows are cut into 64-row tiles and no prefix exists.
+__global__ __launch_bounds__(256) void decide_kernel(DecideLaunch p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t G = p.group_len > 0 ? p.group_len : 64;
+  const int64_t ngroups = (p.rows + G - 1) / G;
+  if (g >= ngroups) return;
+  const int64_t r0 = g * G;
+  const int64_t r1 = min(r0 + G, p.rows);
+  const bool coupled = p.rule == DV_RULE_COUPLED_ACCEPT;
+
+  int64_t first = G;  // offset of the first breaking row
+  if (coupled || p.prefix_len) {
+    for (int64_t base = r0; base < r1 && first == G; base += 64) {
+      const int64_t r = base + lane;
+      bool brk = false;
+      if (r < r1 && is_subject(p, r)) {
+        const int32_t cur = current_token(p, r);
+        brk = coupled ? (p.tok_v[r] != cur) : (rule_of_row(p, r, cur) != DV_KEEP);
+      }
+      const unsigned long long m = __ballot(brk);
+      if (m) first = (base - r0) + __ffsll(m) - 1;
+    }
+  }
+  for (int64_t base = r0; base < r1; base += 64) {
+    const int64_t r = base + lane;
+    if (r >= r1) continue;
+    const int32_t cur = current_token(p, r);
+    uint8_t d = DV_NONE;
+    if (is_subject(p, r)) {
+      if (coupled) {
+        const int64_t j = r - r0;
+        d = j < first ? DV_KEEP : (j == first ? DV_REPLACE : DV_REMASK);
+      } else {
+        d = rule_of_row(p, r, cur);
+      }
+    }
+    emit(p, r, d, cur);
+  }
+  if (p.prefix_len && lane == 0) p.prefix_len[g] = static_cast<int32_t>(first);
+}
+
+// Longest accepted prefix over all groups, lowest group index on ties.
+__global__ __launch_bounds__(1024) void best_group_kernel(const int32_t *prefix, int64_t ngroups, int32_t *best) {
+  __shared__ long long s_key[1024];
+  long long key = LLONG_MIN;
+  for (int64_t g = threadIdx.x; g < ngroups; g += blockDim.x) {
+    // larger prefix first; among equal prefixes the smaller index gives the larger key
+    const long long k = (static_cast<long long>(prefix[g]) << 32) | static_cast<long long>(0xFFFFFFFFu - static_cast<uint32_t>(g));
+    key = k > key ? k : key;
+  }
+  s_key[threadIdx.x] = key;
+  __syncthreads();
+  for (int o = blockDim.x / 2; o > 0; o >>= 1) {
+    if (threadIdx.x < o) {
+      const long long other = s_key[threadIdx.x + o];
+      if (other > s_key[threadIdx.x]) s_key[threadIdx.x] = other;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    best[0] = ngroups > 0 ? static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(s_key[0] & 0xFFFFFFFFll)) : -1;
+  }
+}
+
+// ------------------------------------------------------------ seed score ----
+// [COVER] §2, the Score equation: u (1 + d_in) / (1 + d_out).
+__global__ __launch_bounds__(256) void seed_score_kernel(int64_t rows, const float *u, const float *d_in,
+                                                        const float *d_out, const uint8_t *eligible, float *score) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (r >= rows) return;
+  float s = -INFINITY;
+  if (eligible == nullptr || eligible[r] != 0) s = u[r] * (1.0f + d_in[r]) / (1.0f + d_out[r]);
+  score[r] = s;
+}
+
+// --------------------------------------------------------------- top-k ----
+// Keys sort descending: the upper word orders the scores (largest or smallest
+// first), the lower word is ~index so that equal scores go to the lower index.
+// Ineligible positions get key 0, below every real key.
+__device__ __forceinline__ unsigned long long select_key(float s, uint32_t i, int32_t largest) {
+  uint32_t b = __float_as_uint(s);
+  if (b == 0x80000000u) b = 0u;  // -0 ranks as +0
+  uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);  // increasing in s
+  if (!largest) ord = ~ord;
+  return (static_cast<unsigned long long>(ord) << 32) | static_cast<unsigned long long>(0xFFFFFFFFu - i);
+}
+
+// One workgroup per sequence: bitonic sort of pow2 keys in LDS.
+__global__ __launch_bounds__(1024) void select_topk_kernel(SelectLaunch p, int32_t pow2) {
+  extern __shared__ unsigned long long keys[];
+  uint8_t *flags = reinterpret_cast<uint8_t *>(keys + pow2);
+  __shared__ int s_count;
+  const int64_t seq = blockIdx.x;
+  const int32_t L = static_cast<int32_t>(p.seq_len);
+  const float *sc = p.score + seq * p.seq_len;
+  const uint8_t *el = p.eligible ? p.eligible + seq * p.seq_len : nullptr;
+  for (int32_t i = threadIdx.x; i < pow2; i += blockDim.x) {
+    unsigned long long k = 0;
+    if (i < L && (el == nullptr || el[i] != 0)) k = select_key(sc[i], static_cast<uint32_t>(i), p.largest);
+    keys[i] = k;
+  }
+  if (threadIdx.x == 0) s_count = p.k;
+  for (int32_t size = 2; size <= pow2; size <<= 1) {
+    for (int32_t stride = size >> 1; stride > 0; stride >>= 1) {
+      __syncthreads();
+      for (int32_t t = threadIdx.x; t < (pow2 >> 1); t += blockDim.x) {
+        const int32_t i = 2 * t - (t & (stride - 1));
+        const int32_t j = i + stride;
+        const bool desc = (i & size) == 0;
+        const unsigned long long a = keys[i], b = keys[j];
+        if ((a < b) == desc && a != b) {
+          keys[i] = b;
+          keys[j] = a;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // the kept entries are a prefix of the sorted list: find where it ends
+  for (int32_t j = threadIdx.x; j < p.k; j += blockDim.x) {
+    const unsigned long long k = keys[j];
+    bool keep = k != 0;
+    if (keep && p.use_thr) {
+      const float v = sc[0xFFFFFFFFu - static_cast<uint32_t>(k & 0xFFFFFFFFull)];
+      keep = p.largest ? (v > p.thr) : (v < p.thr);
+    }
+    if (!keep) atomicMin(&s_count, j);
+  }
+  for (int32_t i = threadIdx.x; i < L; i += blockDim.x) flags[i] = 0;
+  __syncthreads();
+  const int32_t count = s_count;
+  for (int32_t j = threadIdx.x; j < p.k; j += blockDim.x) {
+    int32_t idx = -1;
+    float val = __builtin_nanf("");
+    if (j < count) {
+      idx = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(keys[j] & 0xFFFFFFFFull));
+      val = sc[idx];
+      flags[idx] = 1;
+    }
+    if (p.out_idx) p.out_idx[seq * p.k + j] = idx;
+    if (p.out_val) p.out_val[seq * p.k + j] = val;
+  }
+  if (threadIdx.x == 0 && p.out_count) p.out_count[seq] = count;
+  __syncthreads();
+  if (p.out_mask) {
+    for (int32_t i = threadIdx.x; i < L; i += blockDim.x) p.out_mask[seq * p.seq_len + i] = flags[i];
+  }
+}
+
+// ------------------------------------------------------------- noise dump ----
+__global__ __launch_bounds__(256) void debug_hash_kernel(uint32_t seed_b, const int32_t *pos, int64_t pos_period,
+                                                        int64_t rows, int64_t vocab, uint32_t *out) {
+  const int64_t n = rows * vocab;
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < n;
+       t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t r = t / vocab, i = t % vocab;
+    const int32_t ps = pos ? pos[r] : (pos_period > 0 ? static_cast<int32_t>(r % pos_period) : static_cast<int32_t>(r));
+    const uint32_t key = mix32(seed_b ^ mix32(static_cast<uint32_t>(ps) ^ kPosSalt));
+    out[t] = mix32(key ^ (static_cast<uint32_t>(i) * kIndexStep));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decide(const DecideLaunch &p, hipStream_t stream) {
+  const int64_t G = p.group_len > 0 ? p.group_len : 64;
+  const int64_t ngroups = (p.rows + G - 1) / G;
+  if (p.rows > 0) {
+    const unsigned blocks = static_cast<unsigned>((ngroups + 3) / 4);
+    hipLaunchKernelGGL(decide_kernel, dim3(blocks), dim3(256), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.best_group == nullptr) return hipSuccess;
+  hipLaunchKernelGGL(best_group_kernel, dim3(1), dim3(1024), 0, stream, p.prefix_len, ngroups, p.best_group);
+  return hipGetLastError();
+}
+
+hipError_t launch_seed_score(int64_t rows, const float *u, const float *d_in, const float *d_out,
+                             const uint8_t *eligible, float *score, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  const unsigned blocks = static_cast<unsigned>((rows + 255) / 256);
+  hipLaunchKernelGGL(seed_score_kernel, dim3(blocks), dim3(256), 0, stream, rows, u, d_in, d_out, eligible, score);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_topk(const SelectLaunch &p, hipStream_t stream) {
+  if (p.nseq == 0) return hipSuccess;
+  int32_t pow2 = 2;
+  while (pow2 < p.seq_len) pow2 <<= 1;
+  const size_t lds = static_cast<size_t>(pow2) * sizeof(unsigned long long) + static_cast<size_t>(p.seq_len);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&select_topk_kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  const int threads = pow2 >= 2048 ? 1024 : (pow2 / 2 < 64 ? 64 : pow2 / 2);
+  hipLaunchKernelGGL(select_topk_kernel, dim3(static_cast<unsigned>(p.nseq)), dim3(threads), lds, stream, p, pow2);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_hash(uint32_t seed_b, const int32_t *pos, int64_t pos_period, int64_t rows, int64_t vocab,
+                             uint32_t *out, hipStream_t stream) {
+  const int64_t n = rows * vocab;
+  if (n == 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(debug_hash_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, seed_b, pos,
+                     pos_period, rows, vocab, out);
+  return hipGetLastError();
+}
+
+}  // namespace dv

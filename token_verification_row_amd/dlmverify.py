@@ -1,0 +1,296 @@
+"""ctypes binding of libdlmverify (include/dlmverify.h), same names as the C API.
+
+Argument marshalling only: each function checks device, dtype and layout of
+the torch tensors it is given, allocates output tensors where the caller did
+not pass them, and calls the C entry point on the current HIP stream. Every
+step of the computation runs in the library's HIP kernels. There is no CPU
+fallback: without the built library, or without a GPU, the calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime the library binds to (same soname)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdlmverify.so")
+
+DV_OK, DV_ERR_NULL, DV_ERR_SHAPE, DV_ERR_DTYPE, DV_ERR_ALIGN, DV_ERR_ARG, \
+    DV_ERR_WORKSPACE, DV_ERR_UNSUPPORTED, DV_ERR_HIP = range(9)
+DV_FP32, DV_BF16 = 0, 1
+DV_NONE, DV_KEEP, DV_REPLACE, DV_REMASK = 0, 1, 2, 3
+DV_RULE_TRUST, DV_RULE_KL, DV_RULE_CONF, DV_RULE_KL_OR_CONF, DV_RULE_COVER, DV_RULE_COUPLED_ACCEPT = range(6)
+RULES = {"TRUST": 0, "KL": 1, "CONF": 2, "KL_OR_CONF": 3, "COVER": 4, "COUPLED_ACCEPT": 5}
+STAT_FIELDS = ("lse_v", "lse_d", "kl", "entropy", "conf", "argmax_v", "argmax_d", "tok_v", "tok_d")
+_FLOAT_FIELDS = {"lse_v", "lse_d", "kl", "entropy", "conf"}
+
+
+class DVError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class dv_logits(ctypes.Structure):
+    _fields_ = [("verifier", ctypes.c_void_p), ("drafter", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("rows", ctypes.c_int64), ("vocab", ctypes.c_int64),
+                ("ld", ctypes.c_int64)]
+
+
+class dv_noise(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("reserved", ctypes.c_int32), ("seed", ctypes.c_uint64),
+                ("pos", ctypes.c_void_p), ("pos_period", ctypes.c_int64)]
+
+
+class dv_row_stats(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in STAT_FIELDS]
+
+
+class dv_tuning(ctypes.Structure):
+    _fields_ = [("split", ctypes.c_int32), ("block", ctypes.c_int32), ("shared_noise", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class dv_decide_args(ctypes.Structure):
+    _fields_ = [("rule", ctypes.c_int32), ("tau_kl", ctypes.c_float), ("conf_thr", ctypes.c_float),
+                ("mask_token", ctypes.c_int32), ("rows", ctypes.c_int64), ("group_len", ctypes.c_int64)]
+
+
+_P = ctypes.c_void_p
+_SIGNATURES = {
+    "dv_verify_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(dv_logits), ctypes.POINTER(dv_noise),
+                                                 ctypes.POINTER(dv_tuning), ctypes.POINTER(ctypes.c_size_t)]),
+    "dv_verify_rows": (ctypes.c_int, [ctypes.POINTER(dv_logits), ctypes.POINTER(dv_noise),
+                                      ctypes.POINTER(dv_tuning), ctypes.POINTER(dv_row_stats), _P,
+                                      ctypes.c_size_t, _P]),
+    "dv_decide": (ctypes.c_int, [ctypes.POINTER(dv_decide_args), ctypes.POINTER(dv_row_stats), _P, _P, _P, _P,
+                                 _P, _P, _P]),
+    "dv_seed_score": (ctypes.c_int, [ctypes.c_int64, _P, _P, _P, _P, _P, _P]),
+    "dv_select_topk": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, _P, _P, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_int32, ctypes.c_float, _P, _P, _P, _P, _P]),
+    "dv_debug_hash": (ctypes.c_int, [ctypes.c_uint64, _P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P]),
+    "dv_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "dv_last_error": (ctypes.c_char_p, []),
+    "dv_version": (ctypes.c_int, []),
+}
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libdlmverify.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
+                               "(token_verification_row_amd/build_lib.py)")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status: int, call: str):
+    if status != DV_OK:
+        lib = load_library()
+        raise DVError(status, f"{call}: {lib.dv_status_str(status).decode()}: {lib.dv_last_error().decode()}")
+
+
+def dv_status_str(status: int) -> str:
+    return load_library().dv_status_str(status).decode()
+
+
+def dv_last_error() -> str:
+    return load_library().dv_last_error().decode()
+
+
+def dv_version() -> int:
+    return load_library().dv_version()
+
+
+def _stream_handle(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need_cuda(t, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+
+
+def _logits_desc(verifier, drafter, vocab):
+    _need_cuda(verifier, "verifier")
+    _need_cuda(drafter, "drafter")
+    if verifier.dim() != 2 or drafter.shape != verifier.shape:
+        raise ValueError("verifier and drafter must both be [rows, ld]")
+    if verifier.dtype != drafter.dtype or verifier.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("logits must both be float32 or both bfloat16")
+    if verifier.stride() != drafter.stride() or verifier.stride(1) != 1:
+        raise ValueError("logit rows must be contiguous with one common row stride")
+    rows, width = verifier.shape
+    ld = verifier.stride(0) if rows > 0 else width
+    vocab = width if vocab is None else int(vocab)
+    if vocab > width:
+        raise ValueError(f"vocab {vocab} exceeds the row width {width}")
+    return dv_logits(verifier=verifier.data_ptr(), drafter=drafter.data_ptr(),
+                     dtype=DV_BF16 if verifier.dtype == torch.bfloat16 else DV_FP32, reserved=0,
+                     rows=rows, vocab=vocab, ld=ld)
+
+
+def _noise_desc(temperature, seed, pos, pos_period):
+    if pos is not None:
+        _need_cuda(pos, "pos")
+        if pos.dtype != torch.int32 or not pos.is_contiguous():
+            raise TypeError("pos must be a contiguous int32 tensor")
+    return dv_noise(temperature=float(temperature), reserved=0, seed=int(seed) & 0xFFFFFFFFFFFFFFFF,
+                    pos=None if pos is None else pos.data_ptr(), pos_period=int(pos_period))
+
+
+def _tuning_desc(tuning):
+    if tuning is None:
+        return None
+    t = dict(tuning)
+    return dv_tuning(split=int(t.get("split", 0)), block=int(t.get("block", 0)),
+                     shared_noise=int(t.get("shared_noise", -1)), reserved=0)
+
+
+def dv_verify_workspace_bytes(verifier, drafter, temperature=0.0, seed=0, pos=None, pos_period=0, *,
+                              vocab=None, tuning=None) -> int:
+    d = _logits_desc(verifier, drafter, vocab)
+    n = _noise_desc(temperature, seed, pos, pos_period)
+    t = _tuning_desc(tuning)
+    out = ctypes.c_size_t(0)
+    _check(load_library().dv_verify_workspace_bytes(ctypes.byref(d), ctypes.byref(n),
+                                                    None if t is None else ctypes.byref(t), ctypes.byref(out)),
+           "dv_verify_workspace_bytes")
+    return out.value
+
+
+def dv_verify_rows(verifier, drafter, temperature=0.0, seed=0, pos=None, pos_period=0, *, vocab=None,
+                   outputs=STAT_FIELDS, out=None, workspace=None, tuning=None):
+    """Row statistics of [rows, ld] verifier/drafter logits. Returns a dict of
+    tensors (float32 for lse_v, lse_d, kl, entropy, conf; int32 for the rest)."""
+    d = _logits_desc(verifier, drafter, vocab)
+    n = _noise_desc(temperature, seed, pos, pos_period)
+    t = _tuning_desc(tuning)
+    rows, dev = d.rows, verifier.device
+    res = dict(out or {})
+    for f in outputs:
+        if f not in STAT_FIELDS:
+            raise KeyError(f)
+        if f not in res:
+            res[f] = torch.empty(rows, dtype=torch.float32 if f in _FLOAT_FIELDS else torch.int32, device=dev)
+    for f, v in res.items():
+        _need_cuda(v, f)
+        want = torch.float32 if f in _FLOAT_FIELDS else torch.int32
+        if v.dtype != want or v.numel() < rows or not v.is_contiguous():
+            raise TypeError(f"output {f} must be a contiguous {want} tensor of >= {rows} elements")
+    st = dv_row_stats(**{f: (res[f].data_ptr() if f in res else None) for f in STAT_FIELDS})
+    lib = load_library()
+    need = ctypes.c_size_t(0)
+    _check(lib.dv_verify_workspace_bytes(ctypes.byref(d), ctypes.byref(n), None if t is None else ctypes.byref(t),
+                                         ctypes.byref(need)), "dv_verify_workspace_bytes")
+    if need.value and workspace is None:
+        workspace = torch.empty(need.value + 256, dtype=torch.uint8, device=dev)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        base = workspace.data_ptr()
+        off = (-base) % 256
+        ws_ptr, ws_bytes = base + off, workspace.numel() * workspace.element_size() - off
+    _check(lib.dv_verify_rows(ctypes.byref(d), ctypes.byref(n), None if t is None else ctypes.byref(t),
+                              ctypes.byref(st), ws_ptr, ws_bytes, _stream_handle(dev)), "dv_verify_rows")
+    res["_workspace"] = workspace  # keep the scratch alive until the caller drops the result
+    return res
+
+
+def dv_decide(rule, stats, *, rows=None, tau_kl=0.0, conf_thr=0.0, mask_token=-1, subject=None, cur_tok=None,
+              group_len=0, want_prefix=False, want_best=False):
+    """Per-position decisions. ``stats`` is a dict with kl / conf / tok_v / tok_d
+    tensors. Returns (decision uint8, out_tok int32, prefix int32 or None, best int32[1] or None)."""
+    rule = RULES[rule] if isinstance(rule, str) else int(rule)
+    ref = next(v for k, v in stats.items() if k in STAT_FIELDS and v is not None)
+    rows = ref.numel() if rows is None else int(rows)
+    dev = ref.device
+    for name, v in (("subject", subject), ("cur_tok", cur_tok)):
+        if v is not None:
+            _need_cuda(v, name)
+    if subject is not None and subject.dtype != torch.uint8:
+        raise TypeError("subject must be uint8")
+    if cur_tok is not None and cur_tok.dtype != torch.int32:
+        raise TypeError("cur_tok must be int32")
+    decision = torch.empty(rows, dtype=torch.uint8, device=dev)
+    out_tok = torch.empty(rows, dtype=torch.int32, device=dev)
+    ngroups = rows // group_len if group_len > 0 else 0
+    prefix = torch.empty(max(ngroups, 1), dtype=torch.int32, device=dev) if (want_prefix or want_best) else None
+    best = torch.empty(1, dtype=torch.int32, device=dev) if want_best else None
+    args = dv_decide_args(rule=rule, tau_kl=float(tau_kl), conf_thr=float(conf_thr), mask_token=int(mask_token),
+                          rows=rows, group_len=int(group_len))
+    st = dv_row_stats(**{f: (stats[f].data_ptr() if stats.get(f) is not None else None) for f in STAT_FIELDS})
+    _check(load_library().dv_decide(ctypes.byref(args), ctypes.byref(st), _ptr(subject), _ptr(cur_tok),
+                                    _ptr(decision), _ptr(out_tok), _ptr(prefix), _ptr(best), _stream_handle(dev)),
+           "dv_decide")
+    if prefix is not None:
+        prefix = prefix[:ngroups]
+    return decision, out_tok, prefix, best
+
+
+def dv_seed_score(u, d_in, d_out, eligible=None, *, out=None):
+    """COVER seed score u (1 + d_in) / (1 + d_out), -inf where not eligible."""
+    for name, v in (("u", u), ("d_in", d_in), ("d_out", d_out)):
+        _need_cuda(v, name)
+        if v.dtype != torch.float32 or not v.is_contiguous():
+            raise TypeError(f"{name} must be contiguous float32")
+    rows = u.numel()
+    if d_in.numel() != rows or d_out.numel() != rows:
+        raise ValueError("u, d_in and d_out must have the same length")
+    if eligible is not None:
+        _need_cuda(eligible, "eligible")
+        if eligible.dtype != torch.uint8:
+            raise TypeError("eligible must be uint8")
+    score = torch.empty(rows, dtype=torch.float32, device=u.device) if out is None else out
+    _check(load_library().dv_seed_score(rows, _ptr(u), _ptr(d_in), _ptr(d_out), _ptr(eligible), _ptr(score),
+                                        _stream_handle(u.device)), "dv_seed_score")
+    return score
+
+
+def dv_select_topk(score, k, *, eligible=None, largest=True, use_thr=False, thr=0.0, want_mask=False):
+    """Per-sequence top-k of score [nseq, L]. Returns (idx, val, count, mask or None)."""
+    _need_cuda(score, "score")
+    if score.dim() != 2 or score.dtype != torch.float32 or not score.is_contiguous():
+        raise TypeError("score must be a contiguous float32 [nseq, L] tensor")
+    nseq, L = score.shape
+    if eligible is not None:
+        _need_cuda(eligible, "eligible")
+        if eligible.dtype != torch.uint8 or eligible.shape != score.shape or not eligible.is_contiguous():
+            raise TypeError("eligible must be contiguous uint8 shaped like score")
+    dev = score.device
+    kk = max(int(k), 1)
+    idx = torch.empty((nseq, kk), dtype=torch.int32, device=dev)
+    val = torch.empty((nseq, kk), dtype=torch.float32, device=dev)
+    cnt = torch.empty(max(nseq, 1), dtype=torch.int32, device=dev)
+    mask = torch.empty((nseq, L), dtype=torch.uint8, device=dev) if want_mask else None
+    _check(load_library().dv_select_topk(nseq, L, _ptr(score), _ptr(eligible), int(k), int(bool(largest)),
+                                         int(bool(use_thr)), float(thr), _ptr(idx), _ptr(val), _ptr(cnt),
+                                         _ptr(mask), _stream_handle(dev)), "dv_select_topk")
+    return idx, val, cnt[:nseq], mask
+
+
+def dv_debug_hash(seed, rows, vocab, *, pos=None, pos_period=0, device="cuda"):
+    """Noise hash words [rows, vocab] (returned as int32 tensor holding the uint32 bits)."""
+    if pos is not None:
+        _need_cuda(pos, "pos")
+        if pos.dtype != torch.int32:
+            raise TypeError("pos must be int32")
+        device = pos.device
+    out = torch.empty((rows, vocab), dtype=torch.int32, device=device)
+    _check(load_library().dv_debug_hash(int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(pos), int(pos_period), int(rows),
+                                        int(vocab), _ptr(out), _stream_handle(out.device)), "dv_debug_hash")
+    return out

@@ -1,0 +1,199 @@
+"""Throughput of the verification hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic logits:
+dv_verify_rows (the fused verify pass), dv_decide, dv_seed_score and
+dv_select_topk. The default workload is the SPOT-style tree of 64 candidate
+block states x 32 positions over a 151 936-token vocabulary, bf16, T = 1,
+noise shared per position (coupled-noise acceptance per candidate).
+
+Prints ONE JSON line: verified rows/s for the whole step, the verify pass's
+achieved HBM bandwidth against the 8 TB/s peak (timed live with HIP events on
+the stream the kernels run on), and the CPU oracle's rows/s on a sample of the
+same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+STAT_BYTES_PER_ROW = 36      # 5 float32 + 4 int32 outputs
+
+
+def _oracle_block(args):
+    """CPU oracle over a block of rows (runs in a worker process)."""
+    a, b, temperature, seed, pos, group_len = args
+    from oracle import decide as odecide
+    from oracle import noise as onoise
+    from oracle import rowstats
+
+    a64 = rowstats.as_float64(a, "bf16")
+    b64 = rowstats.as_float64(b, "bf16")
+    st = rowstats.row_stats(a64, b64)
+    st.update(onoise.gumbel_tokens(a64, b64, temperature, seed, pos))
+    if group_len:
+        odecide.decide(odecide.COUPLED_ACCEPT, st, mask_token=-1, group_len=group_len)
+    return len(a)
+
+
+def cpu_baseline(a_rows, b_rows, w, pos, workers):
+    """Time the oracle (as it is) on the given rows across ``workers`` processes."""
+    import multiprocessing as mp
+
+    G = w.group_len or 32
+    tasks = [(a_rows[s:s + G], b_rows[s:s + G], w.temperature, w.seed, pos[s:s + G], w.group_len)
+             for s in range(0, len(a_rows), G)]
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(workers) as pool:
+        pool.map(_oracle_block, tasks[:workers])          # warm the workers up (imports)
+        t0 = time.perf_counter()
+        n = sum(pool.map(_oracle_block, tasks))
+        dt = time.perf_counter() - t0
+    return n, dt
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=4, choices=[2, 3, 4, 5])
+    ap.add_argument("--cpu-rows", type=int, default=1024, help="rows of the workload the CPU oracle is timed on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copies", type=int, default=0, help="input copies rotated between steps (0: auto)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the path, run a plain device copy of MIB MiB --steps times (reference for "
+                         "the HBM byte counters of a profiler)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; the verification path has no multi-GPU mode (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import token_verification_row_amd as dv
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dv.load_library()
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": args.steps}), flush=True)
+        return 0
+    w = W.workload(args.workload)
+    R, V = w.rows, w.V
+    # rotate enough copies that one step never finds its inputs in the 256 MB last-level cache
+    copies = args.copies or max(2, -(-1_000_000_000 // w.input_bytes) + 1)
+    inputs = [W.make_logits_torch(w, dev)]
+    for _ in range(copies - 1):
+        inputs.append((inputs[0][0].clone(), inputs[0][1].clone()))
+    period = w.pos_period
+    d_in_np, d_out_np = (np.random.default_rng(1).random(R, dtype=np.float32) for _ in range(2))
+    d_in = torch.from_numpy(d_in_np).to(dev)
+    d_out = torch.from_numpy(d_out_np).to(dev)
+    outs = [dv.dv_verify_rows(*inputs[0], temperature=w.temperature, seed=w.seed, pos_period=period)
+            for _ in range(2)]
+    seq_len = w.group_len or w.L
+    nseq = R // seq_len
+    k = min(w.topk or 8, seq_len)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        a, b = inputs[i % copies]
+        out = outs[i % 2]
+        if ev is not None:
+            ev[0].record(stream)
+        got = dv.dv_verify_rows(a, b, temperature=w.temperature, seed=w.seed, pos_period=period, out=out,
+                                workspace=out.get("_workspace"))
+        if ev is not None:
+            ev[1].record(stream)
+        if w.group_len:
+            dv.dv_decide("COUPLED_ACCEPT", got, mask_token=-1, group_len=w.group_len, want_prefix=True,
+                         want_best=True)
+        else:
+            dv.dv_decide("KL_OR_CONF", got, tau_kl=0.05, conf_thr=0.9, mask_token=-1)
+        score = dv.dv_seed_score(got["entropy"], d_in, d_out)
+        dv.dv_select_topk(score.view(nseq, seq_len), k)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    verify_ms = [s.elapsed_time(e) for s, e in events]
+    ms_per_step = ms_total / args.steps
+    verify_us = 1000.0 * float(np.mean(verify_ms))
+    alg_bytes = 2 * R * V * w.elt + STAT_BYTES_PER_ROW * R
+    achieved = alg_bytes / (verify_us * 1e-6) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        n = min(args.cpu_rows, R)
+        rows = torch.arange(n, device=dev)
+        a_rows = inputs[0][0][rows].view(torch.int16).cpu().numpy().view(np.uint16)
+        b_rows = inputs[0][1][rows].view(torch.int16).cpu().numpy().view(np.uint16)
+        pos = W.positions(w)[:n]
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        done, dt = cpu_baseline(a_rows, b_rows, w, pos, workers)
+        cpu = {"value": done / dt, "unit": "rows/s", "cores": workers, "kind": "oracle",
+               "sample": f"first {done} rows ({done // (w.group_len or w.L)} "
+                         f"{'candidates' if w.group_len else 'sequences'}) of the same workload: row statistics, "
+                         f"shared-Gumbel tokens{' and coupled acceptance' if w.group_len else ''} in float64, "
+                         f"{workers} worker processes, {dt:.1f} s wall"}
+
+    line = {
+        "metric": "verified rows/s and achieved HBM GB/s (% of peak), fused verify kernel",
+        "value": R / (ms_per_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.B} x {w.L} rows, vocab {V}, {w.dtype} logits, T={w.temperature}"
+                               + (f", noise shared per position (period {period}), coupled acceptance per "
+                                  f"{w.group_len}-row candidate" if period else ""),
+                   "rows": R, "vocab": V, "input_copies": copies,
+                   "step": "dv_verify_rows + dv_decide + dv_seed_score + dv_select_topk"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "dv_verify_rows (verify pass + split merge)", "avg_us": verify_us,
+                     "bytes_per_launch": alg_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

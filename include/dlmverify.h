@@ -112,11 +112,12 @@ typedef struct dv_row_stats {
  * zero field keeps its automatic value. Results do not depend on it beyond
  * float rounding: integer outputs are identical for every shape.
  *   split         vocabulary slices per row (1..64)
- *   block         threads per workgroup of the shared-noise kernel (256 or
- *                 512; the per-row kernel always uses 256)
- *   shared_noise  1: compute the noise once per (position, slice) in LDS and
- *                 reuse it for every row at that position (needs pos == NULL
- *                 and pos_period > 0); 0: compute it per row; -1: automatic */
+ *   block         threads per workgroup: 0 or 256
+ *   shared_noise  1: rows share positions (needs temperature > 0, pos == NULL
+ *                 and pos_period > 0); a table of the largest noise value of
+ *                 each (position, 16-byte chunk) lets the pass skip the
+ *                 Gumbel scores of chunks that cannot hold a token;
+ *                 0: every chunk is scored; -1: automatic */
 typedef struct dv_tuning {
   int32_t split;
   int32_t block;

@@ -106,11 +106,19 @@ def test_workspace_query(lib):
                                          ctypes.byref(out)) == B.DV_OK
     assert out.value == 0
     assert lib.dv_verify_workspace_bytes(ctypes.byref(lg), ctypes.byref(nz), None, None) == B.DV_ERR_NULL
-    # shared noise: one workgroup per (position, slice); slices keep the LDS copy of the noise small
+    # rows sharing positions: a table of the largest noise value per (position, 16-byte chunk) comes first
     lg = _logits(rows=2048, vocab=151936, ld=151936)
     nz = _noise(T=1.0, period=32)
     assert lib.dv_verify_workspace_bytes(ctypes.byref(lg), ctypes.byref(nz), None, ctypes.byref(out)) == B.DV_OK
-    assert out.value == 2048 * 16 * 64
+    table = 32 * (151936 // 8) * 4
+    assert out.value == table + 2048 * 2 * 64                  # two slices per row
+    t = B.dv_tuning(split=4, block=0, shared_noise=1, reserved=0)
+    assert lib.dv_verify_workspace_bytes(ctypes.byref(lg), ctypes.byref(nz), ctypes.byref(t),
+                                         ctypes.byref(out)) == B.DV_OK
+    assert out.value == table + 2048 * 4 * 64
+    lg = _logits(rows=2048, vocab=1001, ld=1008)                 # 126 chunks, the last one partly filled
+    assert lib.dv_verify_workspace_bytes(ctypes.byref(lg), ctypes.byref(nz), None, ctypes.byref(out)) == B.DV_OK
+    assert out.value == ((32 * 126 * 4 + 255) // 256) * 256
 
 
 def _decide(lib, rule=B.DV_RULE_KL, rows=8, group_len=0, tau=0.1, thr=0.9, stats=None, subject=None, cur=None,

@@ -12,6 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdlmverify.so")
 SOURCES = ["api.cpp", "verify.hip", "rules.hip"]
+BUILD_DIR = os.path.join(HERE, "_build")
 
 # gfx950 only; packed fp32 arithmetic is switched off for the device code and
 # floating-point contraction is off so that every fused multiply-add in the
@@ -22,11 +23,16 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-ffp-contract=off",
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# The verification kernels take finite logits only (documented in the header),
+# so their device code may assume no NaN: max() then needs no quieting of its
+# operands.
+PER_SOURCE_FLAGS = {
+    "verify.hip": ["-Xarch_device", "-fno-honor-nans"],
+}
 
 
 def hipcc() -> str:
@@ -36,11 +42,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libdlmverify)")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the library; returns its path. Always recompiles."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"),
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,6 +52,20 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile the library; returns its path. Always recompiles."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    cc = hipcc()
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD_DIR, src.rsplit(".", 1)[0] + ".o")
+        _run([cc, *HIPCC_FLAGS, *PER_SOURCE_FLAGS.get(src, []), *extra_flags, "-I", os.path.join(ROOT, "include"),
+              "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

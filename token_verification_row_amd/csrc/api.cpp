@@ -37,13 +37,15 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Launch shape of dv_verify_rows, decided from the sizes alone.
 struct Geometry {
   int32_t split = 1;
-  int32_t block = 256;
-  int32_t shared = 0;
+  int32_t pruned = 0;       // chunk-max noise table + bound + queued scoring
   int32_t slice_chunks = 0;
+  int64_t cmax_rows = 0;
+  int64_t cmax_ld = 0;
+  size_t cmax_bytes = 0;    // at the start of the workspace, 256-byte aligned size
   size_t workspace = 0;
 };
 
-constexpr size_t kMaxSharedLds = 160 * 1024;
+constexpr size_t kMaxTableBytes = size_t(1) << 30;
 
 dv_status check_logits(const dv_logits *x, bool need_ptrs) {
   if (!x) return fail(DV_ERR_NULL, "logits descriptor is NULL");
@@ -77,50 +79,38 @@ dv_status choose_geometry(const dv_logits *x, const dv_noise *n, const dv_tuning
   const int32_t want_shared = t ? t->shared_noise : -1;
   if (t) {
     if (t->split < 0 || t->split > 64) return fail(DV_ERR_ARG, "tuning.split must be 0..64");
-    if (t->block != 0 && t->block != 256 && t->block != 512 && t->block != 1024)
-      return fail(DV_ERR_ARG, "tuning.block must be 0, 256, 512 or 1024");
+    if (t->block != 0 && t->block != 256) return fail(DV_ERR_ARG, "tuning.block must be 0 or 256");
     if (want_shared < -1 || want_shared > 1) return fail(DV_ERR_ARG, "tuning.shared_noise must be -1, 0 or 1");
     if (want_shared == 1 && !can_share)
       return fail(DV_ERR_ARG, "shared noise needs temperature > 0, pos == NULL and pos_period > 0");
   }
+  const int64_t npos = can_share ? (n->pos_period < x->rows ? n->pos_period : x->rows) : 0;
+  const size_t cmax_bytes = can_share ? ((static_cast<size_t>(npos) * nch * 4 + 255) / 256) * 256 : 0;
   if (want_shared == 1) {
-    g.shared = 1;
-  } else if (want_shared == 0) {
-    g.shared = 0;
-  } else {
-    // share when each position carries several rows
-    g.shared = can_share && x->rows >= 2 * n->pos_period ? 1 : 0;
+    if (cmax_bytes > kMaxTableBytes) return fail(DV_ERR_ARG, "noise table of %zu bytes is too large", cmax_bytes);
+    g.pruned = 1;
+  } else if (want_shared == -1) {
+    // positions carrying several rows amortize the table
+    g.pruned = can_share && x->rows >= 2 * n->pos_period && cmax_bytes <= kMaxTableBytes ? 1 : 0;
   }
-  int64_t split;
-  if (g.shared) {
-    const int64_t groups = n->pos_period < x->rows ? n->pos_period : x->rows;
-    // aim for ~2 workgroups per CU, and a slice whose noise fits 64 KiB of LDS
-    split = (512 + groups - 1) / (groups > 0 ? groups : 1);
-    const int64_t min_split = (nch * N * 4 + 65535) / 65536;
-    if (split < min_split) split = min_split;
-    g.block = 512;
-  } else {
-    // aim for ~8192 waves in flight, each slice at least 256 chunks
-    split = x->rows > 0 ? (8192 + x->rows - 1) / x->rows : 1;
-    const int64_t max_by_len = nch / 256 > 0 ? nch / 256 : 1;
-    if (split > max_by_len) split = max_by_len;
-    g.block = 256;
+  if (g.pruned) {
+    g.cmax_rows = npos;
+    g.cmax_ld = nch;
+    g.cmax_bytes = cmax_bytes;
   }
+  // aim for ~4096 waves (16 per CU), each slice at least 256 chunks
+  int64_t split = x->rows > 0 ? (4096 + x->rows - 1) / x->rows : 1;
+  const int64_t max_by_len = nch / 256 > 0 ? nch / 256 : 1;
+  if (split > max_by_len) split = max_by_len;
   if (t && t->split > 0) split = t->split;
-  if (t && t->block > 0 && g.shared) {
-    if (t->block > 512) return fail(DV_ERR_ARG, "tuning.block must be 256 or 512 with shared noise");
-    g.block = t->block;
-  }
   if (split > 64) split = 64;
   if (split > nch) split = nch;
   if (split < 1) split = 1;
   g.split = static_cast<int32_t>(split);
   g.slice_chunks = static_cast<int32_t>((nch + split - 1) / split);
-  if (g.shared && static_cast<size_t>(g.slice_chunks) * N * 4 > kMaxSharedLds)
-    return fail(DV_ERR_ARG, "tuning.split %d leaves a slice too long for LDS", g.split);
   const int64_t waves = x->rows * split;
-  if (!g.shared && (waves + 3) / 4 > kMaxIndex) return fail(DV_ERR_UNSUPPORTED, "too many rows for one launch");
-  g.workspace = split > 1 ? static_cast<size_t>(x->rows) * split * sizeof(dv::Partial) : 0;
+  if ((waves + 3) / 4 > kMaxIndex) return fail(DV_ERR_UNSUPPORTED, "too many rows for one launch");
+  g.workspace = g.cmax_bytes + (split > 1 ? static_cast<size_t>(x->rows) * split * sizeof(dv::Partial) : 0);
   return DV_OK;
 }
 
@@ -171,10 +161,11 @@ dv_status dv_verify_rows(const dv_logits *logits, const dv_noise *noise, const d
   p.pos = noise->pos;
   p.pos_period = noise->pos_period;
   p.split = g.split;
-  p.block = g.block;
-  p.shared = g.shared;
   p.slice_chunks = g.slice_chunks;
-  p.ws = static_cast<dv::Partial *>(workspace);
+  p.noise_cmax = g.pruned ? static_cast<float *>(workspace) : nullptr;
+  p.cmax_rows = g.cmax_rows;
+  p.cmax_ld = g.cmax_ld;
+  p.ws = reinterpret_cast<dv::Partial *>(static_cast<char *>(workspace) + g.cmax_bytes);
   p.out = *out;
   return hip_status(dv::launch_verify(p, stream), "dv_verify_rows launch");
 }

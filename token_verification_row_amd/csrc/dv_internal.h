@@ -62,11 +62,12 @@ struct VerifyLaunch {
   uint32_t seed_b;     // seed word B
   const int32_t *pos;  // device or NULL
   int64_t pos_period;
-  int32_t split;       // vocabulary slices per row
-  int32_t block;       // threads per workgroup
-  int32_t shared;      // 1: noise computed once per (position, slice) in LDS
+  int32_t split;         // vocabulary slices per row
   int32_t slice_chunks;  // 16-byte chunks per slice
-  Partial *ws;         // [rows][split] when split > 1
+  Partial *ws;           // [rows][split] when split > 1
+  float *noise_cmax;     // [cmax_rows][cmax_ld] chunk-max noise table (workspace), or NULL
+  int64_t cmax_rows;     // positions 0 .. cmax_rows-1
+  int64_t cmax_ld;       // chunks per row
   dv_row_stats out;
 };
 

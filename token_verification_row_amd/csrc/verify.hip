@@ -10,25 +10,29 @@
 //   same Gumbel noise);
 //   [COVER] §2 (the seed score's uncertainty u is the entropy).
 //
-// Design (HBM-bound streaming reduction, no matrix cores):
+// Design (a streaming reduction with no matrix-core work; at T > 0 its VALU
+// load is as large as its HBM traffic, so both are budgeted):
 //   * a wavefront owns a (row, vocabulary slice); each lane reads 16-byte
-//     chunks (8 bf16 or 4 fp32) of both rows with non-temporal loads, lanes
-//     of a wave covering 1 KiB of contiguous memory per load;
+//     chunks (8 bf16 or 4 fp32) of both rows with non-temporal loads, the
+//     lanes of a wave covering 1 KiB of contiguous memory per load, and keeps
+//     the next chunks' loads in flight in a second register set;
 //   * sums of exponentials are taken against a per-lane reference rho that is
 //     only moved when a logit exceeds it by more than 64 (log2 units), so the
-//     usual per-element online rescale disappears: the running maximum is
-//     tracked separately, per 16-byte chunk, for the argmax;
+//     usual per-element online rescale disappears; the running maximum is
+//     tracked separately, per chunk, for the argmax;
 //   * KL and entropy come from the same pass: D = sum e_v (a - b) and
 //     W = sum e_v t_v with t_v = a log2(e) - rho;
 //   * argmax and Gumbel-max tokens are tracked per chunk (value, chunk index);
-//     the exact lowest index inside the winning chunk is recovered at the end
-//     by re-reading 16 bytes, so the hot loop carries no per-element index;
-//   * the noise is computed in registers from a counter hash; when rows share
-//     positions (the candidates of a tree level), a workgroup computes it once
-//     per (position, slice) into LDS and every row at that position reuses it;
-//   * lane states are combined across the wave with cross-lane shuffles, then
-//     per row in double precision (split rows go through a workspace of 64-byte
-//     partials and a merge kernel).
+//     the lowest index inside the winning chunk is recovered at the end by
+//     re-reading 16 bytes, so the hot loop carries no per-element index;
+//   * noise comes from a counter hash. When rows share positions (the
+//     candidates of a tree level) a small table holds, per (position, chunk),
+//     the largest noise value; a chunk can then be skipped when
+//     max(x)/T + max(noise) is below the best score the wave has seen, and the
+//     chunks that cannot be skipped are queued in LDS with their logits and
+//     scored 64 at a time, one per lane, noise recomputed from the hash;
+//   * lane states are combined across the wave with DPP, then per row (split
+//     rows go through a workspace of 64-byte partials and a merge kernel).
 #include <climits>
 #include <cmath>
 
@@ -39,10 +43,13 @@ namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr double kLn2 = 0.693147180559945309417232121458;
-constexpr float kRebase = 64.0f;                          // log2 units
+constexpr float kRebase = 64.0f;                                   // log2 units
 constexpr float kOneMinusHalfUlp = 0.999999940395355224609375f;  // 1 - 2^-24
 
-enum { kGreedy = 0, kInline = 1, kShared = 2 };
+// Noise modes of the streaming kernel.
+enum { kGreedy = 0,   // T = 0: tokens are the argmaxes, no noise
+       kInline = 1,   // per-element noise from the hash
+       kPruned = 2 }; // chunk-max noise table + bound + queued scoring
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -97,33 +104,97 @@ __device__ __forceinline__ void widen(const u32x4 &w, float (&x)[Chunk<BF16>::N]
   }
 }
 
+template <bool BF16>
+__device__ __forceinline__ void noise_chunk(float (&g)[Chunk<BF16>::N], int32_t c, uint32_t key) {
+  constexpr int N = Chunk<BF16>::N;
+  const uint32_t i0 = static_cast<uint32_t>(c) * N;
+#pragma unroll
+  for (int j = 0; j < N; ++j) g[j] = noise_at(key, i0 + j);
+}
+
 // Per-lane accumulator of one (row, slice).
 struct Lane {
-  float rho_v, S_v, W_v, D_v, thr_v;
-  float rho_d, S_d, thr_d;
+  float rho_v, S_v, S_v2, W_v, D_v, thr_v;  // S_v + S_v2: even / odd elements (independent add chains)
+  float rho_d, S_d, S_d2, thr_d;
   float m_v, m_d, s_v, s_d;
   int32_t cm_v, cm_d, cs_v, cs_d;
+  float wb_v, wb_d;  // wave-wide lower bounds of the best perturbed scores (equal in all lanes)
 
   __device__ __forceinline__ void init() {
+    wb_v = wb_d = -INFINITY;
     rho_v = rho_d = -INFINITY;
     thr_v = thr_d = -INFINITY;
-    S_v = W_v = D_v = S_d = 0.0f;
+    S_v = S_v2 = W_v = D_v = S_d = S_d2 = 0.0f;
     m_v = m_d = s_v = s_d = -INFINITY;
     cm_v = cm_d = cs_v = cs_d = INT_MAX;
   }
 };
 
+// ---- cross-lane combination ----
+// Wave64 reductions with DPP moves (VALU, no LDS round trips): an inclusive
+// scan inside each row of 16 lanes (row_shr 1, 2, 4, 8), then row_bcast:15
+// and row_bcast:31 carry the row totals up, so lane 63 ends with the result,
+// which readlane broadcasts to the whole wave.
+enum : int { kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118, kRowBcast15 = 0x142,
+             kRowBcast31 = 0x143 };
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f(float identity, float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(identity), __float_as_int(x), CTRL, ROW_MASK,
+                                                    0xF, false));
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int32_t dpp_i(int32_t identity, int32_t x) {
+  return __builtin_amdgcn_update_dpp(identity, x, CTRL, ROW_MASK, 0xF, false);
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp_f<kRowShr1, 0xF>(0.0f, x);
+  x += dpp_f<kRowShr2, 0xF>(0.0f, x);
+  x += dpp_f<kRowShr4, 0xF>(0.0f, x);
+  x += dpp_f<kRowShr8, 0xF>(0.0f, x);
+  x += dpp_f<kRowBcast15, 0xA>(0.0f, x);
+  x += dpp_f<kRowBcast31, 0xC>(0.0f, x);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_f<kRowShr1, 0xF>(-INFINITY, x));
+  x = fmaxf(x, dpp_f<kRowShr2, 0xF>(-INFINITY, x));
+  x = fmaxf(x, dpp_f<kRowShr4, 0xF>(-INFINITY, x));
+  x = fmaxf(x, dpp_f<kRowShr8, 0xF>(-INFINITY, x));
+  x = fmaxf(x, dpp_f<kRowBcast15, 0xA>(-INFINITY, x));
+  x = fmaxf(x, dpp_f<kRowBcast31, 0xC>(-INFINITY, x));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+__device__ __forceinline__ int32_t wave_min_i(int32_t x) {
+  x = min(x, dpp_i<kRowShr1, 0xF>(INT_MAX, x));
+  x = min(x, dpp_i<kRowShr2, 0xF>(INT_MAX, x));
+  x = min(x, dpp_i<kRowShr4, 0xF>(INT_MAX, x));
+  x = min(x, dpp_i<kRowShr8, 0xF>(INT_MAX, x));
+  x = min(x, dpp_i<kRowBcast15, 0xA>(INT_MAX, x));
+  x = min(x, dpp_i<kRowBcast31, 0xC>(INT_MAX, x));
+  return __builtin_amdgcn_readlane(x, 63);
+}
+// (value, chunk): largest value, lowest chunk among equal values
+__device__ __forceinline__ void wave_argmax(float &m, int32_t &c) {
+  const float M = wave_max(m);
+  c = wave_min_i(m == M ? c : INT_MAX);
+  m = M;
+}
+
 // Move the reference to x * log2(e) and rescale what was accumulated so far.
 __device__ __forceinline__ void rebase_v(Lane &st, float x) {
   const float nr = x * kLog2e;
-  if (st.S_v > 0.0f) {
+  const float S = st.S_v + st.S_v2;
+  if (S > 0.0f) {
     const float d = st.rho_v - nr;  // <= 0
     const float sc = __builtin_amdgcn_exp2f(d);
-    st.W_v = sc * __builtin_fmaf(d, st.S_v, st.W_v);
+    st.W_v = sc * __builtin_fmaf(d, S, st.W_v);
     st.S_v *= sc;
+    st.S_v2 *= sc;
     st.D_v *= sc;
   } else {
-    st.S_v = st.W_v = st.D_v = 0.0f;
+    st.S_v = st.S_v2 = st.W_v = st.D_v = 0.0f;
   }
   st.rho_v = nr;
   st.thr_v = (nr + kRebase) * (1.0f / kLog2e);
@@ -131,10 +202,12 @@ __device__ __forceinline__ void rebase_v(Lane &st, float x) {
 
 __device__ __forceinline__ void rebase_d(Lane &st, float x) {
   const float nr = x * kLog2e;
-  if (st.S_d > 0.0f) {
-    st.S_d *= __builtin_amdgcn_exp2f(st.rho_d - nr);
+  if (st.S_d + st.S_d2 > 0.0f) {
+    const float sc = __builtin_amdgcn_exp2f(st.rho_d - nr);
+    st.S_d *= sc;
+    st.S_d2 *= sc;
   } else {
-    st.S_d = 0.0f;
+    st.S_d = st.S_d2 = 0.0f;
   }
   st.rho_d = nr;
   st.thr_d = (nr + kRebase) * (1.0f / kLog2e);
@@ -148,21 +221,43 @@ __device__ __forceinline__ float max_of(const float (&x)[N]) {
   return m;
 }
 
-template <int N>
-__device__ __forceinline__ float tree_sum(const float (&x)[N]) {
-  if constexpr (N == 8) {
-    return ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
-  } else {
-    return (x[0] + x[1]) + (x[2] + x[3]);
+// Gumbel-max bookkeeping of one chunk: best perturbed score of each model.
+// ANY_ORDER: chunks may arrive out of index order (queued scoring), so equal
+// scores must compare chunk indices explicitly.
+template <int N, bool MASKED, bool ANY_ORDER>
+__device__ __forceinline__ void fold_tokens(Lane &st, const float (&a)[N], const float (&b)[N], const float (&g)[N],
+                                            int32_t c, float cT, int nvalid) {
+  float csa = -INFINITY, csb = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    float pa = __builtin_fmaf(a[j], cT, g[j]);
+    float pb = __builtin_fmaf(b[j], cT, g[j]);
+    if constexpr (MASKED) {
+      if (j >= nvalid) {
+        pa = -INFINITY;
+        pb = -INFINITY;
+      }
+    }
+    csa = fmaxf(csa, pa);
+    csb = fmaxf(csb, pb);
+  }
+  if (csa > st.s_v || (ANY_ORDER && csa == st.s_v && c < st.cs_v)) {
+    st.s_v = csa;
+    st.cs_v = c;
+  }
+  if (csb > st.s_d || (ANY_ORDER && csb == st.s_d && c < st.cs_d)) {
+    st.s_d = csb;
+    st.cs_d = c;
   }
 }
 
-// Fold one chunk (N logits of each model, N noise values) into the lane state.
-// MASKED: only the first nvalid elements are logits (last chunk of a row).
-template <int N, bool NOISE, bool MASKED>
-__device__ __forceinline__ void consume(Lane &st, float (&a)[N], float (&b)[N], const float (&g)[N],
-                                        int32_t c, float cT, int nvalid) {
-  float cma, cmb;
+// Fold the statistics of one chunk (N logits of each model) into the lane
+// state and return the chunk maxima of both rows in cma / cmb. MASKED: only
+// the first nvalid elements are logits (last chunk of a row). One pass over
+// the elements with running accumulators keeps few temporaries live.
+template <int N, bool MASKED>
+__device__ __forceinline__ void fold_stats(Lane &st, float (&a)[N], float (&b)[N], int32_t c, int nvalid, float &cma,
+                                           float &cmb) {
   if constexpr (MASKED) {
     cma = a[0];
     cmb = b[0];
@@ -196,9 +291,9 @@ __device__ __forceinline__ void consume(Lane &st, float (&a)[N], float (&b)[N], 
   if (cma > st.thr_v) rebase_v(st, cma);
   if (cmb > st.thr_d) rebase_d(st, cmb);
 
-  float ev[N], ed[N];
   const float nrv = -st.rho_v, nrd = -st.rho_d;
   float W = st.W_v, D = st.D_v;
+  float sv0 = st.S_v, sv1 = st.S_v2, sd0 = st.S_d, sd1 = st.S_d2;
 #pragma unroll
   for (int j = 0; j < N; ++j) {
     const float tv = __builtin_fmaf(a[j], kLog2e, nrv);
@@ -211,132 +306,177 @@ __device__ __forceinline__ void consume(Lane &st, float (&a)[N], float (&b)[N], 
         f = 0.0f;
       }
     }
-    ev[j] = e;
-    ed[j] = f;
+    if (j & 1) {
+      sv1 += e;
+      sd1 += f;
+    } else {
+      sv0 += e;
+      sd0 += f;
+    }
     W = __builtin_fmaf(e, tv, W);
     D = __builtin_fmaf(e, a[j] - b[j], D);
   }
   st.W_v = W;
   st.D_v = D;
-  st.S_v += tree_sum(ev);
-  st.S_d += tree_sum(ed);
+  st.S_v = sv0;
+  st.S_v2 = sv1;
+  st.S_d = sd0;
+  st.S_d2 = sd1;
+}
 
-  if constexpr (NOISE) {
-    float pa[N], pb[N];
+// One chunk, statistics and (unless greedy) tokens with noise from the hash.
+template <bool BF16, int MODE, bool MASKED>
+__device__ __forceinline__ void fold_chunk(Lane &st, const u32x4 &wa, const u32x4 &wb, int32_t c, uint32_t key,
+                                           float cT, int nvalid) {
+  constexpr int N = Chunk<BF16>::N;
+  float x[N], y[N], cma, cmb;
+  widen<BF16>(wa, x);
+  widen<BF16>(wb, y);
+  fold_stats<N, MASKED>(st, x, y, c, nvalid, cma, cmb);
+  if constexpr (MODE != kGreedy) {
+    float g[N];
+    noise_chunk<BF16>(g, c, key);
+    fold_tokens<N, MASKED, MODE == kPruned>(st, x, y, g, c, cT, nvalid);
+  }
+}
+
+// Chunks whose bound did not rule them out, waiting to be scored: their
+// index and raw logits. One queue per wave, in LDS.
+struct ScoreQueue {
+  int32_t c[64];
+  u32x4 a[64], b[64];
+};
+
+// Score the queued chunks, one per lane, and raise the wave's bounds.
+template <bool BF16>
+__device__ __forceinline__ void flush_queue(Lane &st, ScoreQueue &q, int n, uint32_t key, float cT, int lane) {
+  constexpr int N = Chunk<BF16>::N;
+  __builtin_amdgcn_wave_barrier();  // lanes read entries other lanes of the wave wrote
+  if (lane < n) {
+    const int32_t c = q.c[lane];
+    float x[N], y[N], g[N];
+    widen<BF16>(q.a[lane], x);
+    widen<BF16>(q.b[lane], y);
+    noise_chunk<BF16>(g, c, key);
+    fold_tokens<N, false, true>(st, x, y, g, c, cT, N);
+  }
+  st.wb_v = wave_max(st.s_v);
+  st.wb_d = wave_max(st.s_d);
+  __builtin_amdgcn_wave_barrier();  // the entries are rewritten only after every lane read its own
+}
+
+#ifndef DV_STEP_CHUNKS
+#define DV_STEP_CHUNKS 2
+#endif
+constexpr int kStep = DV_STEP_CHUNKS;  // chunks per lane per step of the streaming loop
+
+// Raw registers of K chunks (c, c + 64, ..., c + 64 (K-1)) of both matrices
+// and, when pruning, the largest noise value of each chunk.
+template <bool BF16, bool PRUNE, int K>
+struct StepRegs {
+  u32x4 a[K], b[K];
+  float gm[K];
+
+  template <typename At>
+  __device__ __forceinline__ void load(const u32x4 *ra, const u32x4 *rb, const float *g_cmax, int32_t c, At at) {
 #pragma unroll
-    for (int j = 0; j < N; ++j) {
-      pa[j] = __builtin_fmaf(a[j], cT, g[j]);
-      pb[j] = __builtin_fmaf(b[j], cT, g[j]);
-      if constexpr (MASKED) {
-        if (j >= nvalid) {
-          pa[j] = -INFINITY;
-          pb[j] = -INFINITY;
+    for (int k = 0; k < K; ++k) {
+      const int32_t ck = at(c + 64 * k);
+      a[k] = load_stream(ra + ck);
+      b[k] = load_stream(rb + ck);
+      if constexpr (PRUNE) gm[k] = g_cmax[ck];
+    }
+  }
+
+  // Fold the K chunks in; chunk k exists only when c + 64 k < cend (lanes past
+  // the end of the slice ran the loop with the others but fold nothing). The
+  // queue operations are wave-wide, so every lane must reach them.
+  template <int MODE>
+  __device__ __forceinline__ void fold(Lane &st, int32_t c, int32_t cend, uint32_t key, float cT, ScoreQueue *q,
+                                       int &nq, int lane) const {
+    constexpr int N = Chunk<BF16>::N;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int32_t ck = c + 64 * k;
+      const bool valid = ck < cend;
+      if constexpr (MODE == kPruned) {
+        // A chunk can hold a model's Gumbel-max token only if the bound
+        // max(x)/T + max(noise) reaches the best score the wave has already
+        // seen (fma is monotone, so the bound holds for the rounded scores;
+        // >= keeps chunks that could tie). The others are queued.
+        bool need = false;
+        if (valid) {
+          float x[N], y[N], cma, cmb;
+          widen<BF16>(a[k], x);
+          widen<BF16>(b[k], y);
+          fold_stats<N, false>(st, x, y, ck, N, cma, cmb);
+          need = __builtin_fmaf(cma, cT, gm[k]) >= st.wb_v || __builtin_fmaf(cmb, cT, gm[k]) >= st.wb_d;
         }
+        const unsigned long long mask = __ballot(need);
+        if (mask) {
+          const int cnt = __popcll(mask);
+          if (nq + cnt > 64) {
+            flush_queue<BF16>(st, *q, nq, key, cT, lane);
+            nq = 0;
+          }
+          if (need) {
+            const int slot = nq + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0));
+            q->c[slot] = ck;
+            q->a[slot] = a[k];
+            q->b[slot] = b[k];
+          }
+          nq += cnt;
+        }
+      } else {
+        if (valid) fold_chunk<BF16, MODE, false>(st, a[k], b[k], ck, key, cT, N);
       }
     }
-    const float csa = max_of(pa), csb = max_of(pb);
-    if (csa > st.s_v) {
-      st.s_v = csa;
-      st.cs_v = c;
-    }
-    if (csb > st.s_d) {
-      st.s_d = csb;
-      st.cs_d = c;
-    }
   }
-}
+};
 
-// Noise values of chunk c into g: computed from the hash (kInline) or read
-// from the workgroup's LDS copy of the slice (kShared).
-template <bool BF16, int MODE>
-__device__ __forceinline__ void noise_chunk(float (&g)[Chunk<BF16>::N], int32_t c, int32_t c0, uint32_t key,
-                                            const float *g_lds) {
-  constexpr int N = Chunk<BF16>::N;
-  if constexpr (MODE == kInline) {
-    const uint32_t i0 = static_cast<uint32_t>(c) * N;
-#pragma unroll
-    for (int j = 0; j < N; ++j) g[j] = noise_at(key, i0 + j);
-  } else if constexpr (MODE == kShared) {
-    const f32x4 *q = reinterpret_cast<const f32x4 *>(g_lds + (c - c0) * N);
-#pragma unroll
-    for (int j = 0; j < N / 4; ++j) {
-      const f32x4 v = q[j];
-      g[4 * j + 0] = v.x;
-      g[4 * j + 1] = v.y;
-      g[4 * j + 2] = v.z;
-      g[4 * j + 3] = v.w;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < N; ++j) g[j] = 0.0f;
-  }
-}
-
-// Stream chunks [c0, c1) of one row pair through the lanes of a wave.
+// Stream chunks [c0, c1) of one row pair through the lanes of a wave. Lane l
+// takes chunks c0 + l, c0 + l + 64, ...; the loop runs the same number of
+// steps in every lane (lanes past the end of the slice load a valid chunk and
+// fold nothing), so wave-wide operations inside it see all lanes. Two register
+// sets, X and Y, work in ping-pong: while one step of chunks is folded in, the
+// loads of the next step land in the other set; the next loads are issued on
+// every path (the last step re-reads its own chunks, which hit in cache), so
+// the wait counts never have to cover a path without them and no register
+// copy forces a wait at the back edge.
 template <bool BF16, int MODE>
 __device__ __forceinline__ void scan_slice(Lane &st, const u32x4 *ra, const u32x4 *rb, int32_t c0, int32_t c1,
                                            int32_t nfull, int nvalid_tail, float cT, uint32_t key,
-                                           const float *g_lds, int lane) {
-  constexpr int N = Chunk<BF16>::N;
-  constexpr bool NOISE = MODE != kGreedy;
-  const int32_t cend = c1 < nfull ? c1 : nfull;
-  int32_t c = c0 + lane;
-  for (; c + 64 < cend; c += 128) {
-    const u32x4 wa0 = load_stream(ra + c), wb0 = load_stream(rb + c);
-    const u32x4 wa1 = load_stream(ra + c + 64), wb1 = load_stream(rb + c + 64);
-    float g0[N], g1[N];
-    noise_chunk<BF16, MODE>(g0, c, c0, key, g_lds);
-    noise_chunk<BF16, MODE>(g1, c + 64, c0, key, g_lds);
-    float a0[N], b0[N], a1[N], b1[N];
-    widen<BF16>(wa0, a0);
-    widen<BF16>(wb0, b0);
-    widen<BF16>(wa1, a1);
-    widen<BF16>(wb1, b1);
-    consume<N, NOISE, false>(st, a0, b0, g0, c, cT, N);
-    consume<N, NOISE, false>(st, a1, b1, g1, c + 64, cT, N);
+                                           const float *g_cmax, ScoreQueue *q, int lane) {
+  constexpr int32_t kSpan = 64 * kStep;
+  const int32_t cend = c1 < nfull ? c1 : nfull;  // whole chunks of the slice
+  const int32_t nsteps = cend > c0 ? (cend - c0 + kSpan - 1) / kSpan : 0;
+  int nq = 0;
+  if (nsteps > 0) {
+    // in-bounds address for chunks past the end (their data is not used)
+    auto at = [&](int32_t cc) { return cc < cend ? cc : c0; };
+    StepRegs<BF16, MODE == kPruned, kStep> X, Y;
+    int32_t c = c0 + lane;
+    X.load(ra, rb, g_cmax, c, at);
+    for (int32_t t = 0;;) {
+      ++t;
+      Y.load(ra, rb, g_cmax, t < nsteps ? c + kSpan : c, at);
+      X.template fold<MODE>(st, c, cend, key, cT, q, nq, lane);
+      if (t == nsteps) break;
+      c += kSpan;
+      ++t;
+      X.load(ra, rb, g_cmax, t < nsteps ? c + kSpan : c, at);
+      Y.template fold<MODE>(st, c, cend, key, cT, q, nq, lane);
+      if (t == nsteps) break;
+      c += kSpan;
+    }
   }
-  if (c < cend) {
-    const u32x4 wa = load_stream(ra + c), wb = load_stream(rb + c);
-    float g[N];
-    noise_chunk<BF16, MODE>(g, c, c0, key, g_lds);
-    float a[N], b[N];
-    widen<BF16>(wa, a);
-    widen<BF16>(wb, b);
-    consume<N, NOISE, false>(st, a, b, g, c, cT, N);
+  if constexpr (MODE == kPruned) {
+    if (nq > 0) flush_queue<BF16>(st, *q, nq, key, cT, lane);
   }
   // the last, partly filled chunk of the row (vocab not a multiple of N)
-  if (nvalid_tail > 0 && nfull >= c0 && nfull < c1 && lane == ((nfull - c0) & 63)) {
-    const u32x4 wa = ra[nfull], wb = rb[nfull];
-    float g[N];
-    noise_chunk<BF16, MODE>(g, nfull, c0, key, g_lds);
-    float a[N], b[N];
-    widen<BF16>(wa, a);
-    widen<BF16>(wb, b);
-    consume<N, NOISE, true>(st, a, b, g, nfull, cT, nvalid_tail);
-  }
-}
-
-// ---- cross-lane combination ----
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
-}
-__device__ __forceinline__ int32_t wave_min_i(int32_t x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o, 64));
-  return x;
-}
-// (value, chunk): largest value, lowest chunk among equal values
-__device__ __forceinline__ void wave_argmax(float &m, int32_t &c) {
-  const float M = wave_max(m);
-  c = wave_min_i(m == M ? c : INT_MAX);
-  m = M;
+  if (nvalid_tail > 0 && nfull >= c0 && nfull < c1 && lane == ((nfull - c0) & 63))
+    fold_chunk<BF16, MODE, true>(st, ra[nfull], rb[nfull], nfull, key, cT, nvalid_tail);
 }
 
 // Reduce the lane states of a wave into one partial (valid in every lane).
@@ -344,19 +484,21 @@ __device__ __forceinline__ Partial wave_reduce(const Lane &st) {
   Partial t;
   {
     const float R = wave_max(st.rho_v);
-    const bool has = st.S_v > 0.0f;
+    const float S = st.S_v + st.S_v2;
+    const bool has = S > 0.0f;
     const float d = has ? st.rho_v - R : 0.0f;
     const float sc = has ? __builtin_amdgcn_exp2f(d) : 0.0f;
-    t.S_v = wave_sum(st.S_v * sc);
-    t.W_v = wave_sum(sc * __builtin_fmaf(d, st.S_v, st.W_v));
+    t.S_v = wave_sum(S * sc);
+    t.W_v = wave_sum(sc * __builtin_fmaf(d, S, st.W_v));
     t.D_v = wave_sum(st.D_v * sc);
     t.rho_v = R;
   }
   {
     const float R = wave_max(st.rho_d);
-    const bool has = st.S_d > 0.0f;
+    const float Sd = st.S_d + st.S_d2;
+    const bool has = Sd > 0.0f;
     const float sc = has ? __builtin_amdgcn_exp2f(st.rho_d - R) : 0.0f;
-    t.S_d = wave_sum(st.S_d * sc);
+    t.S_d = wave_sum(Sd * sc);
     t.rho_d = R;
   }
   t.m_v = st.m_v;
@@ -376,102 +518,81 @@ __device__ __forceinline__ Partial wave_reduce(const Lane &st) {
 }
 
 // ---- per-row epilogue (double precision) ----
-struct Totals {
-  double rho_v, S_v, W_v, D_v, rho_d, S_d;
-  float m_v, m_d, s_v, s_d;
-  int32_t cm_v, cm_d, cs_v, cs_d;
-};
 
-__device__ __forceinline__ Totals totals_of(const Partial &t) {
-  Totals o;
-  o.rho_v = t.rho_v;
-  o.S_v = t.S_v;
-  o.W_v = t.W_v;
-  o.D_v = t.D_v;
-  o.rho_d = t.rho_d;
-  o.S_d = t.S_d;
-  o.m_v = t.m_v;
-  o.m_d = t.m_d;
-  o.s_v = t.s_v;
-  o.s_d = t.s_d;
-  o.cm_v = t.cm_v;
-  o.cm_d = t.cm_d;
-  o.cs_v = t.cs_v;
-  o.cs_d = t.cs_d;
-  return o;
-}
-
-// lowest index inside chunk c whose logit equals m. A chunk index outside the
-// row (only possible when the logits hold NaN, which is not supported) gives
-// -1 without touching memory.
-template <bool BF16>
-__device__ int32_t refine_max(const u32x4 *row, int32_t c, float m, int64_t vocab) {
+// Lowest index inside chunk c of a row whose value equals target, found by the
+// whole wave: lane j < N looks at element c*N + j. For scores the perturbed
+// score is recomputed with exactly the arithmetic of the streaming pass. A
+// chunk index outside the row (only possible when the logits hold NaN, which
+// is not supported) gives -1 without touching memory.
+template <bool BF16, bool SCORE>
+__device__ __forceinline__ int32_t refine_in_chunk(const u32x4 *row, int32_t c, float target, int64_t vocab, float cT,
+                                                   uint32_t key, int lane) {
   constexpr int N = Chunk<BF16>::N;
   if (c < 0 || static_cast<int64_t>(c) * N >= vocab) return -1;
   float x[N];
-  widen<BF16>(row[c], x);
-  for (int j = 0; j < N; ++j) {
-    const int64_t i = static_cast<int64_t>(c) * N + j;
-    if (i < vocab && x[j] == m) return static_cast<int32_t>(i);
+  widen<BF16>(row[c], x);  // the same 16 bytes for every lane: one request
+  float v = x[0];
+#pragma unroll
+  for (int j = 1; j < N; ++j) v = (lane == j) ? x[j] : v;
+  const int64_t i = static_cast<int64_t>(c) * N + lane;
+  bool hit = false;
+  if (lane < N && i < vocab) {
+    if constexpr (SCORE) v = __builtin_fmaf(v, cT, noise_at(key, static_cast<uint32_t>(i)));
+    hit = v == target;
   }
-  return static_cast<int32_t>(static_cast<int64_t>(c) * N);
+  const unsigned long long m = __ballot(hit);
+  return m ? static_cast<int32_t>(static_cast<int64_t>(c) * N + __ffsll(m) - 1) : -1;
 }
 
-// lowest index inside chunk c whose perturbed score equals best (recomputed
-// with exactly the arithmetic of the streaming pass)
+// Row results from the reduced state of a whole row; every lane of the wave
+// calls it (the refinements use the lanes), lane 0 writes.
 template <bool BF16>
-__device__ int32_t refine_score(const u32x4 *row, int32_t c, float best, int64_t vocab, float cT, uint32_t key) {
-  constexpr int N = Chunk<BF16>::N;
-  if (c < 0 || static_cast<int64_t>(c) * N >= vocab) return -1;
-  float x[N];
-  widen<BF16>(row[c], x);
-  for (int j = 0; j < N; ++j) {
-    const int64_t i = static_cast<int64_t>(c) * N + j;
-    if (i < vocab && __builtin_fmaf(x[j], cT, noise_at(key, static_cast<uint32_t>(i))) == best)
-      return static_cast<int32_t>(i);
+__device__ void finalize_row(const VerifyLaunch &p, int64_t r, const Partial &t, int lane) {
+  const size_t row_bytes = static_cast<size_t>(p.ld) * (BF16 ? 2 : 4);
+  const u32x4 *ra = reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.va) + r * row_bytes);
+  const u32x4 *rb = reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.vb) + r * row_bytes);
+  const dv_row_stats &o = p.out;
+  const bool want_am = o.argmax_v || o.argmax_d || (p.greedy && (o.tok_v || o.tok_d));
+  int32_t am_v = 0, am_d = 0, tk_v = 0, tk_d = 0;
+  if (want_am) {
+    am_v = refine_in_chunk<BF16, false>(ra, t.cm_v, t.m_v, p.vocab, 0.0f, 0u, lane);
+    am_d = refine_in_chunk<BF16, false>(rb, t.cm_d, t.m_d, p.vocab, 0.0f, 0u, lane);
   }
-  return static_cast<int32_t>(static_cast<int64_t>(c) * N);
-}
-
-template <bool BF16>
-__device__ void finalize_row(const VerifyLaunch &p, int64_t r, const Totals &t) {
-  const u32x4 *ra = reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.va) +
-                                                    r * p.ld * (BF16 ? 2 : 4));
-  const u32x4 *rb = reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.vb) +
-                                                    r * p.ld * (BF16 ? 2 : 4));
-  const double l2v = log2(t.S_v), l2d = log2(t.S_d);
-  const double lse_v = kLn2 * (t.rho_v + l2v);
-  const double lse_d = kLn2 * (t.rho_d + l2d);
-  double kl = t.D_v / t.S_v - kLn2 * ((t.rho_v - t.rho_d) + (l2v - l2d));
-  double ent = kLn2 * (l2v - t.W_v / t.S_v);
-  double conf = exp2(static_cast<double>(t.m_v) * static_cast<double>(kLog2e) - t.rho_v) / t.S_v;
+  if (o.tok_v || o.tok_d) {
+    if (p.greedy) {
+      tk_v = am_v;
+      tk_d = am_d;
+    } else {
+      const uint32_t key = row_key(p.seed_b, position_of(p, r));
+      tk_v = refine_in_chunk<BF16, true>(ra, t.cs_v, t.s_v, p.vocab, p.cT, key, lane);
+      tk_d = refine_in_chunk<BF16, true>(rb, t.cs_d, t.s_d, p.vocab, p.cT, key, lane);
+    }
+  }
+  if (lane != 0) return;
+  const double S_v = t.S_v, S_d = t.S_d;
+  const double l2v = log2(S_v), l2d = log2(S_d);
+  const double rho_v = t.rho_v, rho_d = t.rho_d;
+  const double lse_v = kLn2 * (rho_v + l2v);
+  const double lse_d = kLn2 * (rho_d + l2d);
+  double kl = static_cast<double>(t.D_v) / S_v - kLn2 * ((rho_v - rho_d) + (l2v - l2d));
+  double ent = kLn2 * (l2v - static_cast<double>(t.W_v) / S_v);
+  // the maximum's own term, computed as the streaming pass computed it for a
+  // lane whose reference equals rho_v, so that a row with one dominant logit
+  // gives conf == 1 exactly
+  const float e_max = __builtin_amdgcn_exp2f(__builtin_fmaf(t.m_v, kLog2e, -t.rho_v));
+  double conf = static_cast<double>(e_max) / S_v;
   kl = kl < 0.0 ? 0.0 : kl;
   ent = ent < 0.0 ? 0.0 : ent;
   conf = conf > 1.0 ? 1.0 : conf;
-  const dv_row_stats &o = p.out;
   if (o.lse_v) o.lse_v[r] = static_cast<float>(lse_v);
   if (o.lse_d) o.lse_d[r] = static_cast<float>(lse_d);
   if (o.kl) o.kl[r] = static_cast<float>(kl);
   if (o.entropy) o.entropy[r] = static_cast<float>(ent);
   if (o.conf) o.conf[r] = static_cast<float>(conf);
-  const bool want_am = o.argmax_v || o.argmax_d || (p.greedy && (o.tok_v || o.tok_d));
-  int32_t am_v = 0, am_d = 0;
-  if (want_am) {
-    am_v = refine_max<BF16>(ra, t.cm_v, t.m_v, p.vocab);
-    am_d = refine_max<BF16>(rb, t.cm_d, t.m_d, p.vocab);
-  }
   if (o.argmax_v) o.argmax_v[r] = am_v;
   if (o.argmax_d) o.argmax_d[r] = am_d;
-  if (o.tok_v || o.tok_d) {
-    if (p.greedy) {
-      if (o.tok_v) o.tok_v[r] = am_v;
-      if (o.tok_d) o.tok_d[r] = am_d;
-    } else {
-      const uint32_t key = row_key(p.seed_b, position_of(p, r));
-      if (o.tok_v) o.tok_v[r] = refine_score<BF16>(ra, t.cs_v, t.s_v, p.vocab, p.cT, key);
-      if (o.tok_d) o.tok_d[r] = refine_score<BF16>(rb, t.cs_d, t.s_d, p.vocab, p.cT, key);
-    }
-  }
+  if (o.tok_v) o.tok_v[r] = tk_v;
+  if (o.tok_d) o.tok_d[r] = tk_d;
 }
 
 template <bool BF16>
@@ -482,10 +603,13 @@ __device__ __forceinline__ void row_geometry(const VerifyLaunch &p, int32_t &nfu
   nch = nfull + (nvalid_tail ? 1 : 0);
 }
 
-// One wave per (row, slice); noise per row in registers, or none when greedy.
+// One wave per (row, slice).
 template <bool BF16, int MODE>
 __global__ __launch_bounds__(256) void verify_rows_kernel(VerifyLaunch p) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ ScoreQueue queues[MODE == kPruned ? 4 : 1];
+  // the wave index is uniform across the wave: keep it (and all row
+  // addressing derived from it) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t task = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + wave;
   if (task >= p.rows * p.split) return;
   const int64_t r = task / p.split;
@@ -498,124 +622,95 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(VerifyLaunch p) {
   const size_t row_bytes = static_cast<size_t>(p.ld) * (BF16 ? 2 : 4);
   const u32x4 *ra = reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.va) + r * row_bytes);
   const u32x4 *rb = reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.vb) + r * row_bytes);
-  const uint32_t key = MODE == kInline ? row_key(p.seed_b, position_of(p, r)) : 0u;
+  const int32_t pos = MODE == kGreedy ? 0 : position_of(p, r);
+  const uint32_t key = MODE == kGreedy ? 0u : row_key(p.seed_b, pos);
+  const float *gcm = MODE == kPruned ? p.noise_cmax + static_cast<int64_t>(pos) * p.cmax_ld : nullptr;
   Lane st;
   st.init();
-  scan_slice<BF16, MODE>(st, ra, rb, c0, c1, nfull, nvalid_tail, p.cT, key, nullptr, lane);
+  scan_slice<BF16, MODE>(st, ra, rb, c0, c1, nfull, nvalid_tail, p.cT, key, gcm,
+                         MODE == kPruned ? &queues[wave] : nullptr, lane);
   const Partial t = wave_reduce(st);
-  if (lane == 0) {
-    if (p.split == 1) {
-      finalize_row<BF16>(p, r, totals_of(t));
-    } else {
-      p.ws[r * p.split + s] = t;
-    }
+  if (p.split == 1) {
+    finalize_row<BF16>(p, r, t, lane);
+  } else if (lane == 0) {
+    p.ws[r * p.split + s] = t;
   }
 }
 
-// One workgroup per (position group, slice): the noise of the slice is
-// computed once into LDS, then the waves stream every row at that position.
-// Rows of group q are q, q + P, q + 2P, ... (P = pos_period).
-template <bool BF16>
-__global__ __launch_bounds__(512) void verify_shared_kernel(VerifyLaunch p) {
-  extern __shared__ float g_lds[];
-  constexpr int N = Chunk<BF16>::N;
-  const int64_t P = p.pos_period;
-  const int64_t grp = blockIdx.x / p.split;
-  const int32_t s = static_cast<int32_t>(blockIdx.x % p.split);
-  int32_t nfull, nch;
-  int nvalid_tail;
-  row_geometry<BF16>(p, nfull, nvalid_tail, nch);
-  const int32_t c0 = s * p.slice_chunks;
-  const int32_t c1 = min(c0 + p.slice_chunks, nch);
-  const uint32_t key = row_key(p.seed_b, static_cast<int32_t>(grp));
-  const int n = (c1 > c0 ? c1 - c0 : 0) * N;
-  for (int idx = threadIdx.x; idx < n; idx += blockDim.x) {
-    const int64_t i = static_cast<int64_t>(c0) * N + idx;
-    g_lds[idx] = i < p.vocab ? noise_at(key, static_cast<uint32_t>(i)) : 0.0f;
-  }
-  __syncthreads();
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
-  const int64_t nq = (p.rows - grp + P - 1) / P;
-  const size_t row_bytes = static_cast<size_t>(p.ld) * (BF16 ? 2 : 4);
-  for (int64_t q = wave; q < nq; q += nw) {
-    const int64_t r = grp + q * P;
-    const u32x4 *ra = reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.va) + r * row_bytes);
-    const u32x4 *rb = reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.vb) + r * row_bytes);
-    Lane st;
-    st.init();
-    scan_slice<BF16, kShared>(st, ra, rb, c0, c1, nfull, nvalid_tail, p.cT, key, g_lds, lane);
-    const Partial t = wave_reduce(st);
-    if (lane == 0) {
-      if (p.split == 1) {
-        finalize_row<BF16>(p, r, totals_of(t));
-      } else {
-        p.ws[r * p.split + s] = t;
-      }
+// Chunk-max noise table: entry (q, c) is the largest noise value of position
+// q over the valid elements of chunk c (one thread per entry). It is the bound
+// that lets the streaming pass skip chunks that cannot hold a Gumbel-max token.
+template <int N>
+__global__ __launch_bounds__(256) void noise_cmax_kernel(uint32_t seed_b, int64_t npos, int64_t vocab, int64_t ld,
+                                                        float *cmax) {
+  const int64_t n = npos * ld;
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < n;
+       t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t q = t / ld, c = t % ld;
+    const uint32_t key = row_key(seed_b, static_cast<int32_t>(q));
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int64_t i = c * N + j;
+      if (i < vocab) m = fmaxf(m, noise_at(key, static_cast<uint32_t>(i)));
     }
+    cmax[t] = m;
   }
 }
 
-// Combine the split partials of each row (double precision) and finish it.
+// Combine the split partials of each row and finish it: one wave per row,
+// lane s holds slice s (split <= 64).
 template <bool BF16>
 __global__ __launch_bounds__(256) void verify_merge_kernel(VerifyLaunch p) {
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int64_t r =
+      static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (r >= p.rows) return;
-  const Partial *w = p.ws + r * p.split;
-  double Rv = -INFINITY, Rd = -INFINITY;
-  for (int s = 0; s < p.split; ++s) {
-    if (w[s].S_v > 0.0f) Rv = fmax(Rv, static_cast<double>(w[s].rho_v));
-    if (w[s].S_d > 0.0f) Rd = fmax(Rd, static_cast<double>(w[s].rho_d));
+  Lane st;
+  st.init();
+  if (lane < p.split) {
+    const Partial x = p.ws[r * p.split + lane];
+    st.rho_v = x.rho_v;
+    st.S_v = x.S_v;
+    st.W_v = x.W_v;
+    st.D_v = x.D_v;
+    st.rho_d = x.rho_d;
+    st.S_d = x.S_d;
+    st.m_v = x.m_v;
+    st.m_d = x.m_d;
+    st.s_v = x.s_v;
+    st.s_d = x.s_d;
+    st.cm_v = x.cm_v;
+    st.cm_d = x.cm_d;
+    st.cs_v = x.cs_v;
+    st.cs_d = x.cs_d;
   }
-  Totals t;
-  t.rho_v = Rv;
-  t.rho_d = Rd;
-  t.S_v = t.W_v = t.D_v = t.S_d = 0.0;
-  t.m_v = t.m_d = t.s_v = t.s_d = -INFINITY;
-  t.cm_v = t.cm_d = t.cs_v = t.cs_d = INT_MAX;
-  for (int s = 0; s < p.split; ++s) {
-    const Partial &x = w[s];
-    if (x.S_v > 0.0f) {
-      const double d = static_cast<double>(x.rho_v) - Rv;
-      const double sc = exp2(d);
-      t.S_v += sc * x.S_v;
-      t.W_v += sc * (static_cast<double>(x.W_v) + d * x.S_v);
-      t.D_v += sc * x.D_v;
-    }
-    if (x.S_d > 0.0f) t.S_d += exp2(static_cast<double>(x.rho_d) - Rd) * x.S_d;
-    // slices are in increasing chunk order, so the first strict improvement
-    // keeps the lowest chunk among equal values
-    if (x.m_v > t.m_v) { t.m_v = x.m_v; t.cm_v = x.cm_v; }
-    if (x.m_d > t.m_d) { t.m_d = x.m_d; t.cm_d = x.cm_d; }
-    if (x.s_v > t.s_v) { t.s_v = x.s_v; t.cs_v = x.cs_v; }
-    if (x.s_d > t.s_d) { t.s_d = x.s_d; t.cs_d = x.cs_d; }
-  }
-  finalize_row<BF16>(p, r, t);
+  const Partial t = wave_reduce(st);
+  finalize_row<BF16>(p, r, t, lane);
 }
 
 template <bool BF16>
 hipError_t launch_typed(const VerifyLaunch &p, hipStream_t stream) {
   constexpr int N = Chunk<BF16>::N;
-  if (p.shared) {
-    const int64_t groups = p.pos_period < p.rows ? p.pos_period : p.rows;
-    const size_t lds = static_cast<size_t>(p.slice_chunks) * N * sizeof(float);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&verify_shared_kernel<BF16>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  const int64_t waves = p.rows * p.split;
+  const unsigned blocks = static_cast<unsigned>((waves + 3) / 4);
+  if (p.noise_cmax) {
+    const int64_t n = p.cmax_rows * p.cmax_ld;
+    int64_t tb = (n + 255) / 256;
+    if (tb > 16384) tb = 16384;
+    hipLaunchKernelGGL(noise_cmax_kernel<N>, dim3(static_cast<unsigned>(tb)), dim3(256), 0, stream, p.seed_b,
+                       p.cmax_rows, p.vocab, p.cmax_ld, p.noise_cmax);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(verify_shared_kernel<BF16>, dim3(static_cast<unsigned>(groups * p.split)),
-                       dim3(p.block), lds, stream, p);
+    hipLaunchKernelGGL((verify_rows_kernel<BF16, kPruned>), dim3(blocks), dim3(256), 0, stream, p);
+  } else if (p.greedy) {
+    hipLaunchKernelGGL((verify_rows_kernel<BF16, kGreedy>), dim3(blocks), dim3(256), 0, stream, p);
   } else {
-    const int64_t waves = p.rows * p.split;
-    const int wpb = 256 / 64;
-    const unsigned blocks = static_cast<unsigned>((waves + wpb - 1) / wpb);
-    if (p.greedy) {
-      hipLaunchKernelGGL((verify_rows_kernel<BF16, kGreedy>), dim3(blocks), dim3(256), 0, stream, p);
-    } else {
-      hipLaunchKernelGGL((verify_rows_kernel<BF16, kInline>), dim3(blocks), dim3(256), 0, stream, p);
-    }
+    hipLaunchKernelGGL((verify_rows_kernel<BF16, kInline>), dim3(blocks), dim3(256), 0, stream, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.split == 1) return e;
-  const unsigned mblocks = static_cast<unsigned>((p.rows + 255) / 256);
+  const unsigned mblocks = static_cast<unsigned>((p.rows + 3) / 4);
   hipLaunchKernelGGL(verify_merge_kernel<BF16>, dim3(mblocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

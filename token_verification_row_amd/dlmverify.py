@@ -182,7 +182,7 @@ def dv_verify_rows(verifier, drafter, temperature=0.0, seed=0, pos=None, pos_per
     n = _noise_desc(temperature, seed, pos, pos_period)
     t = _tuning_desc(tuning)
     rows, dev = d.rows, verifier.device
-    res = dict(out or {})
+    res = {k: v for k, v in (out or {}).items() if not k.startswith("_")}
     for f in outputs:
         if f not in STAT_FIELDS:
             raise KeyError(f)

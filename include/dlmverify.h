@@ -111,18 +111,19 @@ typedef struct dv_row_stats {
 /* Optional launch-shape override for dv_verify_rows (NULL = automatic). A
  * zero field keeps its automatic value. Results do not depend on it beyond
  * float rounding: integer outputs are identical for every shape.
- *   split         vocabulary slices per row (1..64)
- *   block         threads per workgroup: 0 or 256
+ *   split         vocabulary slices per row (1..16), each one wavefront; the
+ *                 slices of a row run in one workgroup
  *   shared_noise  1: rows share positions (needs temperature > 0, pos == NULL
- *                 and pos_period > 0); a table of the largest noise value of
- *                 each (position, 16-byte chunk) lets the pass skip the
- *                 Gumbel scores of chunks that cannot hold a token;
- *                 0: every chunk is scored; -1: automatic */
+ *                 and pos_period > 0): a table of the largest noise value of
+ *                 each (position, 16-byte chunk), built in the workspace,
+ *                 bounds the Gumbel scores of each chunk;
+ *                 0: the bound comes from each chunk's own hash words;
+ *                 -1: automatic (the table when rows >= 2 * pos_period)
+ *   reserved      must be zero */
 typedef struct dv_tuning {
   int32_t split;
-  int32_t block;
   int32_t shared_noise;
-  int32_t reserved;
+  int32_t reserved[2];
 } dv_tuning;
 
 /* Bytes of device workspace dv_verify_rows needs for these arguments (may be

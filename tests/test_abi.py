@@ -75,19 +75,24 @@ def test_verify_validation(lib):
     assert _verify(lib, _logits(), _noise(T=float("nan"))) == B.DV_ERR_ARG
     assert _verify(lib, _logits(), _noise(T=float("inf"))) == B.DV_ERR_ARG
     assert _verify(lib, _logits(), _noise(period=-3)) == B.DV_ERR_SHAPE
-    bad = B.dv_tuning(split=65, block=0, shared_noise=-1, reserved=0)
+    bad = B.dv_tuning(split=17, shared_noise=-1)
     assert _verify(lib, _logits(), _noise(), tuning=bad) == B.DV_ERR_ARG
-    bad = B.dv_tuning(split=0, block=300, shared_noise=-1, reserved=0)
+    bad = B.dv_tuning(split=-1, shared_noise=-1)
     assert _verify(lib, _logits(), _noise(), tuning=bad) == B.DV_ERR_ARG
-    bad = B.dv_tuning(split=0, block=0, shared_noise=1, reserved=0)   # greedy cannot share noise
+    bad = B.dv_tuning(split=0, shared_noise=2)
+    assert _verify(lib, _logits(), _noise(), tuning=bad) == B.DV_ERR_ARG
+    bad = B.dv_tuning(split=0, shared_noise=-1)
+    bad.reserved[1] = 5
+    assert _verify(lib, _logits(), _noise(), tuning=bad) == B.DV_ERR_ARG
+    bad = B.dv_tuning(split=0, shared_noise=1)   # greedy cannot share noise
     assert _verify(lib, _logits(), _noise(), tuning=bad) == B.DV_ERR_ARG
     assert "shared noise" in lib.dv_last_error().decode()
-    # a split that needs a workspace must get one
-    t = B.dv_tuning(split=4, block=0, shared_noise=0, reserved=0)
-    assert _verify(lib, _logits(vocab=4096, ld=4096), _noise(), tuning=t) == B.DV_ERR_WORKSPACE
-    assert _verify(lib, _logits(vocab=4096, ld=4096), _noise(), tuning=t, ws=FAKE, ws_bytes=100) == B.DV_ERR_WORKSPACE
-    assert _verify(lib, _logits(vocab=4096, ld=4096), _noise(), tuning=t, ws=FAKE + 16,
-                   ws_bytes=1 << 20) == B.DV_ERR_ALIGN
+    # the noise table needs a workspace
+    t = B.dv_tuning(split=4, shared_noise=1)
+    lg, nz = _logits(rows=8, vocab=4096, ld=4096), _noise(T=1.0, period=4)
+    assert _verify(lib, lg, nz, tuning=t) == B.DV_ERR_WORKSPACE
+    assert _verify(lib, lg, nz, tuning=t, ws=FAKE, ws_bytes=100) == B.DV_ERR_WORKSPACE
+    assert _verify(lib, lg, nz, tuning=t, ws=FAKE + 16, ws_bytes=1 << 20) == B.DV_ERR_ALIGN
 
 
 def test_verify_empty_rows_is_a_noop(lib):
@@ -97,28 +102,30 @@ def test_verify_empty_rows_is_a_noop(lib):
 def test_workspace_query(lib):
     out = ctypes.c_size_t(123)
     lg, nz = _logits(rows=4, vocab=4096, ld=4096), _noise()
-    t = B.dv_tuning(split=4, block=0, shared_noise=0, reserved=0)
-    assert lib.dv_verify_workspace_bytes(ctypes.byref(lg), ctypes.byref(nz), ctypes.byref(t),
-                                         ctypes.byref(out)) == B.DV_OK
-    assert out.value == 4 * 4 * 64
-    t = B.dv_tuning(split=1, block=0, shared_noise=0, reserved=0)
+    for split in (1, 4, 16):    # slices of a row are combined on chip: no workspace
+        t = B.dv_tuning(split=split, shared_noise=0)
+        assert lib.dv_verify_workspace_bytes(ctypes.byref(lg), ctypes.byref(nz), ctypes.byref(t),
+                                             ctypes.byref(out)) == B.DV_OK
+        assert out.value == 0
+    assert lib.dv_verify_workspace_bytes(ctypes.byref(lg), ctypes.byref(nz), None, None) == B.DV_ERR_NULL
+    # rows sharing positions: a table of the largest noise value per (position, 16-byte chunk)
+    lg = _logits(rows=2048, vocab=151936, ld=151936)
+    nz = _noise(T=1.0, period=32)
+    table = 32 * (151936 // 8) * 4
+    for t in (None, B.dv_tuning(split=4, shared_noise=1), B.dv_tuning(split=0, shared_noise=-1)):
+        assert lib.dv_verify_workspace_bytes(ctypes.byref(lg), ctypes.byref(nz), None if t is None else ctypes.byref(t),
+                                             ctypes.byref(out)) == B.DV_OK
+        assert out.value == table
+    t = B.dv_tuning(split=0, shared_noise=0)
     assert lib.dv_verify_workspace_bytes(ctypes.byref(lg), ctypes.byref(nz), ctypes.byref(t),
                                          ctypes.byref(out)) == B.DV_OK
     assert out.value == 0
-    assert lib.dv_verify_workspace_bytes(ctypes.byref(lg), ctypes.byref(nz), None, None) == B.DV_ERR_NULL
-    # rows sharing positions: a table of the largest noise value per (position, 16-byte chunk) comes first
-    lg = _logits(rows=2048, vocab=151936, ld=151936)
-    nz = _noise(T=1.0, period=32)
-    assert lib.dv_verify_workspace_bytes(ctypes.byref(lg), ctypes.byref(nz), None, ctypes.byref(out)) == B.DV_OK
-    table = 32 * (151936 // 8) * 4
-    assert out.value == table + 2048 * 2 * 64                  # two slices per row
-    t = B.dv_tuning(split=4, block=0, shared_noise=1, reserved=0)
-    assert lib.dv_verify_workspace_bytes(ctypes.byref(lg), ctypes.byref(nz), ctypes.byref(t),
-                                         ctypes.byref(out)) == B.DV_OK
-    assert out.value == table + 2048 * 4 * 64
     lg = _logits(rows=2048, vocab=1001, ld=1008)                 # 126 chunks, the last one partly filled
     assert lib.dv_verify_workspace_bytes(ctypes.byref(lg), ctypes.byref(nz), None, ctypes.byref(out)) == B.DV_OK
     assert out.value == ((32 * 126 * 4 + 255) // 256) * 256
+    lg = _logits(rows=63, vocab=151936, ld=151936)               # fewer than two rows per position: no table
+    assert lib.dv_verify_workspace_bytes(ctypes.byref(lg), ctypes.byref(nz), None, ctypes.byref(out)) == B.DV_OK
+    assert out.value == 0
 
 
 def _decide(lib, rule=B.DV_RULE_KL, rows=8, group_len=0, tau=0.1, thr=0.9, stats=None, subject=None, cur=None,

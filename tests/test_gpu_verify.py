@@ -128,8 +128,8 @@ def test_geometry_invariance_and_determinism():
     ref = oracle_rows(a, b, "bf16", 1.0, 9, _positions(rows, None, 8))
     base = None
     for tuning in ({"split": 1, "shared_noise": 0}, {"split": 2, "shared_noise": 0}, {"split": 5, "shared_noise": 0},
-                   {"split": 8, "shared_noise": 0}, {"split": 1, "shared_noise": 1}, {"split": 3, "shared_noise": 1},
-                   {"split": 8, "shared_noise": 1, "block": 256}, None):
+                   {"split": 16, "shared_noise": 0}, {"split": 1, "shared_noise": 1}, {"split": 3, "shared_noise": 1},
+                   {"split": 8, "shared_noise": 1}, {"split": 4, "shared_noise": 1}, None):
         got = _run(a, b, "bf16", 1.0, seed=9, period=8, tuning=tuning)
         compare_stats(got, ref, 1.0, str(tuning))
         if base is None:

@@ -37,8 +37,9 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Launch shape of dv_verify_rows, decided from the sizes alone.
 struct Geometry {
   int32_t split = 1;
-  int32_t pruned = 0;       // chunk-max noise table + bound + queued scoring
+  int32_t pruned = 0;       // chunk-max noise table (rows share positions)
   int32_t slice_chunks = 0;
+  int32_t rows_per_block = 1;
   int64_t cmax_rows = 0;
   int64_t cmax_ld = 0;
   size_t cmax_bytes = 0;    // at the start of the workspace, 256-byte aligned size
@@ -46,6 +47,7 @@ struct Geometry {
 };
 
 constexpr size_t kMaxTableBytes = size_t(1) << 30;
+constexpr int32_t kMaxSplit = 16;  // waves of one workgroup
 
 dv_status check_logits(const dv_logits *x, bool need_ptrs) {
   if (!x) return fail(DV_ERR_NULL, "logits descriptor is NULL");
@@ -78,8 +80,8 @@ dv_status choose_geometry(const dv_logits *x, const dv_noise *n, const dv_tuning
   const bool can_share = !greedy && n->pos == nullptr && n->pos_period > 0;
   const int32_t want_shared = t ? t->shared_noise : -1;
   if (t) {
-    if (t->split < 0 || t->split > 64) return fail(DV_ERR_ARG, "tuning.split must be 0..64");
-    if (t->block != 0 && t->block != 256) return fail(DV_ERR_ARG, "tuning.block must be 0 or 256");
+    if (t->split < 0 || t->split > kMaxSplit) return fail(DV_ERR_ARG, "tuning.split must be 0..%d", kMaxSplit);
+    if (t->reserved[0] != 0 || t->reserved[1] != 0) return fail(DV_ERR_ARG, "tuning.reserved must be zero");
     if (want_shared < -1 || want_shared > 1) return fail(DV_ERR_ARG, "tuning.shared_noise must be -1, 0 or 1");
     if (want_shared == 1 && !can_share)
       return fail(DV_ERR_ARG, "shared noise needs temperature > 0, pos == NULL and pos_period > 0");
@@ -103,14 +105,14 @@ dv_status choose_geometry(const dv_logits *x, const dv_noise *n, const dv_tuning
   const int64_t max_by_len = nch / 256 > 0 ? nch / 256 : 1;
   if (split > max_by_len) split = max_by_len;
   if (t && t->split > 0) split = t->split;
-  if (split > 64) split = 64;
+  if (split > kMaxSplit) split = kMaxSplit;
   if (split > nch) split = nch;
   if (split < 1) split = 1;
   g.split = static_cast<int32_t>(split);
   g.slice_chunks = static_cast<int32_t>((nch + split - 1) / split);
-  const int64_t waves = x->rows * split;
-  if ((waves + 3) / 4 > kMaxIndex) return fail(DV_ERR_UNSUPPORTED, "too many rows for one launch");
-  g.workspace = g.cmax_bytes + (split > 1 ? static_cast<size_t>(x->rows) * split * sizeof(dv::Partial) : 0);
+  // a workgroup holds whole rows: 4 waves when split divides 4, else one row
+  g.rows_per_block = 4 % split == 0 ? static_cast<int32_t>(4 / split) : 1;
+  g.workspace = g.cmax_bytes;
   return DV_OK;
 }
 
@@ -162,10 +164,10 @@ dv_status dv_verify_rows(const dv_logits *logits, const dv_noise *noise, const d
   p.pos_period = noise->pos_period;
   p.split = g.split;
   p.slice_chunks = g.slice_chunks;
+  p.rows_per_block = g.rows_per_block;
   p.noise_cmax = g.pruned ? static_cast<float *>(workspace) : nullptr;
   p.cmax_rows = g.cmax_rows;
   p.cmax_ld = g.cmax_ld;
-  p.ws = reinterpret_cast<dv::Partial *>(static_cast<char *>(workspace) + g.cmax_bytes);
   p.out = *out;
   return hip_status(dv::launch_verify(p, stream), "dv_verify_rows launch");
 }

@@ -34,7 +34,7 @@ inline uint32_t seed_word(uint64_t seed) {
   return mix32(a ^ static_cast<uint32_t>(seed));
 }
 
-// ---- per-(row, slice) partial state written to the workspace: 64 bytes ----
+// ---- per-(row, slice) partial state handed between the waves of a row: 64 bytes ----
 // rho: reference (log2 units) the exponentials were taken against, i.e.
 //      e_i = 2^(x_i * log2e - rho); S = sum e_i; W = sum e_i * (x_i*log2e - rho);
 //      D = sum e_v,i * (a_i - b_i) (nats).
@@ -62,10 +62,10 @@ struct VerifyLaunch {
   uint32_t seed_b;     // seed word B
   const int32_t *pos;  // device or NULL
   int64_t pos_period;
-  int32_t split;         // vocabulary slices per row
-  int32_t slice_chunks;  // 16-byte chunks per slice
-  Partial *ws;           // [rows][split] when split > 1
-  float *noise_cmax;     // [cmax_rows][cmax_ld] chunk-max noise table (workspace), or NULL
+  int32_t split;           // vocabulary slices per row: consecutive waves of one workgroup
+  int32_t slice_chunks;    // 16-byte chunks per slice
+  int32_t rows_per_block;  // rows of one workgroup (rows_per_block * split <= 16 waves)
+  float *noise_cmax;       // [cmax_rows][cmax_ld] chunk-max noise table (workspace), or NULL
   int64_t cmax_rows;     // positions 0 .. cmax_rows-1
   int64_t cmax_ld;       // chunks per row
   dv_row_stats out;

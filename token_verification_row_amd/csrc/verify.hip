@@ -25,14 +25,15 @@
 //   * argmax and Gumbel-max tokens are tracked per chunk (value, chunk index);
 //     the lowest index inside the winning chunk is recovered at the end by
 //     re-reading 16 bytes, so the hot loop carries no per-element index;
-//   * noise comes from a counter hash. When rows share positions (the
-//     candidates of a tree level) a small table holds, per (position, chunk),
-//     the largest noise value; a chunk can then be skipped when
-//     max(x)/T + max(noise) is below the best score the wave has seen, and the
-//     chunks that cannot be skipped are queued in LDS with their logits and
-//     scored 64 at a time, one per lane, noise recomputed from the hash;
-//   * lane states are combined across the wave with DPP, then per row (split
-//     rows go through a workspace of 64-byte partials and a merge kernel).
+//   * noise comes from a counter hash. A chunk's Gumbel scores are only
+//     computed when max(x)/T + max(noise) reaches the best score the wave has
+//     seen; the largest noise value of a chunk comes from the largest of its
+//     hash words (two logarithms per chunk instead of two per element) or,
+//     when rows share positions (the candidates of a tree level), from a table
+//     built once per (position, chunk). Chunks that pass are queued in LDS
+//     with their logits and scored 64 at a time, one per lane;
+//   * lane states are combined across the wave with DPP; the vocabulary
+//     slices of a row are waves of one workgroup, combined through LDS.
 #include <climits>
 #include <cmath>
 
@@ -46,10 +47,15 @@ constexpr double kLn2 = 0.693147180559945309417232121458;
 constexpr float kRebase = 64.0f;                                   // log2 units
 constexpr float kOneMinusHalfUlp = 0.999999940395355224609375f;  // 1 - 2^-24
 
-// Noise modes of the streaming kernel.
-enum { kGreedy = 0,   // T = 0: tokens are the argmaxes, no noise
-       kInline = 1,   // per-element noise from the hash
-       kPruned = 2 }; // chunk-max noise table + bound + queued scoring
+// Noise modes of the streaming kernel. With noise, a chunk is scored only when
+// a bound on its best perturbed score reaches the best score seen so far; the
+// bound's noise term is the largest noise value of the chunk, taken
+//   kHashBound:  from the chunk's hash words, in registers (rows with their
+//                own noise);
+//   kTableBound: from a table built once per position (rows sharing noise).
+enum { kGreedy = 0,      // T = 0: tokens are the argmaxes, no noise
+       kHashBound = 1,
+       kTableBound = 2 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -110,6 +116,24 @@ __device__ __forceinline__ void noise_chunk(float (&g)[Chunk<BF16>::N], int32_t 
   const uint32_t i0 = static_cast<uint32_t>(c) * N;
 #pragma unroll
   for (int j = 0; j < N; ++j) g[j] = noise_at(key, i0 + j);
+}
+
+// Upper bound of the noise of chunk c: u, and with it G, grows with the hash
+// word, so the largest word of the chunk gives its largest noise value. The
+// slack covers a hardware log2 that is not exactly monotone (1 ulp), so the
+// bound is never below a noise value the scoring recomputes.
+__device__ __forceinline__ float noise_bound_of_word(uint32_t hmax) {
+  const float g = gumbel_log2(hmax);
+  return g + __builtin_fabsf(g) * 0x1p-20f + 0x1p-20f;
+}
+
+template <int N>
+__device__ __forceinline__ float chunk_noise_bound(int32_t c, uint32_t key) {
+  const uint32_t i0 = static_cast<uint32_t>(c) * N;
+  uint32_t hm = 0;
+#pragma unroll
+  for (int j = 0; j < N; ++j) hm = max(hm, mix32(key ^ ((i0 + j) * kIndexStep)));
+  return noise_bound_of_word(hm);
 }
 
 // Per-lane accumulator of one (row, slice).
@@ -325,6 +349,8 @@ __device__ __forceinline__ void fold_stats(Lane &st, float (&a)[N], float (&b)[N
 }
 
 // One chunk, statistics and (unless greedy) tokens with noise from the hash.
+// Chunks reach the token bookkeeping out of index order (queued scoring), so
+// ties compare chunk indices.
 template <bool BF16, int MODE, bool MASKED>
 __device__ __forceinline__ void fold_chunk(Lane &st, const u32x4 &wa, const u32x4 &wb, int32_t c, uint32_t key,
                                            float cT, int nvalid) {
@@ -336,7 +362,7 @@ __device__ __forceinline__ void fold_chunk(Lane &st, const u32x4 &wa, const u32x
   if constexpr (MODE != kGreedy) {
     float g[N];
     noise_chunk<BF16>(g, c, key);
-    fold_tokens<N, MASKED, MODE == kPruned>(st, x, y, g, c, cT, nvalid);
+    fold_tokens<N, MASKED, true>(st, x, y, g, c, cT, nvalid);
   }
 }
 
@@ -371,7 +397,7 @@ __device__ __forceinline__ void flush_queue(Lane &st, ScoreQueue &q, int n, uint
 constexpr int kStep = DV_STEP_CHUNKS;  // chunks per lane per step of the streaming loop
 
 // Raw registers of K chunks (c, c + 64, ..., c + 64 (K-1)) of both matrices
-// and, when pruning, the largest noise value of each chunk.
+// and, with a noise table, the largest noise value of each chunk.
 template <bool BF16, bool PRUNE, int K>
 struct StepRegs {
   u32x4 a[K], b[K];
@@ -399,18 +425,19 @@ struct StepRegs {
     for (int k = 0; k < K; ++k) {
       const int32_t ck = c + 64 * k;
       const bool valid = ck < cend;
-      if constexpr (MODE == kPruned) {
+      if constexpr (MODE != kGreedy) {
         // A chunk can hold a model's Gumbel-max token only if the bound
         // max(x)/T + max(noise) reaches the best score the wave has already
         // seen (fma is monotone, so the bound holds for the rounded scores;
-        // >= keeps chunks that could tie). The others are queued.
+        // >= keeps chunks that could tie). Those are queued.
         bool need = false;
         if (valid) {
           float x[N], y[N], cma, cmb;
           widen<BF16>(a[k], x);
           widen<BF16>(b[k], y);
           fold_stats<N, false>(st, x, y, ck, N, cma, cmb);
-          need = __builtin_fmaf(cma, cT, gm[k]) >= st.wb_v || __builtin_fmaf(cmb, cT, gm[k]) >= st.wb_d;
+          const float g = MODE == kTableBound ? gm[k] : chunk_noise_bound<N>(ck, key);
+          need = __builtin_fmaf(cma, cT, g) >= st.wb_v || __builtin_fmaf(cmb, cT, g) >= st.wb_d;
         }
         const unsigned long long mask = __ballot(need);
         if (mask) {
@@ -429,7 +456,7 @@ struct StepRegs {
           nq += cnt;
         }
       } else {
-        if (valid) fold_chunk<BF16, MODE, false>(st, a[k], b[k], ck, key, cT, N);
+        if (valid) fold_chunk<BF16, kGreedy, false>(st, a[k], b[k], ck, key, cT, N);
       }
     }
   }
@@ -455,7 +482,7 @@ __device__ __forceinline__ void scan_slice(Lane &st, const u32x4 *ra, const u32x
   if (nsteps > 0) {
     // in-bounds address for chunks past the end (their data is not used)
     auto at = [&](int32_t cc) { return cc < cend ? cc : c0; };
-    StepRegs<BF16, MODE == kPruned, kStep> X, Y;
+    StepRegs<BF16, MODE == kTableBound, kStep> X, Y;
     int32_t c = c0 + lane;
     X.load(ra, rb, g_cmax, c, at);
     for (int32_t t = 0;;) {
@@ -471,7 +498,7 @@ __device__ __forceinline__ void scan_slice(Lane &st, const u32x4 *ra, const u32x
       c += kSpan;
     }
   }
-  if constexpr (MODE == kPruned) {
+  if constexpr (MODE != kGreedy) {
     if (nq > 0) flush_queue<BF16>(st, *q, nq, key, cT, lane);
   }
   // the last, partly filled chunk of the row (vocab not a multiple of N)
@@ -603,116 +630,113 @@ __device__ __forceinline__ void row_geometry(const VerifyLaunch &p, int32_t &nfu
   nch = nfull + (nvalid_tail ? 1 : 0);
 }
 
-// One wave per (row, slice).
+// Per-wave LDS of the streaming kernel: the score queue (with noise) and the
+// reduced state handed to the first wave of the row (split rows).
+struct WaveLds {
+  ScoreQueue q;
+  Partial part;
+};
+
+// One wave per (row, slice); the split slices of a row are consecutive waves
+// of one workgroup and are combined through LDS by the row's first wave.
 template <bool BF16, int MODE>
-__global__ __launch_bounds__(256) void verify_rows_kernel(VerifyLaunch p) {
-  __shared__ ScoreQueue queues[MODE == kPruned ? 4 : 1];
+__global__ __launch_bounds__(1024) void verify_rows_kernel(VerifyLaunch p) {
+  extern __shared__ WaveLds lds[];
   // the wave index is uniform across the wave: keep it (and all row
   // addressing derived from it) in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int64_t task = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + wave;
-  if (task >= p.rows * p.split) return;
-  const int64_t r = task / p.split;
-  const int32_t s = static_cast<int32_t>(task % p.split);
-  int32_t nfull, nch;
-  int nvalid_tail;
-  row_geometry<BF16>(p, nfull, nvalid_tail, nch);
-  const int32_t c0 = s * p.slice_chunks;
-  const int32_t c1 = min(c0 + p.slice_chunks, nch);
-  const size_t row_bytes = static_cast<size_t>(p.ld) * (BF16 ? 2 : 4);
-  const u32x4 *ra = reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.va) + r * row_bytes);
-  const u32x4 *rb = reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.vb) + r * row_bytes);
-  const int32_t pos = MODE == kGreedy ? 0 : position_of(p, r);
-  const uint32_t key = MODE == kGreedy ? 0u : row_key(p.seed_b, pos);
-  const float *gcm = MODE == kPruned ? p.noise_cmax + static_cast<int64_t>(pos) * p.cmax_ld : nullptr;
+  const int split = p.split;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * p.rows_per_block + wave / split;
+  const int32_t s = wave % split;
+  const bool live = r < p.rows;
   Lane st;
   st.init();
-  scan_slice<BF16, MODE>(st, ra, rb, c0, c1, nfull, nvalid_tail, p.cT, key, gcm,
-                         MODE == kPruned ? &queues[wave] : nullptr, lane);
-  const Partial t = wave_reduce(st);
-  if (p.split == 1) {
-    finalize_row<BF16>(p, r, t, lane);
-  } else if (lane == 0) {
-    p.ws[r * p.split + s] = t;
+  if (live) {
+    int32_t nfull, nch;
+    int nvalid_tail;
+    row_geometry<BF16>(p, nfull, nvalid_tail, nch);
+    const int32_t c0 = s * p.slice_chunks;
+    const int32_t c1 = min(c0 + p.slice_chunks, nch);
+    const size_t row_bytes = static_cast<size_t>(p.ld) * (BF16 ? 2 : 4);
+    const u32x4 *ra = reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.va) + r * row_bytes);
+    const u32x4 *rb = reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.vb) + r * row_bytes);
+    const int32_t pos = MODE == kGreedy ? 0 : position_of(p, r);
+    const uint32_t key = MODE == kGreedy ? 0u : row_key(p.seed_b, pos);
+    const float *gcm = MODE == kTableBound ? p.noise_cmax + static_cast<int64_t>(pos) * p.cmax_ld : nullptr;
+    scan_slice<BF16, MODE>(st, ra, rb, c0, c1, nfull, nvalid_tail, p.cT, key, gcm,
+                           MODE == kGreedy ? nullptr : &lds[wave].q, lane);
   }
+  const Partial t = wave_reduce(st);
+  if (split == 1) {
+    if (live) finalize_row<BF16>(p, r, t, lane);
+    return;
+  }
+  if (lane == 0) lds[wave].part = t;
+  __syncthreads();
+  if (!live || s != 0) return;
+  // lane l takes slice l of the row
+  Lane m;
+  m.init();
+  if (lane < split) {
+    const Partial x = lds[wave + lane].part;
+    m.rho_v = x.rho_v;
+    m.S_v = x.S_v;
+    m.W_v = x.W_v;
+    m.D_v = x.D_v;
+    m.rho_d = x.rho_d;
+    m.S_d = x.S_d;
+    m.m_v = x.m_v;
+    m.m_d = x.m_d;
+    m.s_v = x.s_v;
+    m.s_d = x.s_d;
+    m.cm_v = x.cm_v;
+    m.cm_d = x.cm_d;
+    m.cs_v = x.cs_v;
+    m.cs_d = x.cs_d;
+  }
+  finalize_row<BF16>(p, r, wave_reduce(m), lane);
 }
 
-// Chunk-max noise table: entry (q, c) is the largest noise value of position
-// q over the valid elements of chunk c (one thread per entry). It is the bound
-// that lets the streaming pass skip chunks that cannot hold a Gumbel-max token.
+// Chunk-max noise table: entry (q, c) bounds the noise of position q over the
+// valid elements of chunk c (one thread per entry), as chunk_noise_bound does
+// in registers. Entries number below 2^28 (the table is at most 1 GiB).
 template <int N>
-__global__ __launch_bounds__(256) void noise_cmax_kernel(uint32_t seed_b, int64_t npos, int64_t vocab, int64_t ld,
+__global__ __launch_bounds__(256) void noise_cmax_kernel(uint32_t seed_b, uint32_t n, uint32_t ld, int64_t vocab,
                                                         float *cmax) {
-  const int64_t n = npos * ld;
-  for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < n;
-       t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t q = t / ld, c = t % ld;
-    const uint32_t key = row_key(seed_b, static_cast<int32_t>(q));
-    float m = -INFINITY;
+  const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+  if (t >= n) return;
+  const uint32_t q = t / ld, c = t - q * ld;
+  const uint32_t key = row_key(seed_b, static_cast<int32_t>(q));
+  uint32_t hm = 0;
 #pragma unroll
-    for (int j = 0; j < N; ++j) {
-      const int64_t i = c * N + j;
-      if (i < vocab) m = fmaxf(m, noise_at(key, static_cast<uint32_t>(i)));
-    }
-    cmax[t] = m;
+  for (int j = 0; j < N; ++j) {
+    const int64_t i = static_cast<int64_t>(c) * N + j;
+    if (i < vocab) hm = max(hm, mix32(key ^ (static_cast<uint32_t>(i) * kIndexStep)));
   }
+  cmax[t] = noise_bound_of_word(hm);
 }
 
-// Combine the split partials of each row and finish it: one wave per row,
-// lane s holds slice s (split <= 64).
-template <bool BF16>
-__global__ __launch_bounds__(256) void verify_merge_kernel(VerifyLaunch p) {
-  const int lane = threadIdx.x & 63;
-  const int64_t r =
-      static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (r >= p.rows) return;
-  Lane st;
-  st.init();
-  if (lane < p.split) {
-    const Partial x = p.ws[r * p.split + lane];
-    st.rho_v = x.rho_v;
-    st.S_v = x.S_v;
-    st.W_v = x.W_v;
-    st.D_v = x.D_v;
-    st.rho_d = x.rho_d;
-    st.S_d = x.S_d;
-    st.m_v = x.m_v;
-    st.m_d = x.m_d;
-    st.s_v = x.s_v;
-    st.s_d = x.s_d;
-    st.cm_v = x.cm_v;
-    st.cm_d = x.cm_d;
-    st.cs_v = x.cs_v;
-    st.cs_d = x.cs_d;
-  }
-  const Partial t = wave_reduce(st);
-  finalize_row<BF16>(p, r, t, lane);
+template <bool BF16, int MODE>
+hipError_t launch_rows(const VerifyLaunch &p, hipStream_t stream) {
+  const unsigned blocks = static_cast<unsigned>((p.rows + p.rows_per_block - 1) / p.rows_per_block);
+  const int waves = p.rows_per_block * p.split;
+  const size_t lds = MODE == kGreedy ? (p.split > 1 ? waves * sizeof(WaveLds) : 0) : waves * sizeof(WaveLds);
+  hipLaunchKernelGGL((verify_rows_kernel<BF16, MODE>), dim3(blocks), dim3(64 * waves), lds, stream, p);
+  return hipGetLastError();
 }
 
 template <bool BF16>
 hipError_t launch_typed(const VerifyLaunch &p, hipStream_t stream) {
   constexpr int N = Chunk<BF16>::N;
-  const int64_t waves = p.rows * p.split;
-  const unsigned blocks = static_cast<unsigned>((waves + 3) / 4);
   if (p.noise_cmax) {
-    const int64_t n = p.cmax_rows * p.cmax_ld;
-    int64_t tb = (n + 255) / 256;
-    if (tb > 16384) tb = 16384;
-    hipLaunchKernelGGL(noise_cmax_kernel<N>, dim3(static_cast<unsigned>(tb)), dim3(256), 0, stream, p.seed_b,
-                       p.cmax_rows, p.vocab, p.cmax_ld, p.noise_cmax);
+    const uint32_t n = static_cast<uint32_t>(p.cmax_rows * p.cmax_ld);
+    hipLaunchKernelGGL(noise_cmax_kernel<N>, dim3((n + 255) / 256), dim3(256), 0, stream, p.seed_b, n,
+                       static_cast<uint32_t>(p.cmax_ld), p.vocab, p.noise_cmax);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((verify_rows_kernel<BF16, kPruned>), dim3(blocks), dim3(256), 0, stream, p);
-  } else if (p.greedy) {
-    hipLaunchKernelGGL((verify_rows_kernel<BF16, kGreedy>), dim3(blocks), dim3(256), 0, stream, p);
-  } else {
-    hipLaunchKernelGGL((verify_rows_kernel<BF16, kInline>), dim3(blocks), dim3(256), 0, stream, p);
+    return launch_rows<BF16, kTableBound>(p, stream);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.split == 1) return e;
-  const unsigned mblocks = static_cast<unsigned>((p.rows + 3) / 4);
-  hipLaunchKernelGGL(verify_merge_kernel<BF16>, dim3(mblocks), dim3(256), 0, stream, p);
-  return hipGetLastError();
+  return p.greedy ? launch_rows<BF16, kGreedy>(p, stream) : launch_rows<BF16, kHashBound>(p, stream);
 }
 
 }  // namespace

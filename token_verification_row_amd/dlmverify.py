@@ -49,8 +49,7 @@ class dv_row_stats(ctypes.Structure):
 
 
 class dv_tuning(ctypes.Structure):
-    _fields_ = [("split", ctypes.c_int32), ("block", ctypes.c_int32), ("shared_noise", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+    _fields_ = [("split", ctypes.c_int32), ("shared_noise", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
 
 
 class dv_decide_args(ctypes.Structure):
@@ -158,8 +157,10 @@ def _tuning_desc(tuning):
     if tuning is None:
         return None
     t = dict(tuning)
-    return dv_tuning(split=int(t.get("split", 0)), block=int(t.get("block", 0)),
-                     shared_noise=int(t.get("shared_noise", -1)), reserved=0)
+    unknown = set(t) - {"split", "shared_noise"}
+    if unknown:
+        raise ValueError(f"unknown tuning keys {sorted(unknown)}")
+    return dv_tuning(split=int(t.get("split", 0)), shared_noise=int(t.get("shared_noise", -1)))
 
 
 def dv_verify_workspace_bytes(verifier, drafter, temperature=0.0, seed=0, pos=None, pos_period=0, *,

@@ -46,7 +46,7 @@ typedef enum dv_status {
   DV_ERR_ALIGN = 4,       /* a pointer or row pitch is not 16-byte aligned */
   DV_ERR_ARG = 5,         /* a scalar argument is out of range (T, tau, theta, k, rule, ...) */
   DV_ERR_WORKSPACE = 6,   /* workspace missing or too small */
-  DV_ERR_UNSUPPORTED = 7, /* valid request this build cannot serve (e.g. seq_len too long) */
+  DV_ERR_UNSUPPORTED = 7, /* a valid request the library cannot serve (e.g. seq_len too long) */
   DV_ERR_HIP = 8          /* a HIP launch or runtime call failed */
 } dv_status;
 

@@ -26,6 +26,30 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 STAT_BYTES_PER_ROW = 36      # 5 float32 + 4 int32 outputs
+VERIFY_SOURCE = os.path.join(ROOT, "token_verification_row_amd", "csrc", "verify.hip")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "verify_rows_traffic.json")
+
+
+def measured_traffic(workload: int):
+    """HBM bytes per verify pass from the committed profiler counters, or None.
+
+    The record holds FETCH_SIZE and WRITE_SIZE per pass (already scaled by the
+    plain-copy calibration) and the SHA-256 of the kernel source they were
+    taken on; a changed kernel gives None until the counters are taken again.
+    """
+    import hashlib
+
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+        with open(VERIFY_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    entry = rec.get("workloads", {}).get(str(workload))
+    if rec.get("verify_hip_sha256") != sha or not entry:
+        return None
+    return entry["fetch_bytes"] + entry["write_bytes"]
 
 
 def _oracle_block(args):
@@ -106,9 +130,11 @@ def main() -> int:
     for _ in range(copies - 1):
         inputs.append((inputs[0][0].clone(), inputs[0][1].clone()))
     period = w.pos_period
-    d_in_np, d_out_np = (np.random.default_rng(1).random(R, dtype=np.float32) for _ in range(2))
-    d_in = torch.from_numpy(d_in_np).to(dev)
-    d_out = torch.from_numpy(d_out_np).to(dev)
+    d_in_np, d_out_np = W.diffusion_inputs(w) if w.n_committed else \
+        tuple(np.random.default_rng(1).random(R, dtype=np.float32) for _ in range(2))
+    d_in = torch.from_numpy(np.ascontiguousarray(d_in_np, np.float32)).to(dev)
+    d_out = torch.from_numpy(np.ascontiguousarray(d_out_np, np.float32)).to(dev)
+    committed = torch.from_numpy(W.committed_rows(w)).to(dev) if w.n_committed else None
     outs = [dv.dv_verify_rows(*inputs[0], temperature=w.temperature, seed=w.seed, pos_period=period)
             for _ in range(2)]
     seq_len = w.group_len or w.L
@@ -117,6 +143,7 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
 
     def step(i, ev=None):
+        """verify -> decide -> seed score -> select, with the workload's own rule and selection score."""
         a, b = inputs[i % copies]
         out = outs[i % 2]
         if ev is not None:
@@ -125,13 +152,20 @@ def main() -> int:
                                 workspace=out.get("_workspace"))
         if ev is not None:
             ev[1].record(stream)
+        score = dv.dv_seed_score(got["entropy"], d_in, d_out, committed)
+        if w.n_committed:
+            # COVER: the top seeds among committed positions are re-verified (KEEP / REPLACE / REMASK)
+            _, _, _, mask = dv.dv_select_topk(score.view(nseq, seq_len), k, eligible=committed.view(nseq, seq_len),
+                                              want_mask=True)
+            dv.dv_decide("COVER", got, conf_thr=w.conf_thr, mask_token=-1, subject=mask.view(-1))
+            return
         if w.group_len:
             dv.dv_decide("COUPLED_ACCEPT", got, mask_token=-1, group_len=w.group_len, want_prefix=True,
                          want_best=True)
         else:
-            dv.dv_decide("KL_OR_CONF", got, tau_kl=0.05, conf_thr=0.9, mask_token=-1)
-        score = dv.dv_seed_score(got["entropy"], d_in, d_out)
-        dv.dv_select_topk(score.view(nseq, seq_len), k)
+            dv.dv_decide("KL_OR_CONF", got, tau_kl=w.tau_kl or 0.05, conf_thr=w.conf_thr or 0.9, mask_token=-1)
+        # workload 5 ranks positions by KL; the others by the seed score
+        dv.dv_select_topk((got["kl"] if w.number == 5 else score).view(nseq, seq_len), k)
 
     for i in range(args.warmup):
         step(i)
@@ -184,10 +218,11 @@ def main() -> int:
                                + (f", noise shared per position (period {period}), coupled acceptance per "
                                   f"{w.group_len}-row candidate" if period else ""),
                    "rows": R, "vocab": V, "input_copies": copies,
-                   "step": "dv_verify_rows + dv_decide + dv_seed_score + dv_select_topk"},
+                   "step": "dv_verify_rows + dv_seed_score + dv_select_topk + dv_decide"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "kernel": "dv_verify_rows (verify pass + split merge)", "avg_us": verify_us,
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(w.number),
+                     "kernel": "dv_verify_rows (noise table when rows share positions + streaming verify kernel)",
+                     "avg_us": verify_us,
                      "bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
     }

@@ -98,6 +98,21 @@ def test_small_shapes(dtype, rows, V, T):
     compare_stats(got, ref, T, f"{dtype} {rows}x{V} T={T}")
 
 
+@pytest.mark.parametrize("dtype,V", [("bf16", (1 << 20) + 5), ("fp32", (1 << 20) + 3)])
+def test_large_vocab_ragged(dtype, V):
+    """A vocabulary of about 2^20 with a partly filled last chunk: chunk indices past 2^17, long slices,
+    the noise table over many chunks (period 2 over 6 rows) and the per-row hash bound."""
+    print(f"case: large vocab {dtype} V={V}", flush=True)
+    a, b = _peaked(6, V, V, dtype)
+    for T in (0.0, 1.0):
+        for period, tuning in ((0, None), (2, {"shared_noise": 1}), (2, {"shared_noise": 0, "split": 16})):
+            if T == 0.0 and period:
+                continue
+            got = _run(a, b, dtype, T, seed=21, period=period, tuning=tuning)
+            ref = oracle_rows(a, b, dtype, T, 21, _positions(6, None, period))
+            compare_stats(got, ref, T, f"large vocab {dtype} T={T} period={period} {tuning}")
+
+
 def test_explicit_positions_and_period():
     print("case: explicit positions / period", flush=True)
     a, b = _peaked(40, 3001, 11, "bf16")

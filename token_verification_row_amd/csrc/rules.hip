@@ -116,6 +116,62 @@ __global__ __launch_bounds__(1024) void best_group_kernel(const int32_t *prefix,
   }
 }
 
+// Small batches in one launch: one workgroup finds the first breaking row of
+// every group (LDS atomicMin over the rows), writes the decisions, the prefixes
+// and the best group. The same results as decide_kernel + best_group_kernel.
+constexpr int64_t kSmallDecideRows = 16384;
+constexpr int64_t kSmallDecideGroups = 1024;
+
+__global__ __launch_bounds__(1024) void decide_small_kernel(DecideLaunch p) {
+  __shared__ int32_t s_first[kSmallDecideGroups];
+  __shared__ long long s_key[1024];
+  const int tid = threadIdx.x;
+  const int64_t G = p.group_len;  // > 0 and dividing rows
+  const int64_t ngroups = p.rows / G;
+  const bool coupled = p.rule == DV_RULE_COUPLED_ACCEPT;
+  for (int64_t g = tid; g < ngroups; g += 1024) s_first[g] = static_cast<int32_t>(G);
+  __syncthreads();
+  for (int64_t r = tid; r < p.rows; r += 1024) {
+    if (!is_subject(p, r)) continue;
+    const int32_t cur = current_token(p, r);
+    const bool brk = coupled ? (p.tok_v[r] != cur) : (rule_of_row(p, r, cur) != DV_KEEP);
+    if (brk) atomicMin(&s_first[r / G], static_cast<int32_t>(r % G));
+  }
+  __syncthreads();
+  for (int64_t r = tid; r < p.rows; r += 1024) {
+    const int32_t cur = current_token(p, r);
+    uint8_t d = DV_NONE;
+    if (is_subject(p, r)) {
+      if (coupled) {
+        const int64_t j = r % G, first = s_first[r / G];
+        d = j < first ? DV_KEEP : (j == first ? DV_REPLACE : DV_REMASK);
+      } else {
+        d = rule_of_row(p, r, cur);
+      }
+    }
+    emit(p, r, d, cur);
+  }
+  long long key = LLONG_MIN;
+  for (int64_t g = tid; g < ngroups; g += 1024) {
+    const int32_t f = s_first[g];
+    if (p.prefix_len) p.prefix_len[g] = f;
+    const long long k = (static_cast<long long>(f) << 32) | static_cast<long long>(0xFFFFFFFFu - static_cast<uint32_t>(g));
+    key = k > key ? k : key;
+  }
+  if (p.best_group == nullptr) return;  // uniform: no barrier follows for anyone
+  s_key[tid] = key;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if (tid < o) {
+      const long long other = s_key[tid + o];
+      if (other > s_key[tid]) s_key[tid] = other;
+    }
+    __syncthreads();
+  }
+  if (tid == 0)
+    p.best_group[0] = ngroups > 0 ? static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(s_key[0] & 0xFFFFFFFFll)) : -1;
+}
+
 // ------------------------------------------------------------ seed score ----
 // [COVER] §2, the Score equation: u (1 + d_in) / (1 + d_out).
 __global__ __launch_bounds__(256) void seed_score_kernel(int64_t rows, const float *u, const float *d_in,
@@ -219,6 +275,10 @@ __global__ __launch_bounds__(256) void debug_hash_kernel(uint32_t seed_b, const 
 hipError_t launch_decide(const DecideLaunch &p, hipStream_t stream) {
   const int64_t G = p.group_len > 0 ? p.group_len : 64;
   const int64_t ngroups = (p.rows + G - 1) / G;
+  if (p.group_len > 0 && p.rows <= kSmallDecideRows && ngroups <= kSmallDecideGroups) {
+    hipLaunchKernelGGL(decide_small_kernel, dim3(1), dim3(1024), 0, stream, p);
+    return hipGetLastError();
+  }
   if (p.rows > 0) {
     const unsigned blocks = static_cast<unsigned>((ngroups + 3) / 4);
     hipLaunchKernelGGL(decide_kernel, dim3(blocks), dim3(256), 0, stream, p);

@@ -29,12 +29,14 @@ Modules:
   accepted prefix per candidate.
 * ``select``    COVER's seed score and the per-sequence top-k / threshold
   selection.
+* ``tree``      acceptance over a tree of candidate block states and the
+  commit list it yields.
 
 Every function is pinned by tests under ``tests/`` against closed forms,
 library routines, invariants or brute force; none of the pages prints a
 worked example, so no end-to-end value is pinned by the pages themselves.
 """
 
-from . import rowstats, noise, decide, select  # noqa: F401
+from . import rowstats, noise, decide, select, tree  # noqa: F401
 
-__all__ = ["rowstats", "noise", "decide", "select"]
+__all__ = ["rowstats", "noise", "decide", "select", "tree"]

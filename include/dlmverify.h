@@ -211,6 +211,52 @@ dv_status dv_select_topk(int64_t nseq, int64_t seq_len, const float *score, cons
                          int32_t k, int32_t largest, int32_t use_thr, float thr, int32_t *out_idx,
                          float *out_val, int32_t *out_count, uint8_t *out_mask, hipStream_t stream);
 
+/* Shape of dv_tree_accept's input: ntrees independent trees of `nodes` nodes
+ * each over blocks of `block_len` positions. */
+typedef struct dv_tree_args {
+  int64_t ntrees;     /* >= 0 */
+  int64_t nodes;      /* 1..2048 per tree; node 0 is the root */
+  int64_t block_len;  /* 1..1024 positions per block state */
+} dv_tree_args;
+
+/* Acceptance over trees of candidate block states and the commit it yields
+ * ([SPOT] §1 "Key Terms & Definitions" and §3 "Method & Key Results": the
+ * drafter proposes a multi-level tree of block states, the target verifies
+ * all of them in one batched pass, and under coupled noise a proposed child is
+ * right exactly when it equals the target's own transition).
+ * Inputs, all device, trees consecutive:
+ *   parent      int32 [ntrees][nodes], 0 <= parent[i] < i for i >= 1 (the
+ *               root's entry is ignored); node i >= 1 commits node_tok[i] at
+ *               block position node_pos[i] on top of its parent's state
+ *   node_pos, node_tok  int32 [ntrees][nodes]
+ *   root_masked uint8 [ntrees][block_len], nonzero = masked in the root state
+ *   conf, tok_v float32 / int32 [ntrees][nodes][block_len]: the verifier's
+ *               confidence and shared-noise token of every position of every
+ *               node's state (the dv_row_stats of those rows, row index
+ *               (tree * nodes + node) * block_len + position)
+ * The target's transition from a state commits its masked position (the
+ * root's masked positions minus those committed on the path) of highest conf,
+ * lowest position on ties, with that position's tok_v. A node is accepted
+ * when its parent is and (node_pos, node_tok) equals the parent's transition;
+ * the root is accepted. A node whose parent breaks the order, or whose path
+ * is longer than block_len, is not accepted.
+ * Outputs, each may be NULL: accepted uint8 [ntrees][nodes]; depth int32
+ * [ntrees][nodes] (commits from the root, -1 if not accepted); best_node
+ * int32 [ntrees] (deepest accepted node, lowest index on ties); commit_pos /
+ * commit_tok int32 [ntrees][block_len] (the path's commits in order, then the
+ * target's transition at the best node if it has one; padded with -1);
+ * commit_len int32 [ntrees]; block_tokens int32 [ntrees][block_len] (in/out:
+ * committed positions take their tokens); out_masked uint8
+ * [ntrees][block_len] (root_masked with committed positions cleared; may be
+ * the root_masked buffer itself).
+ * Errors: DV_ERR_NULL (args or a required input NULL), DV_ERR_SHAPE (sizes out
+ * of range). */
+dv_status dv_tree_accept(const dv_tree_args *args, const int32_t *parent, const int32_t *node_pos,
+                         const int32_t *node_tok, const uint8_t *root_masked, const float *conf,
+                         const int32_t *tok_v, uint8_t *accepted, int32_t *depth, int32_t *best_node,
+                         int32_t *commit_pos, int32_t *commit_tok, int32_t *commit_len,
+                         int32_t *block_tokens, uint8_t *out_masked, hipStream_t stream);
+
 /* The noise hash words h[r][i] (uint32, device [rows][vocab]) for the
  * positions described as in dv_noise. For testing the noise generator bit
  * for bit. Errors: DV_ERR_NULL, DV_ERR_SHAPE. */

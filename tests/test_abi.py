@@ -30,7 +30,8 @@ def _declared_functions():
 def test_exports_every_declared_function(lib):
     names = _declared_functions()
     assert names == sorted(["dv_verify_workspace_bytes", "dv_verify_rows", "dv_decide", "dv_seed_score",
-                           "dv_select_topk", "dv_debug_hash", "dv_status_str", "dv_last_error", "dv_version"])
+                           "dv_select_topk", "dv_tree_accept", "dv_debug_hash", "dv_status_str", "dv_last_error",
+                           "dv_version"])
     for n in names:
         assert hasattr(lib, n), n
     assert lib.dv_version() == 1
@@ -174,3 +175,20 @@ def test_binding_refuses_cpu_tensors():
         B.dv_verify_rows(a, a)
     with pytest.raises(TypeError):
         B.dv_seed_score(torch.zeros(3), torch.zeros(3), torch.zeros(3))
+
+
+def _tree(lib, ntrees=1, nodes=4, block_len=8, inputs=FAKE, args=True):
+    a = B.dv_tree_args(ntrees=ntrees, nodes=nodes, block_len=block_len)
+    return lib.dv_tree_accept(ctypes.byref(a) if args else None, inputs, inputs, inputs, inputs, inputs, inputs,
+                              None, None, None, None, None, None, None, None, None)
+
+
+def test_tree_validation(lib):
+    assert _tree(lib, args=False) == B.DV_ERR_NULL
+    assert _tree(lib, ntrees=-1) == B.DV_ERR_SHAPE
+    assert _tree(lib, nodes=0) == B.DV_ERR_SHAPE
+    assert _tree(lib, nodes=2049) == B.DV_ERR_SHAPE
+    assert _tree(lib, block_len=0) == B.DV_ERR_SHAPE
+    assert _tree(lib, block_len=1025) == B.DV_ERR_SHAPE
+    assert _tree(lib, inputs=None) == B.DV_ERR_NULL
+    assert _tree(lib, ntrees=0, inputs=None) == B.DV_OK        # nothing to do: no launch

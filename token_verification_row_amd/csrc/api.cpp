@@ -271,6 +271,40 @@ dv_status dv_select_topk(int64_t nseq, int64_t seq_len, const float *score, cons
   return hip_status(dv::launch_select_topk(p, stream), "dv_select_topk launch");
 }
 
+dv_status dv_tree_accept(const dv_tree_args *a, const int32_t *parent, const int32_t *node_pos,
+                         const int32_t *node_tok, const uint8_t *root_masked, const float *conf,
+                         const int32_t *tok_v, uint8_t *accepted, int32_t *depth, int32_t *best_node,
+                         int32_t *commit_pos, int32_t *commit_tok, int32_t *commit_len, int32_t *block_tokens,
+                         uint8_t *out_masked, hipStream_t stream) {
+  if (!a) return fail(DV_ERR_NULL, "args is NULL");
+  if (a->ntrees < 0 || a->ntrees > kMaxIndex) return fail(DV_ERR_SHAPE, "ntrees out of range");
+  if (a->nodes < 1 || a->nodes > dv::kMaxTreeNodes)
+    return fail(DV_ERR_SHAPE, "nodes must be 1..%d", dv::kMaxTreeNodes);
+  if (a->block_len < 1 || a->block_len > dv::kMaxTreeBlockLen)
+    return fail(DV_ERR_SHAPE, "block_len must be 1..%d", dv::kMaxTreeBlockLen);
+  if (a->ntrees > 0 && (!parent || !node_pos || !node_tok || !root_masked || !conf || !tok_v))
+    return fail(DV_ERR_NULL, "an input array is NULL");
+  dv::TreeLaunch p{};
+  p.ntrees = a->ntrees;
+  p.nodes = a->nodes;
+  p.block_len = a->block_len;
+  p.parent = parent;
+  p.node_pos = node_pos;
+  p.node_tok = node_tok;
+  p.root_masked = root_masked;
+  p.conf = conf;
+  p.tok_v = tok_v;
+  p.accepted = accepted;
+  p.depth = depth;
+  p.best_node = best_node;
+  p.commit_pos = commit_pos;
+  p.commit_tok = commit_tok;
+  p.commit_len = commit_len;
+  p.block_tokens = block_tokens;
+  p.out_masked = out_masked;
+  return hip_status(dv::launch_tree_accept(p, stream), "dv_tree_accept launch");
+}
+
 dv_status dv_debug_hash(uint64_t seed, const int32_t *pos, int64_t pos_period, int64_t rows, int64_t vocab,
                         uint32_t *out, hipStream_t stream) {
   if (rows < 0 || rows > kMaxIndex || vocab < 0 || vocab > kMaxIndex) return fail(DV_ERR_SHAPE, "size out of range");

@@ -104,6 +104,20 @@ struct SelectLaunch {
 constexpr int64_t kMaxSelectLen = 16384;
 hipError_t launch_select_topk(const SelectLaunch &p, hipStream_t stream);
 
+constexpr int kMaxTreeNodes = 2048;
+constexpr int kMaxTreeBlockLen = 1024;
+struct TreeLaunch {
+  int64_t ntrees, nodes, block_len;
+  const int32_t *parent, *node_pos, *node_tok;
+  const uint8_t *root_masked;
+  const float *conf;
+  const int32_t *tok_v;
+  uint8_t *accepted;
+  int32_t *depth, *best_node, *commit_pos, *commit_tok, *commit_len, *block_tokens;
+  uint8_t *out_masked;
+};
+hipError_t launch_tree_accept(const TreeLaunch &p, hipStream_t stream);
+
 hipError_t launch_debug_hash(uint32_t seed_b, const int32_t *pos, int64_t pos_period, int64_t rows,
                              int64_t vocab, uint32_t *out, hipStream_t stream);
 

@@ -1,0 +1,211 @@
+// Acceptance over trees of candidate block states and the commit it yields
+// ([SPOT] §1 "Key Terms & Definitions", §3 "Method & Key Results": the
+// drafter proposes a multi-level tree of block states, the target verifies all
+// of them in one batched pass, and under coupled noise a proposed child is
+// right exactly when it equals the target's own transition). gfx950.
+//
+// One workgroup per tree:
+//   1. the node arrays go to LDS;
+//   2. one wave per node finds the target's transition from the node's state:
+//      the masked positions are the root's minus those committed on the path
+//      (a walk over LDS), the transition is the masked position with the
+//      highest confidence, lowest position on ties, with the verifier's token;
+//   3. one thread per node accepts it when every node on its path matches its
+//      parent's transition, and counts its depth;
+//   4. the deepest accepted node (lowest index on ties), its path and the
+//      target's transition there form the commit list, which can be applied
+//      to the block's tokens and mask.
+// An accepted path commits distinct masked positions, so a node deeper than
+// block_len cannot be accepted: every walk stops after block_len + 1 steps.
+// Device data that breaks the layout (a parent not below its node, a position
+// outside the block) makes that node unacceptable, never an access outside
+// the arrays.
+#include <climits>
+
+#include "dv_internal.h"
+
+namespace dv {
+namespace {
+
+constexpr int kTreeThreads = 256;
+constexpr int kPosPerLane = kMaxTreeBlockLen / 64;
+
+struct TreeLds {
+  int32_t parent[kMaxTreeNodes];
+  int32_t pos[kMaxTreeNodes];
+  int32_t tok[kMaxTreeNodes];
+  int32_t tpos[kMaxTreeNodes];   // transition of each node's state (-1: none or not needed)
+  int32_t ttok[kMaxTreeNodes];
+  int32_t depth[kMaxTreeNodes];  // accepted depth, -1 when not accepted
+  int32_t commit_pos[kMaxTreeBlockLen + 1];
+  int32_t commit_tok[kMaxTreeBlockLen + 1];
+  unsigned long long best_key[kTreeThreads / 64];
+  int32_t ncommit;
+};
+
+// Parent of node i, or -1 when the layout is broken (parent not in [0, i)).
+__device__ __forceinline__ int32_t parent_of(const TreeLds &s, int32_t i) {
+  const int32_t q = s.parent[i];
+  return (q >= 0 && q < i) ? q : -1;
+}
+
+__global__ __launch_bounds__(kTreeThreads) void tree_accept_kernel(TreeLaunch p) {
+  __shared__ TreeLds s;
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t n = static_cast<int32_t>(p.nodes), L = static_cast<int32_t>(p.block_len);
+  const int64_t nb = t * p.nodes;  // node base of this tree
+  for (int32_t i = tid; i < n; i += kTreeThreads) {
+    s.parent[i] = i == 0 ? -1 : p.parent[nb + i];
+    s.pos[i] = p.node_pos[nb + i];
+    s.tok[i] = p.node_tok[nb + i];
+    s.tpos[i] = -1;
+    s.ttok[i] = -1;
+  }
+  __syncthreads();
+
+  // 2. transitions, one wave per node; lane l holds positions l, l + 64, ...
+  const uint8_t *root_masked = p.root_masked + t * p.block_len;
+  uint32_t root_bits = 0;
+#pragma unroll
+  for (int k = 0; k < kPosPerLane; ++k) {
+    const int32_t q = lane + 64 * k;
+    if (q < L && root_masked[q]) root_bits |= 1u << k;
+  }
+  for (int32_t i = wave; i < n; i += kTreeThreads / 64) {
+    uint32_t bits = root_bits;
+    int32_t j = i, steps = 0;
+    bool broken = false;
+    while (j > 0) {  // uniform across the wave
+      if (++steps > L) {  // deeper than any accepted node can be
+        broken = true;
+        break;
+      }
+      const int32_t q = s.pos[j];
+      if (q >= 0 && q < L && (q & 63) == lane) bits &= ~(1u << (q >> 6));
+      const int32_t up = parent_of(s, j);
+      if (up < 0) {
+        broken = true;
+        break;
+      }
+      j = up;
+    }
+    if (broken) continue;
+    const float *crow = p.conf + (nb + i) * p.block_len;
+    float best_c = -INFINITY;
+    int32_t best_q = INT_MAX;
+#pragma unroll
+    for (int k = 0; k < kPosPerLane; ++k) {
+      const int32_t q = lane + 64 * k;
+      if ((bits >> k) & 1u) {
+        const float c = crow[q];
+        if (c > best_c || best_q == INT_MAX) {  // positions rise with k: keep the first of equal values
+          best_c = c;
+          best_q = q;
+        }
+      }
+    }
+    // wave argmax: largest confidence, then lowest position
+    for (int o = 32; o > 0; o >>= 1) {
+      const float oc = __shfl_xor(best_c, o);
+      const int32_t oq = __shfl_xor(best_q, o);
+      if (oq != INT_MAX && (best_q == INT_MAX || oc > best_c || (oc == best_c && oq < best_q))) {
+        best_c = oc;
+        best_q = oq;
+      }
+    }
+    if (lane == 0 && best_q != INT_MAX) {
+      s.tpos[i] = best_q;
+      s.ttok[i] = p.tok_v[(nb + i) * p.block_len + best_q];
+    }
+  }
+  __syncthreads();
+
+  // 3. acceptance and depth, one thread per node: walk to the root while every
+  // node on the way matches its parent's transition
+  for (int32_t i = tid; i < n; i += kTreeThreads) {
+    int32_t j = i, d = 0;
+    bool ok = true;
+    while (j > 0) {
+      const int32_t up = parent_of(s, j);
+      if (up < 0 || d >= L || s.tpos[up] < 0 || s.pos[j] != s.tpos[up] || s.tok[j] != s.ttok[up]) {
+        ok = false;
+        break;
+      }
+      ++d;
+      j = up;
+    }
+    s.depth[i] = ok ? d : -1;
+  }
+  __syncthreads();
+
+  // 4. best node: deepest, lowest index (key = depth << 32 | ~index)
+  unsigned long long key = 0;
+  for (int32_t i = tid; i < n; i += kTreeThreads) {
+    const int32_t d = s.depth[i];
+    if (d >= 0) {
+      const unsigned long long k = (static_cast<unsigned long long>(d + 1) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(i));
+      key = k > key ? k : key;
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long other = __shfl_xor(key, o);
+    key = other > key ? other : key;
+  }
+  if (lane == 0) s.best_key[wave] = key;
+  __syncthreads();
+  if (tid == 0) {
+    unsigned long long k = s.best_key[0];
+    for (int w = 1; w < kTreeThreads / 64; ++w) k = s.best_key[w] > k ? s.best_key[w] : k;
+    const int32_t best = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(k & 0xFFFFFFFFull));  // the root at least
+    const int32_t d = s.depth[best];
+    int32_t j = best;
+    for (int32_t m = d - 1; m >= 0; --m) {  // the path, written from its end
+      s.commit_pos[m] = s.pos[j];
+      s.commit_tok[m] = s.tok[j];
+      j = s.parent[j];
+    }
+    int32_t c = d;
+    if (s.tpos[best] >= 0) {
+      s.commit_pos[c] = s.tpos[best];
+      s.commit_tok[c] = s.ttok[best];
+      ++c;
+    }
+    s.ncommit = c;
+    if (p.best_node) p.best_node[t] = best;
+    if (p.commit_len) p.commit_len[t] = c;
+  }
+  __syncthreads();
+  for (int32_t i = tid; i < n; i += kTreeThreads) {
+    if (p.accepted) p.accepted[nb + i] = s.depth[i] >= 0 ? 1 : 0;
+    if (p.depth) p.depth[nb + i] = s.depth[i];
+  }
+  const int32_t nc = s.ncommit;
+  for (int32_t m = tid; m < L; m += kTreeThreads) {
+    if (p.commit_pos) p.commit_pos[t * p.block_len + m] = m < nc ? s.commit_pos[m] : -1;
+    if (p.commit_tok) p.commit_tok[t * p.block_len + m] = m < nc ? s.commit_tok[m] : -1;
+  }
+  // apply the commits (committed positions are distinct); out_masked may alias
+  // root_masked: every read of it happened before the barriers above
+  for (int32_t m = tid; m < nc; m += kTreeThreads) {
+    const int32_t q = s.commit_pos[m];
+    if (p.block_tokens) p.block_tokens[t * p.block_len + q] = s.commit_tok[m];
+  }
+  if (p.out_masked) {
+    for (int32_t q = tid; q < L; q += kTreeThreads) {
+      bool m = root_masked[q] != 0;
+      for (int32_t c = 0; c < nc && m; ++c) m = s.commit_pos[c] != q;
+      p.out_masked[t * p.block_len + q] = m ? 1 : 0;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_tree_accept(const TreeLaunch &p, hipStream_t stream) {
+  if (p.ntrees == 0) return hipSuccess;
+  hipLaunchKernelGGL(tree_accept_kernel, dim3(static_cast<unsigned>(p.ntrees)), dim3(kTreeThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace dv

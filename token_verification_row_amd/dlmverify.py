@@ -57,6 +57,10 @@ class dv_decide_args(ctypes.Structure):
                 ("mask_token", ctypes.c_int32), ("rows", ctypes.c_int64), ("group_len", ctypes.c_int64)]
 
 
+class dv_tree_args(ctypes.Structure):
+    _fields_ = [("ntrees", ctypes.c_int64), ("nodes", ctypes.c_int64), ("block_len", ctypes.c_int64)]
+
+
 _P = ctypes.c_void_p
 _SIGNATURES = {
     "dv_verify_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(dv_logits), ctypes.POINTER(dv_noise),
@@ -69,6 +73,7 @@ _SIGNATURES = {
     "dv_seed_score": (ctypes.c_int, [ctypes.c_int64, _P, _P, _P, _P, _P, _P]),
     "dv_select_topk": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_int32, ctypes.c_float, _P, _P, _P, _P, _P]),
+    "dv_tree_accept": (ctypes.c_int, [ctypes.POINTER(dv_tree_args)] + [_P] * 15),
     "dv_debug_hash": (ctypes.c_int, [ctypes.c_uint64, _P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P]),
     "dv_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "dv_last_error": (ctypes.c_char_p, []),
@@ -282,6 +287,51 @@ def dv_select_topk(score, k, *, eligible=None, largest=True, use_thr=False, thr=
                                          int(bool(use_thr)), float(thr), _ptr(idx), _ptr(val), _ptr(cnt),
                                          _ptr(mask), _stream_handle(dev)), "dv_select_topk")
     return idx, val, cnt[:nseq], mask
+
+
+def dv_tree_accept(parent, node_pos, node_tok, root_masked, conf, tok_v, *, block_tokens=None, update_mask=False):
+    """Acceptance over trees of candidate block states (see dlmverify.h).
+
+    parent, node_pos, node_tok: int32 [ntrees, nodes]; root_masked: uint8
+    [ntrees, block_len]; conf (float32) and tok_v (int32): [ntrees, nodes,
+    block_len] or the flat per-row statistics of those rows. block_tokens
+    (int32 [ntrees, block_len]) is updated in place when given; with
+    update_mask the committed positions of root_masked are cleared in place.
+    Returns a dict: accepted, depth, best_node, commit_pos, commit_tok,
+    commit_len.
+    """
+    for name, t, dt in (("parent", parent, torch.int32), ("node_pos", node_pos, torch.int32),
+                        ("node_tok", node_tok, torch.int32), ("root_masked", root_masked, torch.uint8),
+                        ("conf", conf, torch.float32), ("tok_v", tok_v, torch.int32)):
+        _need_cuda(t, name)
+        if t.dtype != dt or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous {dt} tensor")
+    if parent.dim() != 2 or root_masked.dim() != 2:
+        raise ValueError("parent must be [ntrees, nodes] and root_masked [ntrees, block_len]")
+    ntrees, nodes = parent.shape
+    L = root_masked.shape[1]
+    if node_pos.shape != parent.shape or node_tok.shape != parent.shape or root_masked.shape[0] != ntrees:
+        raise ValueError("node arrays and root_masked must agree on ntrees and nodes")
+    if conf.numel() != ntrees * nodes * L or tok_v.numel() != ntrees * nodes * L:
+        raise ValueError("conf and tok_v must hold ntrees * nodes * block_len entries")
+    if block_tokens is not None:
+        _need_cuda(block_tokens, "block_tokens")
+        if block_tokens.dtype != torch.int32 or tuple(block_tokens.shape) != (ntrees, L) or not block_tokens.is_contiguous():
+            raise TypeError("block_tokens must be a contiguous int32 [ntrees, block_len] tensor")
+    dev = parent.device
+    out = dict(accepted=torch.empty((ntrees, nodes), dtype=torch.uint8, device=dev),
+               depth=torch.empty((ntrees, nodes), dtype=torch.int32, device=dev),
+               best_node=torch.empty(ntrees, dtype=torch.int32, device=dev),
+               commit_pos=torch.empty((ntrees, L), dtype=torch.int32, device=dev),
+               commit_tok=torch.empty((ntrees, L), dtype=torch.int32, device=dev),
+               commit_len=torch.empty(ntrees, dtype=torch.int32, device=dev))
+    args = dv_tree_args(ntrees=ntrees, nodes=nodes, block_len=L)
+    _check(load_library().dv_tree_accept(
+        ctypes.byref(args), _ptr(parent), _ptr(node_pos), _ptr(node_tok), _ptr(root_masked), _ptr(conf), _ptr(tok_v),
+        _ptr(out["accepted"]), _ptr(out["depth"]), _ptr(out["best_node"]), _ptr(out["commit_pos"]),
+        _ptr(out["commit_tok"]), _ptr(out["commit_len"]), _ptr(block_tokens),
+        _ptr(root_masked) if update_mask else None, _stream_handle(dev)), "dv_tree_accept")
+    return out
 
 
 def dv_debug_hash(seed, rows, vocab, *, pos=None, pos_period=0, device="cuda"):

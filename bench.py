@@ -68,6 +68,38 @@ def _oracle_block(args):
     return len(a)
 
 
+def synthetic_tree(stats, nodes, block_len, dev):
+    """A tree over the candidate block states (one per group of rows) whose nodes mostly
+    follow the target's transition from their parent, read from a first verify pass
+    (set up outside the timed region). Returns the dv_tree_accept inputs before conf/tok_v."""
+    import numpy as np
+    import torch
+
+    conf = stats["conf"].cpu().numpy().reshape(nodes, block_len)
+    tok = stats["tok_v"].cpu().numpy().reshape(nodes, block_len)
+    rng = np.random.default_rng(3)
+    parent = np.zeros(nodes, np.int32)
+    parent[0] = -1
+    pos = np.zeros(nodes, np.int32)
+    tk = np.zeros(nodes, np.int32)
+    masked = [np.ones(block_len, bool)]
+    for i in range(1, nodes):
+        q = int(rng.integers(max(0, i - 4), i))
+        parent[i] = q
+        cand = np.flatnonzero(masked[q])
+        if cand.size and rng.random() < 0.85:
+            p = int(cand[np.argmax(conf[q][cand])])     # the transition of the parent's state
+            pos[i], tk[i] = p, tok[q][p]
+        else:
+            pos[i], tk[i] = int(rng.integers(0, block_len)), int(rng.integers(0, 1 << 17))
+        m = masked[q].copy()
+        m[pos[i]] = False
+        masked.append(m)
+    t = lambda x, dt: torch.from_numpy(np.ascontiguousarray(x[None]).astype(dt)).to(dev)
+    return (t(parent, np.int32), t(pos, np.int32), t(tk, np.int32),
+            torch.ones((1, block_len), dtype=torch.uint8, device=dev))
+
+
 def cpu_baseline(a_rows, b_rows, w, pos, workers):
     """Time the oracle (as it is) on the given rows across ``workers`` processes."""
     import multiprocessing as mp
@@ -92,6 +124,9 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=4, choices=[2, 3, 4, 5])
     ap.add_argument("--cpu-rows", type=int, default=1024, help="rows of the workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tree", action="store_true",
+                    help="workload 4 only: accept over a tree of the 64 candidate block states (dv_tree_accept) "
+                         "instead of a prefix per candidate")
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated between steps (0: auto)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the path, run a plain device copy of MIB MiB --steps times (reference for "
@@ -141,6 +176,12 @@ def main() -> int:
     nseq = R // seq_len
     k = min(w.topk or 8, seq_len)
     stream = torch.cuda.current_stream(dev)
+    tree = None
+    if args.tree:
+        if not w.group_len:
+            print("--tree needs a workload of candidate block states (workload 4)", file=sys.stderr)
+            return 2
+        tree = synthetic_tree(outs[0], nseq, seq_len, dev)
 
     def step(i, ev=None):
         """verify -> decide -> seed score -> select, with the workload's own rule and selection score."""
@@ -159,7 +200,9 @@ def main() -> int:
                                               want_mask=True)
             dv.dv_decide("COVER", got, conf_thr=w.conf_thr, mask_token=-1, subject=mask.view(-1))
             return
-        if w.group_len:
+        if tree is not None:
+            dv.dv_tree_accept(*tree, got["conf"], got["tok_v"])
+        elif w.group_len:
             dv.dv_decide("COUPLED_ACCEPT", got, mask_token=-1, group_len=w.group_len, want_prefix=True,
                          want_best=True)
         else:
@@ -218,7 +261,8 @@ def main() -> int:
                                + (f", noise shared per position (period {period}), coupled acceptance per "
                                   f"{w.group_len}-row candidate" if period else ""),
                    "rows": R, "vocab": V, "input_copies": copies,
-                   "step": "dv_verify_rows + dv_seed_score + dv_select_topk + dv_decide"},
+                   "step": "dv_verify_rows + dv_seed_score + dv_select_topk + "
+                           + ("dv_tree_accept" if tree is not None else "dv_decide")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(w.number),
                      "kernel": "dv_verify_rows (noise table when rows share positions + streaming verify kernel)",

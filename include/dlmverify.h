@@ -215,7 +215,7 @@ dv_status dv_select_topk(int64_t nseq, int64_t seq_len, const float *score, cons
  * each over blocks of `block_len` positions. */
 typedef struct dv_tree_args {
   int64_t ntrees;     /* >= 0 */
-  int64_t nodes;      /* 1..2048 per tree; node 0 is the root */
+  int64_t nodes;      /* 1..1024 per tree; node 0 is the root */
   int64_t block_len;  /* 1..1024 positions per block state */
 } dv_tree_args;
 
@@ -233,7 +233,7 @@ typedef struct dv_tree_args {
  *   conf, tok_v float32 / int32 [ntrees][nodes][block_len]: the verifier's
  *               confidence and shared-noise token of every position of every
  *               node's state (the dv_row_stats of those rows, row index
- *               (tree * nodes + node) * block_len + position)
+ *               (tree * nodes + node) * block_len + position); conf not NaN
  * The target's transition from a state commits its masked position (the
  * root's masked positions minus those committed on the path) of highest conf,
  * lowest position on ties, with that position's tok_v. A node is accepted

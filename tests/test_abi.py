@@ -187,7 +187,7 @@ def test_tree_validation(lib):
     assert _tree(lib, args=False) == B.DV_ERR_NULL
     assert _tree(lib, ntrees=-1) == B.DV_ERR_SHAPE
     assert _tree(lib, nodes=0) == B.DV_ERR_SHAPE
-    assert _tree(lib, nodes=2049) == B.DV_ERR_SHAPE
+    assert _tree(lib, nodes=1025) == B.DV_ERR_SHAPE
     assert _tree(lib, block_len=0) == B.DV_ERR_SHAPE
     assert _tree(lib, block_len=1025) == B.DV_ERR_SHAPE
     assert _tree(lib, inputs=None) == B.DV_ERR_NULL

@@ -104,7 +104,7 @@ def test_hand_example():
 
 
 @pytest.mark.parametrize("n,L,vocab,p_follow", [(1, 1, 1, 0.0), (1, 7, 3, 0.0), (5, 3, 2, 0.9), (64, 32, 4, 0.8),
-                                                (200, 16, 2, 0.6), (300, 100, 3, 0.95), (2048, 64, 2, 0.9)])
+                                                (200, 16, 2, 0.6), (300, 100, 3, 0.95), (1024, 64, 2, 0.9), (1024, 65, 2, 0.9)])
 def test_random_trees(n, L, vocab, p_follow):
     print(f"case: random trees n={n} L={L}", flush=True)
     rng = np.random.default_rng(n * 131 + L)
@@ -119,8 +119,10 @@ def test_maximum_sizes_and_deep_chains():
     rng = np.random.default_rng(5)
     dev = _dev()
     # the largest tree over the largest block; and chains deeper than the block
-    _run_batch([_random_tree(rng, 2048, 1024, 3, 0.97)], dev)
-    _run_batch([_random_tree(rng, 2048, 8, 2, 0.9, deep=True) for _ in range(4)], dev)
+    _run_batch([_random_tree(rng, 1024, 1024, 3, 0.97)], dev)
+    _run_batch([_random_tree(rng, 1024, 8, 2, 0.9, deep=True) for _ in range(4)], dev)
+    _run_batch([_random_tree(rng, 1024, 64, 2, 0.99, deep=True) for _ in range(2)], dev)
+    _run_batch([_random_tree(rng, 1024, 200, 2, 0.99, deep=True)], dev)
     _run_batch([_random_tree(rng, 600, 1, 1, 1.0, deep=True)], dev, with_block=False)
 
 

@@ -104,7 +104,7 @@ struct SelectLaunch {
 constexpr int64_t kMaxSelectLen = 16384;
 hipError_t launch_select_topk(const SelectLaunch &p, hipStream_t stream);
 
-constexpr int kMaxTreeNodes = 2048;
+constexpr int kMaxTreeNodes = 1024;
 constexpr int kMaxTreeBlockLen = 1024;
 struct TreeLaunch {
   int64_t ntrees, nodes, block_len;

@@ -6,10 +6,11 @@
 //
 // One workgroup per tree:
 //   1. the node arrays go to LDS;
-//   2. one wave per node finds the target's transition from the node's state:
-//      the masked positions are the root's minus those committed on the path
-//      (a walk over LDS), the transition is the masked position with the
-//      highest confidence, lowest position on ties, with the verifier's token;
+//   2. the target's transition from each node's state: the masked positions
+//      are the root's minus those committed on the path (a walk over LDS), the
+//      transition is the masked position with the highest confidence, lowest
+//      position on ties, with the verifier's token (one thread per (node,
+//      position) for blocks of up to 64 positions, else one wave per node);
 //   3. one thread per node accepts it when every node on its path matches its
 //      parent's transition, and counts its depth;
 //   4. the deepest accepted node (lowest index on ties), its path and the
@@ -27,19 +28,22 @@
 namespace dv {
 namespace {
 
-constexpr int kTreeThreads = 256;
+constexpr int kTreeThreads = 1024;
+constexpr int kTreeWaves = kTreeThreads / 64;
 constexpr int kPosPerLane = kMaxTreeBlockLen / 64;
 
 struct TreeLds {
   int32_t parent[kMaxTreeNodes];
   int32_t pos[kMaxTreeNodes];
   int32_t tok[kMaxTreeNodes];
-  int32_t tpos[kMaxTreeNodes];   // transition of each node's state (-1: none or not needed)
-  int32_t ttok[kMaxTreeNodes];
-  int32_t depth[kMaxTreeNodes];  // accepted depth, -1 when not accepted
+  int32_t ttok[kMaxTreeNodes];         // transition token of each node's state
+  int16_t tpos[kMaxTreeNodes];         // transition position (-1: none, or not needed)
+  int16_t depth[kMaxTreeNodes];        // accepted depth, -1 when not accepted
+  unsigned long long pmask[kMaxTreeNodes];  // blocks of <= 64 positions: positions committed on the path
+  unsigned long long tkey[kMaxTreeNodes];   // blocks of <= 64 positions: best (confidence, position) key
   int32_t commit_pos[kMaxTreeBlockLen + 1];
   int32_t commit_tok[kMaxTreeBlockLen + 1];
-  unsigned long long best_key[kTreeThreads / 64];
+  unsigned long long best_key[kTreeWaves];
   int32_t ncommit;
 };
 
@@ -49,12 +53,124 @@ __device__ __forceinline__ int32_t parent_of(const TreeLds &s, int32_t i) {
   return (q >= 0 && q < i) ? q : -1;
 }
 
+// Order-preserving unsigned image of a float (larger float, larger image).
+__device__ __forceinline__ uint32_t float_order(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Blocks of up to 64 positions. Each thread walks one node's path (at most
+// block_len steps: a longer path cannot be accepted and gets no transition)
+// into a 64-bit mask of committed positions; then one thread per (node,
+// position) offers its masked position to the node's transition with an LDS
+// atomic max on (confidence, lowest position), and the winner records its
+// token. Every load of confidence and token is independent of the others.
+__device__ void transitions_small(TreeLds &s, const TreeLaunch &p, int64_t nb, const uint8_t *root_masked,
+                                  int32_t n, int32_t L) {
+  const int tid = threadIdx.x;
+  for (int32_t i = tid; i < n; i += kTreeThreads) {
+    unsigned long long m = 0;
+    int32_t j = i, steps = 0;
+    bool ok = true;
+    while (j > 0) {
+      const int32_t q = s.pos[j];
+      const int32_t up = parent_of(s, j);
+      if (++steps > L || up < 0) {
+        ok = false;
+        break;
+      }
+      if (q >= 0 && q < L) m |= 1ull << q;
+      j = up;
+    }
+    s.pmask[i] = ok ? m : ~0ull;  // all positions taken: no transition
+    s.tkey[i] = 0;
+  }
+  __syncthreads();
+  const int64_t total = static_cast<int64_t>(n) * L;
+  for (int64_t e = tid; e < total; e += kTreeThreads) {
+    const int32_t i = static_cast<int32_t>(e / L), q = static_cast<int32_t>(e - static_cast<int64_t>(i) * L);
+    if (!root_masked[q] || ((s.pmask[i] >> q) & 1ull)) continue;
+    const float c = p.conf[nb * L + e];
+    const unsigned long long key = (static_cast<unsigned long long>(float_order(c)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(q));
+    atomicMax(&s.tkey[i], key);
+  }
+  __syncthreads();
+  for (int64_t e = tid; e < total; e += kTreeThreads) {
+    const int32_t i = static_cast<int32_t>(e / L), q = static_cast<int32_t>(e - static_cast<int64_t>(i) * L);
+    const unsigned long long k = s.tkey[i];
+    if (k != 0 && static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(k & 0xFFFFFFFFull)) == q) {
+      s.tpos[i] = static_cast<int16_t>(q);
+      s.ttok[i] = p.tok_v[nb * L + e];
+    }
+  }
+}
+
+// Longer blocks: one wave per node; lane l holds positions l, l + 64, ...
+__device__ void transitions_wide(TreeLds &s, const TreeLaunch &p, int64_t nb, const uint8_t *root_masked,
+                                 int32_t n, int32_t L) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t root_bits = 0;
+#pragma unroll
+  for (int k = 0; k < kPosPerLane; ++k) {
+    const int32_t q = lane + 64 * k;
+    if (q < L && root_masked[q]) root_bits |= 1u << k;
+  }
+  for (int32_t i = wave; i < n; i += kTreeWaves) {
+    uint32_t bits = root_bits;
+    int32_t j = i, steps = 0;
+    bool broken = false;
+    while (j > 0) {  // uniform across the wave
+      const int32_t up = parent_of(s, j);
+      if (++steps > L || up < 0) {
+        broken = true;
+        break;
+      }
+      const int32_t q = s.pos[j];
+      if (q >= 0 && q < L && (q & 63) == lane) bits &= ~(1u << (q >> 6));
+      j = up;
+    }
+    if (broken) continue;
+    const float *crow = p.conf + (nb + i) * p.block_len;
+    const int32_t *trow = p.tok_v + (nb + i) * p.block_len;
+    float best_c = -INFINITY;
+    int32_t best_q = INT_MAX, best_t = -1;
+#pragma unroll
+    for (int k = 0; k < kPosPerLane; ++k) {
+      const int32_t q = lane + 64 * k;
+      if ((bits >> k) & 1u) {
+        const float c = crow[q];
+        if (best_q == INT_MAX || c > best_c) {  // positions rise with k: keep the first of equal values
+          best_c = c;
+          best_q = q;
+          best_t = trow[q];
+        }
+      }
+    }
+    // wave argmax: largest confidence, then lowest position
+    for (int o = 32; o > 0; o >>= 1) {
+      const float oc = __shfl_xor(best_c, o);
+      const int32_t oq = __shfl_xor(best_q, o);
+      const int32_t ot = __shfl_xor(best_t, o);
+      if (oq != INT_MAX && (best_q == INT_MAX || oc > best_c || (oc == best_c && oq < best_q))) {
+        best_c = oc;
+        best_q = oq;
+        best_t = ot;
+      }
+    }
+    if (lane == 0 && best_q != INT_MAX) {
+      s.tpos[i] = static_cast<int16_t>(best_q);
+      s.ttok[i] = best_t;
+    }
+  }
+}
+
 __global__ __launch_bounds__(kTreeThreads) void tree_accept_kernel(TreeLaunch p) {
   __shared__ TreeLds s;
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t n = static_cast<int32_t>(p.nodes), L = static_cast<int32_t>(p.block_len);
   const int64_t nb = t * p.nodes;  // node base of this tree
+  const uint8_t *root_masked = p.root_masked + t * p.block_len;
   for (int32_t i = tid; i < n; i += kTreeThreads) {
     s.parent[i] = i == 0 ? -1 : p.parent[nb + i];
     s.pos[i] = p.node_pos[nb + i];
@@ -64,60 +180,11 @@ __global__ __launch_bounds__(kTreeThreads) void tree_accept_kernel(TreeLaunch p)
   }
   __syncthreads();
 
-  // 2. transitions, one wave per node; lane l holds positions l, l + 64, ...
-  const uint8_t *root_masked = p.root_masked + t * p.block_len;
-  uint32_t root_bits = 0;
-#pragma unroll
-  for (int k = 0; k < kPosPerLane; ++k) {
-    const int32_t q = lane + 64 * k;
-    if (q < L && root_masked[q]) root_bits |= 1u << k;
-  }
-  for (int32_t i = wave; i < n; i += kTreeThreads / 64) {
-    uint32_t bits = root_bits;
-    int32_t j = i, steps = 0;
-    bool broken = false;
-    while (j > 0) {  // uniform across the wave
-      if (++steps > L) {  // deeper than any accepted node can be
-        broken = true;
-        break;
-      }
-      const int32_t q = s.pos[j];
-      if (q >= 0 && q < L && (q & 63) == lane) bits &= ~(1u << (q >> 6));
-      const int32_t up = parent_of(s, j);
-      if (up < 0) {
-        broken = true;
-        break;
-      }
-      j = up;
-    }
-    if (broken) continue;
-    const float *crow = p.conf + (nb + i) * p.block_len;
-    float best_c = -INFINITY;
-    int32_t best_q = INT_MAX;
-#pragma unroll
-    for (int k = 0; k < kPosPerLane; ++k) {
-      const int32_t q = lane + 64 * k;
-      if ((bits >> k) & 1u) {
-        const float c = crow[q];
-        if (c > best_c || best_q == INT_MAX) {  // positions rise with k: keep the first of equal values
-          best_c = c;
-          best_q = q;
-        }
-      }
-    }
-    // wave argmax: largest confidence, then lowest position
-    for (int o = 32; o > 0; o >>= 1) {
-      const float oc = __shfl_xor(best_c, o);
-      const int32_t oq = __shfl_xor(best_q, o);
-      if (oq != INT_MAX && (best_q == INT_MAX || oc > best_c || (oc == best_c && oq < best_q))) {
-        best_c = oc;
-        best_q = oq;
-      }
-    }
-    if (lane == 0 && best_q != INT_MAX) {
-      s.tpos[i] = best_q;
-      s.ttok[i] = p.tok_v[(nb + i) * p.block_len + best_q];
-    }
+  // 2. the target's transition from every node's state that could be accepted
+  if (L <= 64) {
+    transitions_small(s, p, nb, root_masked, n, L);
+  } else {
+    transitions_wide(s, p, nb, root_masked, n, L);
   }
   __syncthreads();
 
@@ -135,11 +202,11 @@ __global__ __launch_bounds__(kTreeThreads) void tree_accept_kernel(TreeLaunch p)
       ++d;
       j = up;
     }
-    s.depth[i] = ok ? d : -1;
+    s.depth[i] = static_cast<int16_t>(ok ? d : -1);
   }
   __syncthreads();
 
-  // 4. best node: deepest, lowest index (key = depth << 32 | ~index)
+  // 4. best node: deepest, lowest index (key = (depth + 1) << 32 | ~index)
   unsigned long long key = 0;
   for (int32_t i = tid; i < n; i += kTreeThreads) {
     const int32_t d = s.depth[i];
@@ -156,7 +223,7 @@ __global__ __launch_bounds__(kTreeThreads) void tree_accept_kernel(TreeLaunch p)
   __syncthreads();
   if (tid == 0) {
     unsigned long long k = s.best_key[0];
-    for (int w = 1; w < kTreeThreads / 64; ++w) k = s.best_key[w] > k ? s.best_key[w] : k;
+    for (int w = 1; w < kTreeWaves; ++w) k = s.best_key[w] > k ? s.best_key[w] : k;
     const int32_t best = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(k & 0xFFFFFFFFull));  // the root at least
     const int32_t d = s.depth[best];
     int32_t j = best;
@@ -186,7 +253,8 @@ __global__ __launch_bounds__(kTreeThreads) void tree_accept_kernel(TreeLaunch p)
     if (p.commit_tok) p.commit_tok[t * p.block_len + m] = m < nc ? s.commit_tok[m] : -1;
   }
   // apply the commits (committed positions are distinct); out_masked may alias
-  // root_masked: every read of it happened before the barriers above
+  // root_masked: every read of it happened before the barriers above, or is
+  // the read of the same element by the thread that writes it
   for (int32_t m = tid; m < nc; m += kTreeThreads) {
     const int32_t q = s.commit_pos[m];
     if (p.block_tokens) p.block_tokens[t * p.block_len + q] = s.commit_tok[m];

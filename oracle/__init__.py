@@ -31,12 +31,14 @@ Modules:
   selection.
 * ``tree``      acceptance over a tree of candidate block states and the
   commit list it yields.
+* ``attention`` COVER's influence d_in and drift sensitivity d_out from
+  attention probabilities.
 
 Every function is pinned by tests under ``tests/`` against closed forms,
 library routines, invariants or brute force; none of the pages prints a
 worked example, so no end-to-end value is pinned by the pages themselves.
 """
 
-from . import rowstats, noise, decide, select, tree  # noqa: F401
+from . import rowstats, noise, decide, select, tree, attention  # noqa: F401
 
-__all__ = ["rowstats", "noise", "decide", "select", "tree"]
+__all__ = ["rowstats", "noise", "decide", "select", "tree", "attention"]

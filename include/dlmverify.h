@@ -257,6 +257,39 @@ dv_status dv_tree_accept(const dv_tree_args *args, const int32_t *parent, const 
                          int32_t *commit_pos, int32_t *commit_tok, int32_t *commit_len,
                          int32_t *block_tokens, uint8_t *out_masked, hipStream_t stream);
 
+/* Attention probabilities of nseq sequences: `heads` maps of [len][len] each,
+ * row-major [nseq][heads][len][ld] of `dtype` (rows sum to one; row i holds the
+ * attention of query i over the keys). Requirements as for dv_logits: 16-byte
+ * aligned base, ld*elt a multiple of 16, len <= ld. */
+typedef struct dv_attention {
+  const void *probs;
+  int32_t dtype;     /* dv_dtype */
+  int32_t reserved;
+  int64_t nseq;      /* 0..65535 */
+  int64_t heads;     /* 1..65535: heads (of one or several layers) averaged with equal weight */
+  int64_t len;       /* 1..4096 positions */
+  int64_t ld;
+} dv_attention;
+
+/* Bytes of device workspace dv_influence_drift needs (never 0 for nseq > 0). */
+dv_status dv_influence_drift_workspace_bytes(const dv_attention *att, size_t *bytes);
+
+/* COVER's influence and drift sensitivity of every position ([COVER] "Method:
+ * COVER" part 2, Stability-Aware Seed Selection: d_in measures how much the
+ * positions that are still masked rely on a token as context, d_out how
+ * strongly the token attends to the newly written positions):
+ *   d_in[b][j]  = (1/heads) sum_h sum_{i: query_masked[b][i]} A[b][h][i][j]
+ *   d_out[b][i] = (1/heads) sum_h sum_{k: new_cols[b][k]}     A[b][h][i][k]
+ * query_masked, new_cols: device uint8 [nseq][len] (nonzero = set); d_in,
+ * d_out: device float32 [nseq][len] (either may be NULL). The result does not
+ * depend on scheduling (fixed summation order). `workspace` (device, 256-byte
+ * aligned) holds dv_influence_drift_workspace_bytes() bytes.
+ * Errors: DV_ERR_NULL, DV_ERR_SHAPE, DV_ERR_DTYPE, DV_ERR_ALIGN,
+ * DV_ERR_WORKSPACE, DV_ERR_HIP. */
+dv_status dv_influence_drift(const dv_attention *att, const uint8_t *query_masked, const uint8_t *new_cols,
+                             float *d_in, float *d_out, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
 /* The noise hash words h[r][i] (uint32, device [rows][vocab]) for the
  * positions described as in dv_noise. For testing the noise generator bit
  * for bit. Errors: DV_ERR_NULL, DV_ERR_SHAPE. */

@@ -30,8 +30,8 @@ def _declared_functions():
 def test_exports_every_declared_function(lib):
     names = _declared_functions()
     assert names == sorted(["dv_verify_workspace_bytes", "dv_verify_rows", "dv_decide", "dv_seed_score",
-                           "dv_select_topk", "dv_tree_accept", "dv_debug_hash", "dv_status_str", "dv_last_error",
-                           "dv_version"])
+                           "dv_select_topk", "dv_tree_accept", "dv_influence_drift_workspace_bytes",
+                           "dv_influence_drift", "dv_debug_hash", "dv_status_str", "dv_last_error", "dv_version"])
     for n in names:
         assert hasattr(lib, n), n
     assert lib.dv_version() == 1
@@ -192,3 +192,35 @@ def test_tree_validation(lib):
     assert _tree(lib, block_len=1025) == B.DV_ERR_SHAPE
     assert _tree(lib, inputs=None) == B.DV_ERR_NULL
     assert _tree(lib, ntrees=0, inputs=None) == B.DV_OK        # nothing to do: no launch
+
+
+def _att(nseq=1, heads=2, length=512, ld=None, dtype=B.DV_BF16, probs=FAKE):
+    return B.dv_attention(probs=probs, dtype=dtype, reserved=0, nseq=nseq, heads=heads, len=length,
+                          ld=length if ld is None else ld)
+
+
+def test_influence_validation_and_workspace(lib):
+    out = ctypes.c_size_t(0)
+    a = _att(nseq=1, heads=784, length=512)
+    assert lib.dv_influence_drift_workspace_bytes(ctypes.byref(a), ctypes.byref(out)) == B.DV_OK
+    # 784 maps: 2 row tiles of 256 rows each -> column partials 784*2*512 floats, row partials 784*512 floats
+    assert out.value == 784 * 2 * 512 * 4 + 784 * 512 * 4
+    a = _att(nseq=1, heads=1, length=100, ld=104)
+    assert lib.dv_influence_drift_workspace_bytes(ctypes.byref(a), ctypes.byref(out)) == B.DV_OK
+    assert out.value == ((2 * 100 * 4 + 255) // 256) * 256 + 100 * 4      # 2 tiles of 56 rows
+    def call(att, qm=FAKE, nc=FAKE, ws=FAKE, ws_bytes=1 << 30):
+        return lib.dv_influence_drift(ctypes.byref(att) if att is not None else None, qm, nc, None, None, ws, ws_bytes,
+                                      None)
+    assert call(None) == B.DV_ERR_NULL
+    assert call(_att(dtype=9)) == B.DV_ERR_DTYPE
+    assert call(_att(heads=0)) == B.DV_ERR_SHAPE
+    assert call(_att(nseq=70000)) == B.DV_ERR_SHAPE
+    assert call(_att(length=4097)) == B.DV_ERR_SHAPE
+    assert call(_att(length=64, ld=32)) == B.DV_ERR_SHAPE
+    assert call(_att(length=60, ld=60)) == B.DV_ERR_ALIGN                  # 120-byte rows
+    assert call(_att(probs=FAKE + 4)) == B.DV_ERR_ALIGN
+    assert call(_att(), qm=None) == B.DV_ERR_NULL
+    assert call(_att(), ws=None) == B.DV_ERR_WORKSPACE
+    assert call(_att(), ws_bytes=16) == B.DV_ERR_WORKSPACE
+    assert call(_att(), ws=FAKE + 16) == B.DV_ERR_ALIGN
+    assert call(_att(nseq=0, probs=None), qm=None, nc=None, ws=None) == B.DV_OK   # nothing to do

@@ -118,6 +118,43 @@ dv_status choose_geometry(const dv_logits *x, const dv_noise *n, const dv_tuning
 
 bool finite(float v) { return std::isfinite(v); }
 
+dv_status influence_geometry(const dv_attention *a, bool need_ptrs, dv::InfluenceLaunch &p, size_t &ws) {
+  if (!a) return fail(DV_ERR_NULL, "attention descriptor is NULL");
+  if (a->dtype != DV_FP32 && a->dtype != DV_BF16) return fail(DV_ERR_DTYPE, "unknown dtype %d", a->dtype);
+  if (a->nseq < 0 || a->nseq > 65535) return fail(DV_ERR_SHAPE, "nseq must be 0..65535");
+  if (a->heads < 1 || a->heads > 65535) return fail(DV_ERR_SHAPE, "heads must be 1..65535");
+  if (a->len < 1 || a->len > dv::kMaxInfluenceLen) return fail(DV_ERR_SHAPE, "len must be 1..%d", dv::kMaxInfluenceLen);
+  if (a->ld < a->len) return fail(DV_ERR_SHAPE, "ld %lld < len %lld", (long long)a->ld, (long long)a->len);
+  const int64_t elt = a->dtype == DV_BF16 ? 2 : 4;
+  if (a->ld > (int64_t(1) << 30)) return fail(DV_ERR_SHAPE, "ld too large");
+  if ((a->ld * elt) % 16 != 0) return fail(DV_ERR_ALIGN, "row pitch ld*elt is not a multiple of 16 bytes");
+  if (need_ptrs && a->nseq > 0) {
+    if (!a->probs) return fail(DV_ERR_NULL, "probs is NULL");
+    if (!aligned16(a->probs)) return fail(DV_ERR_ALIGN, "probs must be 16-byte aligned");
+  }
+  // about 1024 workgroups: split each head's rows into tiles of a multiple of 8 rows
+  const int64_t maps = a->nseq * a->heads;
+  int64_t tiles = maps > 0 ? (1024 + maps - 1) / maps : 1;
+  const int64_t max_tiles = (a->len + 63) / 64;
+  if (tiles > max_tiles) tiles = max_tiles;
+  if (tiles < 1) tiles = 1;
+  int64_t tile_rows = (a->len + tiles - 1) / tiles;
+  tile_rows = (tile_rows + 7) / 8 * 8;
+  tiles = (a->len + tile_rows - 1) / tile_rows;
+  p.bf16 = a->dtype == DV_BF16;
+  p.tiles = static_cast<int32_t>(tiles);
+  p.tile_rows = static_cast<int32_t>(tile_rows);
+  p.nseq = a->nseq;
+  p.heads = a->heads;
+  p.len = a->len;
+  p.ld = a->ld;
+  p.probs = a->probs;
+  const size_t col_bytes = static_cast<size_t>(maps) * tiles * a->len * sizeof(float);
+  const size_t col_aligned = (col_bytes + 255) / 256 * 256;
+  ws = col_aligned + static_cast<size_t>(maps) * a->len * sizeof(float);
+  return DV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -269,6 +306,37 @@ dv_status dv_select_topk(int64_t nseq, int64_t seq_len, const float *score, cons
   p.out_count = out_count;
   p.out_mask = out_mask;
   return hip_status(dv::launch_select_topk(p, stream), "dv_select_topk launch");
+}
+
+dv_status dv_influence_drift_workspace_bytes(const dv_attention *att, size_t *bytes) {
+  if (!bytes) return fail(DV_ERR_NULL, "bytes is NULL");
+  dv::InfluenceLaunch p{};
+  size_t ws = 0;
+  dv_status s = influence_geometry(att, false, p, ws);
+  if (s != DV_OK) return s;
+  *bytes = ws;
+  return ok();
+}
+
+dv_status dv_influence_drift(const dv_attention *att, const uint8_t *query_masked, const uint8_t *new_cols,
+                             float *d_in, float *d_out, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  dv::InfluenceLaunch p{};
+  size_t ws = 0;
+  dv_status s = influence_geometry(att, true, p, ws);
+  if (s != DV_OK) return s;
+  if (att->nseq == 0) return ok();
+  if (!query_masked || !new_cols) return fail(DV_ERR_NULL, "query_masked or new_cols is NULL");
+  if (!workspace) return fail(DV_ERR_WORKSPACE, "workspace of %zu bytes required", ws);
+  if (workspace_bytes < ws) return fail(DV_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", ws, workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(DV_ERR_ALIGN, "workspace must be 256-byte aligned");
+  const size_t col_bytes = static_cast<size_t>(p.nseq * p.heads) * p.tiles * p.len * sizeof(float);
+  p.query_masked = query_masked;
+  p.new_cols = new_cols;
+  p.d_in = d_in;
+  p.d_out = d_out;
+  p.col_part = static_cast<float *>(workspace);
+  p.row_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + (col_bytes + 255) / 256 * 256);
+  return hip_status(dv::launch_influence(p, stream), "dv_influence_drift launch");
 }
 
 dv_status dv_tree_accept(const dv_tree_args *a, const int32_t *parent, const int32_t *node_pos,

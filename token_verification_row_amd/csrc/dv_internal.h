@@ -118,6 +118,19 @@ struct TreeLaunch {
 };
 hipError_t launch_tree_accept(const TreeLaunch &p, hipStream_t stream);
 
+constexpr int kMaxInfluenceLen = 4096;
+struct InfluenceLaunch {
+  const void *probs;  // [nseq][heads][len][ld]
+  int32_t bf16;
+  int32_t tiles, tile_rows;  // row tiles per head
+  int64_t nseq, heads, len, ld;
+  const uint8_t *query_masked, *new_cols;  // [nseq][len]
+  float *d_in, *d_out;                     // [nseq][len]
+  float *col_part;                         // workspace [nseq][heads][tiles][len]
+  float *row_part;                         // workspace [nseq][heads][len]
+};
+hipError_t launch_influence(const InfluenceLaunch &p, hipStream_t stream);
+
 hipError_t launch_debug_hash(uint32_t seed_b, const int32_t *pos, int64_t pos_period, int64_t rows,
                              int64_t vocab, uint32_t *out, hipStream_t stream);
 

@@ -57,6 +57,11 @@ class dv_decide_args(ctypes.Structure):
                 ("mask_token", ctypes.c_int32), ("rows", ctypes.c_int64), ("group_len", ctypes.c_int64)]
 
 
+class dv_attention(ctypes.Structure):
+    _fields_ = [("probs", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("nseq", ctypes.c_int64), ("heads", ctypes.c_int64), ("len", ctypes.c_int64), ("ld", ctypes.c_int64)]
+
+
 class dv_tree_args(ctypes.Structure):
     _fields_ = [("ntrees", ctypes.c_int64), ("nodes", ctypes.c_int64), ("block_len", ctypes.c_int64)]
 
@@ -74,6 +79,8 @@ _SIGNATURES = {
     "dv_select_topk": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_int32, ctypes.c_float, _P, _P, _P, _P, _P]),
     "dv_tree_accept": (ctypes.c_int, [ctypes.POINTER(dv_tree_args)] + [_P] * 15),
+    "dv_influence_drift_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(dv_attention), ctypes.POINTER(ctypes.c_size_t)]),
+    "dv_influence_drift": (ctypes.c_int, [ctypes.POINTER(dv_attention), _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "dv_debug_hash": (ctypes.c_int, [ctypes.c_uint64, _P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P]),
     "dv_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "dv_last_error": (ctypes.c_char_p, []),
@@ -332,6 +339,50 @@ def dv_tree_accept(parent, node_pos, node_tok, root_masked, conf, tok_v, *, bloc
         _ptr(out["commit_tok"]), _ptr(out["commit_len"]), _ptr(block_tokens),
         _ptr(root_masked) if update_mask else None, _stream_handle(dev)), "dv_tree_accept")
     return out
+
+
+def _attention_desc(probs):
+    _need_cuda(probs, "probs")
+    if probs.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("probs must be float32 or bfloat16")
+    if probs.dim() != 4 or probs.shape[2] != probs.shape[3]:
+        raise ValueError("probs must be [nseq, heads, len, len] (a view with a padded row pitch is fine)")
+    B, H, L, _ = probs.shape
+    if probs.stride(3) != 1 or probs.stride(1) != L * probs.stride(2) or probs.stride(0) != H * L * probs.stride(2):
+        raise ValueError("probs rows must be contiguous and the maps packed ([nseq][heads][len][ld])")
+    return dv_attention(probs=probs.data_ptr(), dtype=DV_BF16 if probs.dtype == torch.bfloat16 else DV_FP32,
+                        reserved=0, nseq=B, heads=H, len=L, ld=probs.stride(2))
+
+
+def dv_influence_drift_workspace_bytes(probs) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().dv_influence_drift_workspace_bytes(ctypes.byref(_attention_desc(probs)), ctypes.byref(n)),
+           "dv_influence_drift_workspace_bytes")
+    return n.value
+
+
+def dv_influence_drift(probs, query_masked, new_cols, *, workspace=None):
+    """COVER's d_in and d_out ([nseq, len] float32 each) from attention probabilities
+    [nseq, heads, len, len] and the masks query_masked, new_cols (uint8 [nseq, len])."""
+    att = _attention_desc(probs)
+    B, H, L, _ = probs.shape
+    for name, t in (("query_masked", query_masked), ("new_cols", new_cols)):
+        _need_cuda(t, name)
+        if t.dtype != torch.uint8 or tuple(t.shape) != (B, L) or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous uint8 [nseq, len] tensor")
+    dev = probs.device
+    d_in = torch.empty((B, L), dtype=torch.float32, device=dev)
+    d_out = torch.empty((B, L), dtype=torch.float32, device=dev)
+    need = dv_influence_drift_workspace_bytes(probs)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+    base = workspace.data_ptr()
+    ws_ptr = (base + 255) // 256 * 256
+    avail = workspace.numel() - (ws_ptr - base)
+    _check(load_library().dv_influence_drift(ctypes.byref(att), _ptr(query_masked), _ptr(new_cols), _ptr(d_in),
+                                             _ptr(d_out), ctypes.c_void_p(ws_ptr), avail, _stream_handle(dev)),
+           "dv_influence_drift")
+    return d_in, d_out
 
 
 def dv_debug_hash(seed, rows, vocab, *, pos=None, pos_period=0, device="cuda"):

@@ -100,6 +100,22 @@ def synthetic_tree(stats, nodes, block_len, dev):
             torch.ones((1, block_len), dtype=torch.uint8, device=dev))
 
 
+def synthetic_attention(maps, length, dev):
+    """(probs [1, maps, len, len] bf16, query_masked, new_cols): peaky softmax rows drawn on the device,
+    about 40% of the queries masked and 20% of the columns newly written."""
+    import torch
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(12345)
+    probs = torch.empty((1, maps, length, length), dtype=torch.bfloat16, device=dev)
+    for h in range(maps):
+        x = torch.randn((length, length), generator=g, device=dev, dtype=torch.float32) * 3.0
+        probs[0, h].copy_(torch.softmax(x, dim=-1).to(torch.bfloat16))
+    qm = (torch.rand((1, length), generator=g, device=dev) < 0.4).to(torch.uint8)
+    nc = (torch.rand((1, length), generator=g, device=dev) < 0.2).to(torch.uint8)
+    return probs, qm, nc
+
+
 def cpu_baseline(a_rows, b_rows, w, pos, workers):
     """Time the oracle (as it is) on the given rows across ``workers`` processes."""
     import multiprocessing as mp
@@ -124,6 +140,9 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=4, choices=[2, 3, 4, 5])
     ap.add_argument("--cpu-rows", type=int, default=1024, help="rows of the workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--influence", type=int, default=0, metavar="MAPS",
+                    help="workload 3 only: compute d_in and d_out in the step from MAPS synthetic bf16 attention "
+                         "maps of len x len (dv_influence_drift) and report that kernel's HBM rate")
     ap.add_argument("--tree", action="store_true",
                     help="workload 4 only: accept over a tree of the 64 candidate block states (dv_tree_accept) "
                          "instead of a prefix per candidate")
@@ -176,6 +195,14 @@ def main() -> int:
     nseq = R // seq_len
     k = min(w.topk or 8, seq_len)
     stream = torch.cuda.current_stream(dev)
+    att = None
+    if args.influence:
+        if not w.n_committed:
+            print("--influence needs the COVER workload (3)", file=sys.stderr)
+            return 2
+        att = synthetic_attention(args.influence, w.L, dev)
+        att_ws = torch.empty(dv.dv_influence_drift_workspace_bytes(att[0]) + 256, dtype=torch.uint8, device=dev)
+        att_ev = []
     tree = None
     if args.tree:
         if not w.group_len:
@@ -193,7 +220,17 @@ def main() -> int:
                                 workspace=out.get("_workspace"))
         if ev is not None:
             ev[1].record(stream)
-        score = dv.dv_seed_score(got["entropy"], d_in, d_out, committed)
+        if att is not None:
+            if ev is not None:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            di, do = dv.dv_influence_drift(*att, workspace=att_ws)
+            if ev is not None:
+                e1.record(stream)
+                att_ev.append((e0, e1))
+            score = dv.dv_seed_score(got["entropy"], di.view(-1), do.view(-1), committed)
+        else:
+            score = dv.dv_seed_score(got["entropy"], d_in, d_out, committed)
         if w.n_committed:
             # COVER: the top seeds among committed positions are re-verified (KEEP / REPLACE / REMASK)
             _, _, _, mask = dv.dv_select_topk(score.view(nseq, seq_len), k, eligible=committed.view(nseq, seq_len),
@@ -270,6 +307,12 @@ def main() -> int:
                      "bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
     }
+    if att is not None:
+        att_us = 1000.0 * float(np.mean([a.elapsed_time(b) for a, b in att_ev]))
+        att_bytes = att[0].numel() * 2 + 2 * 4 * R
+        line["influence"] = {"maps": args.influence, "len": w.L, "avg_us": att_us, "bytes_per_launch": att_bytes,
+                             "achieved_GBps": att_bytes / (att_us * 1e-6) / 1e9}
+        line["config"]["step"] = "dv_verify_rows + dv_influence_drift + dv_seed_score + dv_select_topk + dv_decide"
     print(json.dumps(line), flush=True)
     return 0
 

@@ -132,9 +132,9 @@ dv_status influence_geometry(const dv_attention *a, bool need_ptrs, dv::Influenc
     if (!a->probs) return fail(DV_ERR_NULL, "probs is NULL");
     if (!aligned16(a->probs)) return fail(DV_ERR_ALIGN, "probs must be 16-byte aligned");
   }
-  // about 1024 workgroups: split each head's rows into tiles of a multiple of 8 rows
+  // about 512 workgroups: split each head's rows into tiles of a multiple of 8 rows
   const int64_t maps = a->nseq * a->heads;
-  int64_t tiles = maps > 0 ? (1024 + maps - 1) / maps : 1;
+  int64_t tiles = maps > 0 ? (512 + maps - 1) / maps : 1;
   const int64_t max_tiles = (a->len + 63) / 64;
   if (tiles > max_tiles) tiles = max_tiles;
   if (tiles < 1) tiles = 1;

@@ -8,13 +8,14 @@
 //   d_out[b][i] = (1/H) sum_h sum_{k new}    A[b][h][i][k]
 //
 // Pass 1 reads every attention row once (HBM-bound): one workgroup per
-// (sequence, head, tile of rows), lanes over 16-byte chunks of a row, two rows
-// in flight per wave. Each row's mass on new columns is a wave sum written to
-// a per-(sequence, head) row partial; the rows of masked queries are summed
-// into per-lane column accumulators, combined across the four waves in LDS in
-// a fixed order and written as a per-tile column partial. Pass 2 sums the
-// partials of each position over heads and tiles in double precision, in a
-// fixed order, so results do not depend on scheduling.
+// (sequence, head, tile of rows), lanes over 16-byte chunks of a row, up to four
+// rows in flight per wave. Each row's mass on new columns is a wave sum, kept by the
+// lane of that row and stored with those of 63 other rows as a per-(sequence,
+// head) row partial; the rows of masked queries are summed into per-lane
+// column accumulators, combined across the four waves in LDS in a fixed order
+// and written as a per-tile column partial. Pass 2 sums the partials of each
+// position over heads and tiles in double precision, in a fixed order, so
+// results do not depend on scheduling.
 #include "dv_internal.h"
 
 namespace dv {
@@ -63,6 +64,7 @@ __device__ __forceinline__ void widen(const u32x4 &w, float (&x)[BF16 ? 8 : 4]) 
 template <bool BF16, int M>
 __global__ __launch_bounds__(256) void influence_rows_kernel(InfluenceLaunch p) {
   constexpr int N = BF16 ? 8 : 4;
+  constexpr int U = M >= 4 ? 1 : 4 / M;  // rows in flight per wave: about four 16-byte loads per lane
   __shared__ float col[kMaxInfluenceLen];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -78,20 +80,30 @@ __global__ __launch_bounds__(256) void influence_rows_kernel(InfluenceLaunch p) 
   const uint8_t *qmask = p.query_masked + b * L;
   const uint8_t *newc = p.new_cols + b * L;
 
-  // which of my elements are newly written columns, and which lie inside the row
-  uint32_t newbits[M], validbits[M];
+  // per element of my chunks: 1.0 where the column is newly written, else 0.0
+  // (in registers, or for long rows in LDS, shared by the workgroup); and, per
+  // 32-bit word, the bits that belong to the row (the partly filled last
+  // chunk of a row carries padding, which is cleared before use)
+  constexpr bool kNewInLds = M >= 8;
+  __shared__ float s_new[kNewInLds ? kMaxInfluenceLen : 1];
+  float newf[kNewInLds ? 1 : M][N];
+  u32x4 keep[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    newbits[m] = validbits[m] = 0;
     const int32_t c = lane + 64 * m;
+    uint32_t kw[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int e = 0; e < N; ++e) {
       const int32_t j = c * N + e;
-      if (c < nch && j < L) {
-        validbits[m] |= 1u << e;
-        if (newc[j]) newbits[m] |= 1u << e;
-      }
+      const bool valid = c < nch && j < L;
+      if constexpr (!kNewInLds) newf[m][e] = valid && newc[j] ? 1.0f : 0.0f;
+      if (valid) kw[BF16 ? e / 2 : e] |= BF16 ? (0xFFFFu << (16 * (e & 1))) : 0xFFFFFFFFu;
     }
+    keep[m] = u32x4{kw[0], kw[1], kw[2], kw[3]};
+  }
+  if constexpr (kNewInLds) {
+    for (int32_t j = threadIdx.x; j < nch * N; j += 256) s_new[j] = (j < L && newc[j]) ? 1.0f : 0.0f;
+    __syncthreads();
   }
   float acc[M][N];
 #pragma unroll
@@ -107,36 +119,58 @@ __global__ __launch_bounds__(256) void influence_rows_kernel(InfluenceLaunch p) 
       w[m] = c < nch ? __builtin_nontemporal_load(row + c) : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  auto fold_row = [&](int32_t i, const u32x4 (&w)[M]) {
-    const bool masked_query = qmask[i] != 0;  // uniform across the wave
+  // folds one row; returns its mass on new columns (uniform across the wave)
+  auto fold_row = [&](bool masked_query, const u32x4 (&w)[M]) {
     float rs = 0.0f;
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       float x[N];
-      widen<BF16>(w[m], x);
+      widen<BF16>(w[m] & keep[m], x);
 #pragma unroll
       for (int e = 0; e < N; ++e) {
-        const float v = ((validbits[m] >> e) & 1u) ? x[e] : 0.0f;  // the padding after the row is not read as data
-        rs += ((newbits[m] >> e) & 1u) ? v : 0.0f;
-        if (masked_query) acc[m][e] += v;
+        float f;
+        if constexpr (kNewInLds) {
+          const int32_t c = lane + 64 * m;
+          f = c < nch ? s_new[c * N + e] : 0.0f;
+        } else {
+          f = newf[m][e];
+        }
+        rs = __builtin_fmaf(x[e], f, rs);
+      }
+      if (masked_query) {
+#pragma unroll
+        for (int e = 0; e < N; ++e) acc[m][e] += x[e];
       }
     }
-    rs = wave_sum(rs);
-    if (lane == 0) p.row_part[bh * L + i] = rs;
+    return wave_sum(rs);
   };
 
-  int32_t i = r0 + wave;
-  for (; i + 4 < r1; i += 8) {  // two rows of this wave in flight
-    u32x4 w0[M], w1[M];
-    load_row(i, w0);
-    load_row(i + 4, w1);
-    fold_row(i, w0);
-    fold_row(i + 4, w1);
-  }
-  if (i < r1) {
-    u32x4 w0[M];
-    load_row(i, w0);
-    fold_row(i, w0);
+  // this wave's rows: r0 + wave + 4 k, k < K; taken 64 at a time so that lane
+  // k holds the query mask and, at the end, the row sum of row k of the group
+  const int32_t K = r1 > r0 + wave ? (r1 - r0 - wave + 3) / 4 : 0;
+  for (int32_t g = 0; g < K; g += 64) {
+    const int32_t kn = min(64, K - g);
+    const int32_t my_row = r0 + wave + 4 * (g + lane);
+    const unsigned long long qbits = __ballot(lane < kn && qmask[my_row] != 0);
+    float my_sum = 0.0f;
+    int32_t k = 0;
+    for (; k + U <= kn; k += U) {  // U rows of this wave in flight
+      u32x4 w[U][M];
+#pragma unroll
+      for (int u = 0; u < U; ++u) load_row(r0 + wave + 4 * (g + k + u), w[u]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float su = fold_row((qbits >> (k + u)) & 1ull, w[u]);
+        my_sum = lane == k + u ? su : my_sum;
+      }
+    }
+    for (; k < kn; ++k) {
+      u32x4 w0[M];
+      load_row(r0 + wave + 4 * (g + k), w0);
+      const float s0 = fold_row((qbits >> k) & 1ull, w0);
+      my_sum = lane == k ? s0 : my_sum;
+    }
+    if (lane < kn) p.row_part[bh * L + my_row] = my_sum;
   }
 
   // column sums of the tile: wave 0 writes, waves 1..3 add, in that order
@@ -159,19 +193,38 @@ __global__ __launch_bounds__(256) void influence_rows_kernel(InfluenceLaunch p) 
 }
 
 // d_in and d_out of every (sequence, position): the partials summed over heads
-// (and tiles) in double precision, heads in order.
-__global__ __launch_bounds__(256) void influence_reduce_kernel(InfluenceLaunch p) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= p.nseq * p.len) return;
-  const int64_t b = idx / p.len, j = idx - b * p.len;
+// (and tiles) in double precision. A block takes 8 positions; thread (s, c)
+// sums partials s, s + 128, ... of position c in order, then a fixed binary
+// tree over s adds the 128 sums, so the result does not depend on scheduling.
+constexpr int kRedCols = 8, kRedSplit = 128;
+
+__global__ __launch_bounds__(kRedCols * kRedSplit) void influence_reduce_kernel(InfluenceLaunch p) {
+  __shared__ double red_in[kRedSplit][kRedCols], red_out[kRedSplit][kRedCols];
+  const int c = threadIdx.x % kRedCols, sp = threadIdx.x / kRedCols;
+  const int64_t b = blockIdx.y, j = static_cast<int64_t>(blockIdx.x) * kRedCols + c;
   double si = 0.0, so = 0.0;
-  for (int64_t h = 0; h < p.heads; ++h) {
-    const int64_t bh = b * p.heads + h;
-    for (int32_t t = 0; t < p.tiles; ++t) si += p.col_part[(bh * p.tiles + t) * p.len + j];
-    so += p.row_part[bh * p.len + j];
+  if (j < p.len) {
+    const int64_t mc = p.heads * p.tiles;  // column partials of a sequence, in (head, tile) order
+    const float *cp = p.col_part + b * mc * p.len + j;
+    for (int64_t m = sp; m < mc; m += kRedSplit) si += cp[m * p.len];
+    const float *rp = p.row_part + b * p.heads * p.len + j;
+    for (int64_t h = sp; h < p.heads; h += kRedSplit) so += rp[h * p.len];
   }
-  if (p.d_in) p.d_in[idx] = static_cast<float>(si / static_cast<double>(p.heads));
-  if (p.d_out) p.d_out[idx] = static_cast<float>(so / static_cast<double>(p.heads));
+  red_in[sp][c] = si;
+  red_out[sp][c] = so;
+  __syncthreads();
+  for (int stride = kRedSplit / 2; stride > 0; stride >>= 1) {
+    if (sp < stride) {
+      red_in[sp][c] += red_in[sp + stride][c];
+      red_out[sp][c] += red_out[sp + stride][c];
+    }
+    __syncthreads();
+  }
+  if (sp == 0 && j < p.len) {
+    const double inv = 1.0 / static_cast<double>(p.heads);
+    if (p.d_in) p.d_in[b * p.len + j] = static_cast<float>(red_in[0][c] * inv);
+    if (p.d_out) p.d_out[b * p.len + j] = static_cast<float>(red_out[0][c] * inv);
+  }
 }
 
 template <bool BF16, int M>
@@ -201,8 +254,8 @@ hipError_t launch_influence(const InfluenceLaunch &p, hipStream_t stream) {
   if (p.nseq == 0 || p.heads == 0) return hipSuccess;
   hipError_t e = p.bf16 ? launch_typed<true>(p, stream) : launch_typed<false>(p, stream);
   if (e != hipSuccess) return e;
-  const int64_t n = p.nseq * p.len;
-  hipLaunchKernelGGL(influence_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream, p);
+  const dim3 grid(static_cast<unsigned>((p.len + kRedCols - 1) / kRedCols), static_cast<unsigned>(p.nseq));
+  hipLaunchKernelGGL(influence_reduce_kernel, grid, dim3(kRedCols * kRedSplit), 0, stream, p);
   return hipGetLastError();
 }
 

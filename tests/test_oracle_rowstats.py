@@ -10,6 +10,7 @@ import scipy.special
 import scipy.stats
 
 from oracle import rowstats
+from oracle import rowstats as R
 
 
 def _decimal_stats(a, b):
@@ -144,3 +145,60 @@ def test_rejects_non_finite_and_empty_vocab():
 def test_empty_rows():
     st = rowstats.row_stats(np.zeros((0, 5)), np.zeros((0, 5)))
     assert all(len(v) == 0 for v in st.values())
+
+
+# --- variants: reverse KL, -inf logits, probability of a given token ----
+
+def test_kl_reverse_direction_and_closed_form():
+    rng = np.random.default_rng(3)
+    a, b = rng.standard_normal((5, 9)), rng.standard_normal((5, 9)) * 2
+    # the reverse divergence is the forward one with the models exchanged
+    np.testing.assert_allclose(R.kl_reverse(a, b), R.row_stats(b, a)["kl"], rtol=1e-12)
+    # two tokens: KL(q || p) = q ln(q/p) + (1-q) ln((1-q)/(1-p))
+    p, q = 0.3, 0.8
+    a2 = np.log([[p, 1 - p]]); b2 = np.log([[q, 1 - q]])
+    want = q * np.log(q / p) + (1 - q) * np.log((1 - q) / (1 - p))
+    np.testing.assert_allclose(R.kl_reverse(a2, b2), [want], rtol=1e-12)
+
+
+def test_neg_inf_entries_are_absent_tokens():
+    rng = np.random.default_rng(4)
+    V = 12
+    a, b = rng.standard_normal((3, V)) * 2, rng.standard_normal((3, V))
+    drop = np.array([1, 5, 6, 11])
+    ai, bi = a.copy(), b.copy()
+    ai[:, drop] = -np.inf
+    bi[:, drop] = -np.inf
+    keep = np.setdiff1d(np.arange(V), drop)
+    got = R.row_stats(ai, bi, neg_inf=True)
+    ref = R.row_stats(a[:, keep], b[:, keep])
+    for k in ("lse_v", "lse_d", "kl", "entropy", "conf"):
+        np.testing.assert_allclose(got[k], ref[k], rtol=1e-12, atol=1e-15)
+    np.testing.assert_array_equal(got["argmax_v"], keep[ref["argmax_v"]])
+    np.testing.assert_allclose(R.kl_reverse(ai, bi, neg_inf=True), R.kl_reverse(a[:, keep], b[:, keep]), rtol=1e-12)
+    with pytest.raises(ValueError):
+        R.row_stats(ai, bi)                       # -inf only when asked for
+
+
+def test_neg_inf_divergence_to_a_zero():
+    a = np.array([[0.0, 1.0, -np.inf]])
+    b = np.array([[0.0, -np.inf, 2.0]])
+    # the verifier puts mass on token 1 where the drafter has none, and the other way round for token 2
+    assert R.row_stats(a, b, neg_inf=True)["kl"][0] == np.inf
+    assert R.kl_reverse(a, b, neg_inf=True)[0] == np.inf
+    c = np.array([[0.0, 1.0, 2.0]])
+    # mass of the drafter only where the verifier has some: KL(p_v || p_d) is finite, the reverse is not
+    st = R.row_stats(a, c, neg_inf=True)
+    assert np.isfinite(st["kl"][0]) and np.isfinite(st["entropy"][0])
+    assert R.kl_reverse(a, c, neg_inf=True)[0] == np.inf
+    with pytest.raises(ValueError):
+        R.row_stats(np.full((1, 3), -np.inf), c, neg_inf=True)   # a row needs a finite logit
+
+
+def test_prob_of_token():
+    rng = np.random.default_rng(5)
+    a = rng.standard_normal((4, 30)) * 3
+    st = R.row_stats(a, a)
+    np.testing.assert_allclose(R.prob_of(a, st["argmax_v"]), st["conf"], rtol=1e-12)
+    total = sum(R.prob_of(a, np.full(4, t)) for t in range(30))
+    np.testing.assert_allclose(total, 1.0, rtol=1e-12)

@@ -61,12 +61,19 @@ typedef enum dv_decision { DV_NONE = 0, DV_KEEP = 1, DV_REPLACE = 2, DV_REMASK =
  * rows*ld elements. Only the first `vocab` entries of a row are read as
  * logits; the padding up to the next 16-byte boundary is read and ignored.
  * Requirements: both base pointers 16-byte aligned, ld*elt a multiple of 16,
- * vocab <= ld, all logits finite. */
+ * vocab <= ld, all logits finite with |x| <= 1e8 (larger magnitudes overflow
+ * the running sums), or also -inf with DV_LOGITS_NEG_INF. */
+#define DV_LOGITS_NEG_INF 1  /* logits may be -inf: vocabulary entries masked out of the
+                                distribution (probability 0). Each row keeps a finite logit in
+                                each model. Values at or below -2^100 count as -inf. A divergence
+                                is reported +inf when it exceeds 2^64, which it does when one
+                                model puts more than about 1e-11 of its mass where the other has
+                                -inf. */
 typedef struct dv_logits {
   const void *verifier;
   const void *drafter;
   int32_t dtype;   /* dv_dtype */
-  int32_t reserved;
+  int32_t flags;   /* 0 or DV_LOGITS_NEG_INF */
   int64_t rows;
   int64_t vocab;
   int64_t ld;
@@ -95,7 +102,13 @@ typedef struct dv_noise {
  *   entropy        -sum_i p_v,i ln p_v,i, nats
  *   conf           max_i p_v,i
  *   argmax_v/_d    lowest index of the row maximum
- *   tok_v/_d       Gumbel-max token under the shared noise (argmax at T = 0) */
+ *   tok_v/_d       Gumbel-max token under the shared noise (argmax at T = 0)
+ *   kl_rev         KL(p_drafter || p_verifier), nats (asking for it, like
+ *                  DV_LOGITS_NEG_INF, selects the extended pass: one more
+ *                  multiply-add per logit pair)
+ *   p_tok_d        p_v of the drafter's token tok_d: the verifier's confidence
+ *                  for the drafted token ([DualDiffusion] §2 item 3, the other
+ *                  reading of "confidence for the token") */
 typedef struct dv_row_stats {
   float *lse_v;
   float *lse_d;
@@ -106,6 +119,8 @@ typedef struct dv_row_stats {
   int32_t *argmax_d;
   int32_t *tok_v;
   int32_t *tok_d;
+  float *kl_rev;
+  float *p_tok_d;
 } dv_row_stats;
 
 /* Optional launch-shape override for dv_verify_rows (NULL = automatic). A
@@ -151,10 +166,12 @@ typedef enum dv_rule {
   DV_RULE_KL_OR_CONF = 3,     /* REMASK iff either holds */
   DV_RULE_COVER = 4,          /* [COVER] §3: KEEP if tok_v == current; else REPLACE if
                                  conf >= conf_thr; else REMASK */
-  DV_RULE_COUPLED_ACCEPT = 5  /* [SPOT] §1/§3: per candidate of group_len rows, KEEP the
+  DV_RULE_COUPLED_ACCEPT = 5, /* [SPOT] §1/§3: per candidate of group_len rows, KEEP the
                                  leading rows whose tok_v equals the current token,
                                  REPLACE the first disagreeing row with tok_v, REMASK
                                  the rows after it */
+  DV_RULE_CONF_DRAFT = 6      /* [DualDiffusion] §2 item 3 read as the verifier's confidence
+                                 in the drafted token: REMASK iff p_tok_d < conf_thr */
 } dv_rule;
 
 typedef struct dv_decide_args {
@@ -171,8 +188,8 @@ typedef struct dv_decide_args {
 
 /* Per-position decision ([DualDiffusion] §2 verification items 1-3;
  * [COVER] §3 adaptive revision outcomes; [SPOT] §1/§3 coupled-noise check).
- * Reads from `stats` only the members the rule needs (kl; conf; tok_v), plus
- * tok_d when cur_tok is NULL. subject: device uint8 [rows] or NULL (all
+ * Reads from `stats` only the members the rule needs (kl; conf; tok_v;
+ * p_tok_d), plus tok_d when cur_tok is NULL. subject: device uint8 [rows] or NULL (all
  * rows); rows with subject == 0 get DV_NONE and keep their current token.
  * cur_tok: device int32 [rows], the current token assignment, or NULL to use
  * tok_d. Outputs: decision uint8 [rows], out_tok int32 [rows] (current token

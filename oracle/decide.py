@@ -3,7 +3,8 @@
 Test infrastructure: see the package docstring for who may import this.
 
 Decision codes: 0 NONE (row not decided), 1 KEEP, 2 REPLACE, 3 REMASK.
-Rule codes: 0 TRUST, 1 KL, 2 CONF, 3 KL_OR_CONF, 4 COVER, 5 COUPLED_ACCEPT.
+Rule codes: 0 TRUST, 1 KL, 2 CONF, 3 KL_OR_CONF, 4 COVER, 5 COUPLED_ACCEPT,
+6 CONF_DRAFT.
 
 Sources and readings:
 
@@ -16,6 +17,9 @@ Sources and readings:
 * CONF, item 3: low verifier confidence leads to remasking. REMASK iff
   conf < theta, else KEEP.
 * KL_OR_CONF: REMASK iff either of the two conditions holds.
+* CONF_DRAFT, item 3 read the other way: the verifier's confidence for the
+  drafted token itself, p_v(tok_d) (``stats["p_tok"]``). REMASK iff
+  p_tok < theta, else KEEP.
 * COVER, [COVER] §3 "Adaptive revision outcomes": when the re-predicted token
   equals the current assignment the token is kept; when it differs and the
   verifier is confident it is replaced in place; it is remasked only when it
@@ -46,10 +50,10 @@ from __future__ import annotations
 import numpy as np
 
 NONE, KEEP, REPLACE, REMASK = 0, 1, 2, 3
-TRUST, KL, CONF, KL_OR_CONF, COVER, COUPLED_ACCEPT = 0, 1, 2, 3, 4, 5
+TRUST, KL, CONF, KL_OR_CONF, COVER, COUPLED_ACCEPT, CONF_DRAFT = 0, 1, 2, 3, 4, 5, 6
 
 __all__ = ["NONE", "KEEP", "REPLACE", "REMASK", "TRUST", "KL", "CONF", "KL_OR_CONF",
-           "COVER", "COUPLED_ACCEPT", "decide", "accepted_prefix", "best_group"]
+           "COVER", "COUPLED_ACCEPT", "CONF_DRAFT", "decide", "accepted_prefix", "best_group"]
 
 
 def decide(rule: int, stats: dict, *, tau_kl: float = 0.0, conf_thr: float = 0.0,
@@ -73,6 +77,9 @@ def decide(rule: int, stats: dict, *, tau_kl: float = 0.0, conf_thr: float = 0.0
         if rule in (CONF, KL_OR_CONF):
             remask |= np.asarray(stats["conf"], dtype=np.float64) < conf_thr
         dec[subj] = np.where(remask[subj], REMASK, KEEP)
+    elif rule == CONF_DRAFT:
+        p_tok = np.asarray(stats["p_tok"], dtype=np.float64)
+        dec[subj] = np.where(p_tok[subj] < conf_thr, REMASK, KEEP)
     elif rule == COVER:
         tok_v = np.asarray(stats["tok_v"]).astype(np.int32)
         conf = np.asarray(stats["conf"], dtype=np.float64)

@@ -17,15 +17,18 @@ from oracle import rowstats
 RTOL = 1e-4
 ATOL = 1e-5
 BAND = 1e-5
-FLOAT_STATS = ("lse_v", "lse_d", "kl", "entropy", "conf")
+FLOAT_STATS = ("lse_v", "lse_d", "kl", "entropy", "conf", "kl_rev")
 
 
-def oracle_rows(a, b, dtype: str, temperature: float, seed: int, pos) -> dict:
-    """Oracle statistics, tokens and token margins of rows stored as ``dtype``."""
+def oracle_rows(a, b, dtype: str, temperature: float, seed: int, pos, neg_inf: bool = False) -> dict:
+    """Oracle statistics, tokens and token margins of rows stored as ``dtype``
+    (with kl_rev and p_tok_d, the verifier's probability of the drafter's token)."""
     a64 = rowstats.as_float64(a, dtype)
     b64 = rowstats.as_float64(b, dtype)
-    st = rowstats.row_stats(a64, b64)
+    st = rowstats.row_stats(a64, b64, neg_inf=neg_inf)
     st.update(onoise.gumbel_tokens(a64, b64, temperature, seed, np.asarray(pos)))
+    st["kl_rev"] = rowstats.kl_reverse(a64, b64, neg_inf=neg_inf)
+    st["p_tok_d"] = rowstats.prob_of(a64, st["tok_d"]) if len(a64) else np.zeros(0)
     return st
 
 
@@ -55,6 +58,12 @@ def compare_stats(got: dict, ref: dict, temperature: float, ctx: str = "") -> di
         if k in got:
             bad = got[k] != ref[k]
             assert not bad.any(), f"{ctx} {k}: rows {np.nonzero(bad)[0][:10]} gpu {got[k][bad][:5]} oracle {ref[k][bad][:5]}"
+    if "p_tok_d" in got and "tok_d" in got:
+        # the probability of the drafter's token, where both sides picked the same token
+        same = got["tok_d"] == ref["tok_d"]
+        g, r = got["p_tok_d"].astype(np.float64)[same], ref["p_tok_d"][same]
+        bad = np.abs(g - r) > ATOL + RTOL * np.abs(r)
+        assert not bad.any(), f"{ctx} p_tok_d: gpu {g[bad][:5]} oracle {r[bad][:5]}"
     for k, mk in (("tok_v", "margin_v"), ("tok_d", "margin_d")):
         if k not in got:
             continue

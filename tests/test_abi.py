@@ -46,8 +46,8 @@ def test_status_strings(lib):
 FAKE = 1 << 20  # a non-null, 16-byte aligned address that is never dereferenced
 
 
-def _logits(rows=4, vocab=64, ld=64, dtype=B.DV_BF16, va=FAKE, vb=FAKE):
-    return B.dv_logits(verifier=va, drafter=vb, dtype=dtype, reserved=0, rows=rows, vocab=vocab, ld=ld)
+def _logits(rows=4, vocab=64, ld=64, dtype=B.DV_BF16, va=FAKE, vb=FAKE, flags=0):
+    return B.dv_logits(verifier=va, drafter=vb, dtype=dtype, flags=flags, rows=rows, vocab=vocab, ld=ld)
 
 
 def _noise(T=0.0, period=0, pos=None):
@@ -65,6 +65,8 @@ def test_verify_validation(lib):
                               None) == B.DV_ERR_NULL
     assert _verify(lib, _logits(), _noise(), out=False) == B.DV_ERR_NULL
     assert _verify(lib, _logits(dtype=7), _noise()) == B.DV_ERR_DTYPE
+    assert _verify(lib, _logits(flags=2), _noise()) == B.DV_ERR_ARG             # unknown flag
+    assert _verify(lib, _logits(rows=0, va=0, vb=0, flags=B.DV_LOGITS_NEG_INF), _noise()) == B.DV_OK
     assert _verify(lib, _logits(rows=-1), _noise()) == B.DV_ERR_SHAPE
     assert _verify(lib, _logits(vocab=0), _noise()) == B.DV_ERR_SHAPE
     assert _verify(lib, _logits(vocab=65, ld=64), _noise()) == B.DV_ERR_SHAPE

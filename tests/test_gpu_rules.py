@@ -299,3 +299,23 @@ def test_band_set_decisions():
         if rule != "COVER":
             assert counts[dv.DV_REMASK] > 50 and counts[dv.DV_KEEP] > 50, (rule, counts)
     print("in-band rows", inband, flush=True)
+
+
+def test_conf_draft_rule():
+    """CONF_DRAFT: REMASK iff the verifier's probability of the drafted token is below theta."""
+    print("case: CONF_DRAFT", flush=True)
+    dev = _dev()
+    rng = np.random.default_rng(12)
+    rows = 999
+    p_tok = rng.uniform(0, 1, rows).astype(np.float32)
+    p_tok[::7] = np.float32(0.6)                      # exactly at the threshold: KEEP
+    tok_d = rng.integers(0, 50, rows).astype(np.int32)
+    subject = (rng.random(rows) < 0.7).astype(np.uint8)
+    gst = {"p_tok_d": _t(p_tok, dev), "tok_d": _t(tok_d, dev)}
+    for subj in (None, subject):
+        d, o, _, _ = dv.dv_decide("CONF_DRAFT", gst, conf_thr=0.6, mask_token=-5,
+                                  subject=None if subj is None else _t(subj, dev))
+        rd, ro = odecide.decide(odecide.CONF_DRAFT, {"p_tok": p_tok.astype(np.float64), "tok_d": tok_d},
+                                conf_thr=np.float32(0.6), mask_token=-5, subject=subj)
+        np.testing.assert_array_equal(d.cpu().numpy(), rd)
+        np.testing.assert_array_equal(o.cpu().numpy(), ro)

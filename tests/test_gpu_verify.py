@@ -258,3 +258,84 @@ def test_workload_throughput_full_size():
     print(rep, flush=True)
     del a, b
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------- extended pass: -inf, reverse KL ----
+
+ALL_OUT = dv.STAT_FIELDS
+
+
+def _run_ext(a_np, b_np, dtype, T, seed=0, period=0, neg_inf=False, tuning=None):
+    dev = _dev()
+    a = _upload(a_np, dtype, dev)
+    b = _upload(b_np, dtype, dev)
+    got = dv.dv_verify_rows(a, b, temperature=T, seed=seed, pos_period=period, outputs=ALL_OUT, neg_inf=neg_inf,
+                            tuning=tuning)
+    torch.cuda.synchronize()
+    return to_numpy(got)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_extended_outputs_and_core_unchanged(dtype):
+    """kl_rev and p_tok_d against the oracle; the extended pass leaves every core output bit for bit the same."""
+    print(f"case: extended outputs {dtype}", flush=True)
+    for rows, V, T, period in ((9, 1003, 1.0, 0), (40, 20000, 1.0, 4), (33, 5000, 0.0, 0), (64, 4096, 0.7, 8)):
+        a, b = _peaked(rows, V, rows + V, dtype)
+        ext = _run_ext(a, b, dtype, T, seed=3, period=period)
+        base = _run(a, b, dtype, T, seed=3, period=period)
+        for k in dv.CORE_FIELDS:
+            np.testing.assert_array_equal(ext[k], base[k], err_msg=f"{k} differs in the extended pass")
+        ref = oracle_rows(a, b, dtype, T, 3, _positions(rows, None, period))
+        compare_stats(ext, ref, T, f"extended {dtype} {rows}x{V} T={T}")
+        for split in (1, 3, 16):
+            got = _run_ext(a, b, dtype, T, seed=3, period=period, tuning={"split": split})
+            compare_stats(got, ref, T, f"extended {dtype} split={split}")
+
+
+LIM = np.float32(-2.0 ** 100)
+
+
+def _below_as_neg_inf(x, dtype):
+    """Values at or below -2^100 count as -inf (the documented meaning of the flag)."""
+    if dtype == "fp32":
+        return np.where(x <= LIM, np.float32(-np.inf), x).astype(np.float32)
+    vals = (x.astype(np.uint32) << 16).view(np.float32)
+    return np.where(vals <= LIM, np.uint16(0xFF80), x).astype(np.uint16)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_neg_inf_logits(dtype):
+    """-inf entries (masked vocabulary) in one or both models, against the oracle's -inf conventions."""
+    print(f"case: -inf logits {dtype}", flush=True)
+    rng = np.random.default_rng(31)
+    rows, V = 24, 3001
+    a = (rng.standard_normal((rows, V)) * 2).astype(np.float32)
+    b = (a + rng.standard_normal((rows, V)) * 0.5).astype(np.float32)
+    shared = rng.random((rows, V)) < 0.3
+    a[shared] = -np.inf
+    b[shared] = -np.inf
+    # rows 0-3: extra -inf in the drafter only (KL(p_v || p_d) = +inf); rows 4-7: in the verifier only
+    only_d = (rng.random((rows, V)) < 0.2) & ~shared
+    b[:4][only_d[:4]] = -np.inf
+    a[4:8][only_d[4:8]] = -np.inf
+    a[8, :] = -np.inf; a[8, 17] = 3.0                              # one finite logit left
+    a[9, :] = -np.inf; a[9, V - 1] = 1.5                           # only the last element, in the tail chunk
+    b[9, :] = -np.inf; b[9, V - 1] = -2.0
+    a[10, :] = -1e35                                               # below -2^100: the same as -inf but one
+    a[10, 5] = 0.0
+    a[11, :] = -np.inf                                             # -2^100 itself, and -inf, in a row
+    a[11, ::3] = -2.0 ** 100
+    a[11, 7] = -4.0
+    if dtype == "bf16":
+        aa, bb = W.round_bf16_bits(a), W.round_bf16_bits(b)
+    else:
+        aa, bb = a, b
+    for T, period in ((0.0, 0), (1.0, 0), (1.0, 4)):
+        got = _run_ext(aa, bb, dtype, T, seed=8, period=period, neg_inf=True)
+        ref = oracle_rows(_below_as_neg_inf(aa, dtype), _below_as_neg_inf(bb, dtype), dtype, T, 8,
+                          _positions(rows, None, period), neg_inf=True)
+        compare_stats(got, ref, T, f"-inf {dtype} T={T} period={period}")
+        assert np.isinf(got["kl"][:4]).all() and np.isfinite(got["kl"][4:8]).all()
+        assert np.isinf(got["kl_rev"][4:8]).all() and np.isfinite(got["kl_rev"][:4]).all()
+        assert got["argmax_v"][8] == 17 and got["argmax_v"][9] == V - 1 and got["tok_d"][9] == V - 1
+        assert got["conf"][8] == 1.0

@@ -193,3 +193,13 @@ def test_exhaustive_small_rule_grid():
         d_kl = D.decide(D.KL, st, tau_kl=0.1, conf_thr=0.9)[0][0]
         d_cf = D.decide(D.CONF, st, tau_kl=0.1, conf_thr=0.9)[0][0]
         assert d_or == (M if M in (d_kl, d_cf) else K)
+
+
+def test_conf_draft_truth_table():
+    # REMASK exactly when the verifier's probability of the drafted token is below theta (strict)
+    st = dict(p_tok=np.array([0.1, 0.9, 0.95, 0.899999]), tok_d=np.array([3, 4, 5, 6], np.int32),
+              tok_v=np.array([3, 0, 0, 0], np.int32))
+    dec, out = D.decide(D.CONF_DRAFT, st, conf_thr=0.9, mask_token=-2)
+    assert list(dec) == [M, K, K, M] and list(out) == [-2, 4, 5, -2]
+    dec, _ = D.decide(D.CONF_DRAFT, st, conf_thr=0.9, subject=[1, 0, 1, 0])
+    assert list(dec) == [M, N, K, N]

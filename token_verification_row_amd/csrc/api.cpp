@@ -52,6 +52,7 @@ constexpr int32_t kMaxSplit = 16;  // waves of one workgroup
 dv_status check_logits(const dv_logits *x, bool need_ptrs) {
   if (!x) return fail(DV_ERR_NULL, "logits descriptor is NULL");
   if (x->dtype != DV_FP32 && x->dtype != DV_BF16) return fail(DV_ERR_DTYPE, "unknown dtype %d", x->dtype);
+  if ((x->flags & ~DV_LOGITS_NEG_INF) != 0) return fail(DV_ERR_ARG, "unknown logits flags 0x%x", x->flags);
   if (x->rows < 0 || x->rows > kMaxIndex) return fail(DV_ERR_SHAPE, "rows %lld out of range", (long long)x->rows);
   if (x->vocab < 1 || x->vocab > kMaxIndex) return fail(DV_ERR_SHAPE, "vocab %lld out of range", (long long)x->vocab);
   if (x->ld < x->vocab) return fail(DV_ERR_SHAPE, "ld %lld < vocab %lld", (long long)x->ld, (long long)x->vocab);
@@ -194,6 +195,7 @@ dv_status dv_verify_rows(const dv_logits *logits, const dv_noise *noise, const d
   p.ld = logits->ld;
   p.bf16 = logits->dtype == DV_BF16;
   p.greedy = noise->temperature == 0.0f;
+  p.neg_inf = (logits->flags & DV_LOGITS_NEG_INF) != 0;
   p.cT = p.greedy ? 0.0f : 1.44269504088896340736f / noise->temperature;
   if (!p.greedy && !std::isfinite(p.cT)) return fail(DV_ERR_ARG, "temperature too small");
   p.seed_b = dv::seed_word(noise->seed);
@@ -214,7 +216,7 @@ dv_status dv_decide(const dv_decide_args *a, const dv_row_stats *stats, const ui
   if (!a || !stats) return fail(DV_ERR_NULL, "args or stats is NULL");
   if (a->rows < 0 || a->rows > kMaxIndex) return fail(DV_ERR_SHAPE, "rows out of range");
   if (a->group_len < 0 || a->group_len > kMaxIndex) return fail(DV_ERR_SHAPE, "group_len out of range");
-  if (a->rule < DV_RULE_TRUST || a->rule > DV_RULE_COUPLED_ACCEPT) return fail(DV_ERR_ARG, "unknown rule %d", a->rule);
+  if (a->rule < DV_RULE_TRUST || a->rule > DV_RULE_CONF_DRAFT) return fail(DV_ERR_ARG, "unknown rule %d", a->rule);
   if (!finite(a->tau_kl) || !finite(a->conf_thr)) return fail(DV_ERR_ARG, "thresholds must be finite");
   const bool need_groups = a->rule == DV_RULE_COUPLED_ACCEPT || prefix_len || best_group;
   if (need_groups) {
@@ -240,6 +242,9 @@ dv_status dv_decide(const dv_decide_args *a, const dv_row_stats *stats, const ui
       case DV_RULE_COUPLED_ACCEPT:
         if (!stats->tok_v) return fail(DV_ERR_NULL, "rule COUPLED_ACCEPT needs stats.tok_v");
         break;
+      case DV_RULE_CONF_DRAFT:
+        if (!stats->p_tok_d) return fail(DV_ERR_NULL, "rule CONF_DRAFT needs stats.p_tok_d");
+        break;
       default:
         break;
     }
@@ -264,6 +269,7 @@ dv_status dv_decide(const dv_decide_args *a, const dv_row_stats *stats, const ui
   p.group_len = a->group_len;
   p.kl = stats->kl;
   p.conf = stats->conf;
+  p.p_tok = stats->p_tok_d;
   p.tok_v = stats->tok_v;
   p.tok_d = stats->tok_d;
   p.subject = subject;

@@ -46,7 +46,8 @@ struct alignas(16) Partial {
   float s_v, s_d;
   int32_t cm_v, cm_d;
   int32_t cs_v, cs_d;
-  int32_t pad0, pad1;
+  float D_d;  // sum e_d (a - b) against rho_d (extended pass; 0 otherwise)
+  int32_t pad1;
 };
 static_assert(sizeof(Partial) == 64, "partial state must be 64 bytes");
 
@@ -58,6 +59,7 @@ struct VerifyLaunch {
   int64_t ld;          // elements
   int32_t bf16;
   int32_t greedy;      // temperature == 0
+  int32_t neg_inf;     // logits may hold -inf (DV_LOGITS_NEG_INF)
   float cT;            // log2(e) / temperature (0 when greedy)
   uint32_t seed_b;     // seed word B
   const int32_t *pos;  // device or NULL
@@ -78,7 +80,7 @@ struct DecideLaunch {
   float tau_kl, conf_thr;
   int32_t mask_token;
   int64_t rows, group_len;
-  const float *kl, *conf;
+  const float *kl, *conf, *p_tok;
   const int32_t *tok_v, *tok_d;
   const uint8_t *subject;
   const int32_t *cur_tok;

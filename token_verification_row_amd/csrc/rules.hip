@@ -11,7 +11,8 @@ namespace {
 
 // ---------------------------------------------------------------- decide ----
 // Rule for one row in isolation ([DualDiffusion] §2 "Verification algorithms"
-// items 1-3; [COVER] §3 "Adaptive revision outcomes").
+// items 1-3, item 3 also read as the confidence in the drafted token;
+// [COVER] §3 "Adaptive revision outcomes").
 __device__ __forceinline__ uint8_t rule_of_row(const DecideLaunch &p, int64_t r, int32_t cur) {
   switch (p.rule) {
     case DV_RULE_TRUST:
@@ -25,6 +26,8 @@ __device__ __forceinline__ uint8_t rule_of_row(const DecideLaunch &p, int64_t r,
     case DV_RULE_COVER:
       if (p.tok_v[r] == cur) return DV_KEEP;
       return p.conf[r] >= p.conf_thr ? DV_REPLACE : DV_REMASK;
+    case DV_RULE_CONF_DRAFT:
+      return p.p_tok[r] < p.conf_thr ? DV_REMASK : DV_KEEP;
     default:
       return DV_NONE;
   }

@@ -68,6 +68,48 @@ struct Chunk {
 
 __device__ __forceinline__ u32x4 load_stream(const u32x4 *p) { return __builtin_nontemporal_load(p); }
 
+// Logits that may hold -inf (masked vocabulary entries): every value at or
+// below -2^100, -inf included, is raised to -2^100 on the raw bits, before any
+// arithmetic. Such an entry keeps probability 0 (its exponential underflows)
+// while products like 0 * (x - rho) stay finite, and because -2^100 times
+// log2(e) is exact in float, a reference taken at that value reproduces it
+// exactly in the fused multiply-adds. Negative values order by their unsigned
+// bit patterns in reverse, so an unsigned minimum does it: per 16-bit half
+// for bf16 (0xF180), per word for fp32 (0xF1800000).
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+template <bool BF16>
+__device__ __forceinline__ u32x4 clamp_neg(u32x4 w) {
+  // the words are copied out of the vector first: a bit cast takes whole
+  // objects, not vector elements
+  uint32_t e[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (BF16) {
+      const u16x2 lim = {0xF180u, 0xF180u};
+      const u16x2 h = __builtin_bit_cast(u16x2, e[i]);
+      e[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(h, lim));
+    } else {
+      e[i] = min(e[i], 0xF1800000u);
+    }
+  }
+  return u32x4{e[0], e[1], e[2], e[3]};
+}
+
+// The streaming read of a chunk, and a plain read (the tail chunk, the
+// argmax refinement); with EXT the -inf clamp is applied to both, so every
+// later comparison sees the same values.
+template <bool BF16, bool EXT>
+__device__ __forceinline__ u32x4 load_chunk(const u32x4 *p) {
+  const u32x4 w = load_stream(p);
+  return EXT ? clamp_neg<BF16>(w) : w;
+}
+template <bool BF16, bool EXT>
+__device__ __forceinline__ u32x4 read_chunk(const u32x4 *p) {
+  const u32x4 w = *p;
+  return EXT ? clamp_neg<BF16>(w) : w;
+}
+
 // Gumbel noise in log2 units: G = -log2(-log2 u), u = (2 (h >> 9) + 1) 2^-24.
 // argmax_i (x_i/T + g_i) with g = -ln(-ln u) equals argmax_i (x_i log2(e)/T + G_i),
 // since g log2(e) = G - log2(e) ln(ln 2) is an increasing map of G.
@@ -156,7 +198,7 @@ __device__ __forceinline__ float chunk_noise_bound(int32_t c, uint32_t key) {
 // Per-lane accumulator of one (row, slice).
 struct Lane {
   float rho_v, S_v, S_v2, W_v, D_v, thr_v;  // S_v + S_v2: even / odd elements (independent add chains)
-  float rho_d, S_d, S_d2, thr_d;
+  float rho_d, S_d, S_d2, thr_d, D_d;  // D_d = sum e_d (a - b): the reverse divergence (extended pass only)
   float m_v, m_d, s_v, s_d;
   int32_t cm_v, cm_d, cs_v, cs_d;
   float wb_v, wb_d;  // wave-wide lower bounds of the best perturbed scores (equal in all lanes)
@@ -165,7 +207,7 @@ struct Lane {
     wb_v = wb_d = -INFINITY;
     rho_v = rho_d = -INFINITY;
     thr_v = thr_d = -INFINITY;
-    S_v = S_v2 = W_v = D_v = S_d = S_d2 = 0.0f;
+    S_v = S_v2 = W_v = D_v = S_d = S_d2 = D_d = 0.0f;
     m_v = m_d = s_v = s_d = -INFINITY;
     cm_v = cm_d = cs_v = cs_d = INT_MAX;
   }
@@ -247,8 +289,9 @@ __device__ __forceinline__ void rebase_d(Lane &st, float x) {
     const float sc = __builtin_amdgcn_exp2f(st.rho_d - nr);
     st.S_d *= sc;
     st.S_d2 *= sc;
+    st.D_d *= sc;
   } else {
-    st.S_d = st.S_d2 = 0.0f;
+    st.S_d = st.S_d2 = st.D_d = 0.0f;
   }
   st.rho_d = nr;
   st.thr_d = (nr + kRebase) * (1.0f / kLog2e);
@@ -296,7 +339,7 @@ __device__ __forceinline__ void fold_tokens(Lane &st, const float (&a)[N], const
 // state and return the chunk maxima of both rows in cma / cmb. MASKED: only
 // the first nvalid elements are logits (last chunk of a row). One pass over
 // the elements with running accumulators keeps few temporaries live.
-template <int N, bool MASKED>
+template <int N, bool MASKED, bool EXT>
 __device__ __forceinline__ void fold_stats(Lane &st, float (&a)[N], float (&b)[N], int32_t c, int nvalid, float &cma,
                                            float &cmb) {
   if constexpr (MASKED) {
@@ -333,7 +376,7 @@ __device__ __forceinline__ void fold_stats(Lane &st, float (&a)[N], float (&b)[N
   if (cmb > st.thr_d) rebase_d(st, cmb);
 
   const float nrv = -st.rho_v, nrd = -st.rho_d;
-  float W = st.W_v, D = st.D_v;
+  float W = st.W_v, D = st.D_v, Dd = st.D_d;
   float sv0 = st.S_v, sv1 = st.S_v2, sd0 = st.S_d, sd1 = st.S_d2;
 #pragma unroll
   for (int j = 0; j < N; ++j) {
@@ -355,10 +398,13 @@ __device__ __forceinline__ void fold_stats(Lane &st, float (&a)[N], float (&b)[N
       sd0 += f;
     }
     W = __builtin_fmaf(e, tv, W);
-    D = __builtin_fmaf(e, a[j] - b[j], D);
+    const float dab = a[j] - b[j];
+    D = __builtin_fmaf(e, dab, D);
+    if constexpr (EXT) Dd = __builtin_fmaf(f, dab, Dd);
   }
   st.W_v = W;
   st.D_v = D;
+  if constexpr (EXT) st.D_d = Dd;
   st.S_v = sv0;
   st.S_v2 = sv1;
   st.S_d = sd0;
@@ -368,14 +414,14 @@ __device__ __forceinline__ void fold_stats(Lane &st, float (&a)[N], float (&b)[N
 // One chunk, statistics and (unless greedy) tokens with noise from the hash.
 // Chunks reach the token bookkeeping out of index order (queued scoring), so
 // ties compare chunk indices.
-template <bool BF16, int MODE, bool MASKED>
+template <bool BF16, int MODE, bool MASKED, bool EXT>
 __device__ __forceinline__ void fold_chunk(Lane &st, const u32x4 &wa, const u32x4 &wb, int32_t c, uint32_t key,
                                            float cT, int nvalid) {
   constexpr int N = Chunk<BF16>::N;
   float x[N], y[N], cma, cmb;
   widen<BF16>(wa, x);
   widen<BF16>(wb, y);
-  fold_stats<N, MASKED>(st, x, y, c, nvalid, cma, cmb);
+  fold_stats<N, MASKED, EXT>(st, x, y, c, nvalid, cma, cmb);
   if constexpr (MODE != kGreedy) {
     float g[N];
     noise_chunk<BF16>(g, c, key);
@@ -415,7 +461,7 @@ constexpr int kStep = DV_STEP_CHUNKS;  // chunks per lane per step of the stream
 
 // Raw registers of K chunks (c, c + 64, ..., c + 64 (K-1)) of both matrices
 // and, with a noise table, the largest noise value of each chunk.
-template <bool BF16, bool PRUNE, int K>
+template <bool BF16, bool PRUNE, int K, bool EXT>
 struct StepRegs {
   u32x4 a[K], b[K];
   float gm[K];
@@ -425,8 +471,8 @@ struct StepRegs {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const int32_t ck = at(c + 64 * k);
-      a[k] = load_stream(ra + ck);
-      b[k] = load_stream(rb + ck);
+      a[k] = load_chunk<BF16, EXT>(ra + ck);
+      b[k] = load_chunk<BF16, EXT>(rb + ck);
       if constexpr (PRUNE) gm[k] = g_cmax[ck];
     }
   }
@@ -452,7 +498,7 @@ struct StepRegs {
           float x[N], y[N], cma, cmb;
           widen<BF16>(a[k], x);
           widen<BF16>(b[k], y);
-          fold_stats<N, false>(st, x, y, ck, N, cma, cmb);
+          fold_stats<N, false, EXT>(st, x, y, ck, N, cma, cmb);
           const float g = MODE == kTableBound ? gm[k] : chunk_noise_bound<N>(ck, key);
           need = __builtin_fmaf(cma, cT, g) >= st.wb_v || __builtin_fmaf(cmb, cT, g) >= st.wb_d;
         }
@@ -473,7 +519,7 @@ struct StepRegs {
           nq += cnt;
         }
       } else {
-        if (valid) fold_chunk<BF16, kGreedy, false>(st, a[k], b[k], ck, key, cT, N);
+        if (valid) fold_chunk<BF16, kGreedy, false, EXT>(st, a[k], b[k], ck, key, cT, N);
       }
     }
   }
@@ -488,7 +534,7 @@ struct StepRegs {
 // every path (the last step re-reads its own chunks, which hit in cache), so
 // the wait counts never have to cover a path without them and no register
 // copy forces a wait at the back edge.
-template <bool BF16, int MODE>
+template <bool BF16, int MODE, bool EXT>
 __device__ __forceinline__ void scan_slice(Lane &st, const u32x4 *ra, const u32x4 *rb, int32_t c0, int32_t c1,
                                            int32_t nfull, int nvalid_tail, float cT, uint32_t key,
                                            const float *g_cmax, ScoreQueue *q, int lane) {
@@ -499,7 +545,7 @@ __device__ __forceinline__ void scan_slice(Lane &st, const u32x4 *ra, const u32x
   if (nsteps > 0) {
     // in-bounds address for chunks past the end (their data is not used)
     auto at = [&](int32_t cc) { return cc < cend ? cc : c0; };
-    StepRegs<BF16, MODE == kTableBound, kStep> X, Y;
+    StepRegs<BF16, MODE == kTableBound, kStep, EXT> X, Y;
     int32_t c = c0 + lane;
     X.load(ra, rb, g_cmax, c, at);
     for (int32_t t = 0;;) {
@@ -520,7 +566,8 @@ __device__ __forceinline__ void scan_slice(Lane &st, const u32x4 *ra, const u32x
   }
   // the last, partly filled chunk of the row (vocab not a multiple of N)
   if (nvalid_tail > 0 && nfull >= c0 && nfull < c1 && lane == ((nfull - c0) & 63))
-    fold_chunk<BF16, MODE, true>(st, ra[nfull], rb[nfull], nfull, key, cT, nvalid_tail);
+    fold_chunk<BF16, MODE, true, EXT>(st, read_chunk<BF16, EXT>(ra + nfull), read_chunk<BF16, EXT>(rb + nfull), nfull, key,
+                                      cT, nvalid_tail);
 }
 
 // Reduce the lane states of a wave into one partial (valid in every lane).
@@ -543,6 +590,7 @@ __device__ __forceinline__ Partial wave_reduce(const Lane &st) {
     const bool has = Sd > 0.0f;
     const float sc = has ? __builtin_amdgcn_exp2f(st.rho_d - R) : 0.0f;
     t.S_d = wave_sum(Sd * sc);
+    t.D_d = wave_sum(st.D_d * sc);
     t.rho_d = R;
   }
   t.m_v = st.m_v;
@@ -557,7 +605,7 @@ __device__ __forceinline__ Partial wave_reduce(const Lane &st) {
   t.s_d = st.s_d;
   t.cs_d = st.cs_d;
   wave_argmax(t.s_d, t.cs_d);
-  t.pad0 = t.pad1 = 0;
+  t.pad1 = 0;
   return t;
 }
 
@@ -568,13 +616,13 @@ __device__ __forceinline__ Partial wave_reduce(const Lane &st) {
 // score is recomputed with exactly the arithmetic of the streaming pass. A
 // chunk index outside the row (only possible when the logits hold NaN, which
 // is not supported) gives -1 without touching memory.
-template <bool BF16, bool SCORE>
+template <bool BF16, bool SCORE, bool EXT>
 __device__ __forceinline__ int32_t refine_in_chunk(const u32x4 *row, int32_t c, float target, int64_t vocab, float cT,
                                                    uint32_t key, int lane) {
   constexpr int N = Chunk<BF16>::N;
   if (c < 0 || static_cast<int64_t>(c) * N >= vocab) return -1;
   float x[N];
-  widen<BF16>(row[c], x);  // the same 16 bytes for every lane: one request
+  widen<BF16>(read_chunk<BF16, EXT>(row + c), x);  // the same 16 bytes for every lane: one request
   float v = x[0];
 #pragma unroll
   for (int j = 1; j < N; ++j) v = (lane == j) ? x[j] : v;
@@ -590,27 +638,38 @@ __device__ __forceinline__ int32_t refine_in_chunk(const u32x4 *row, int32_t c, 
 
 // Row results from the reduced state of a whole row; every lane of the wave
 // calls it (the refinements use the lanes), lane 0 writes.
-template <bool BF16>
+template <bool BF16, bool EXT>
 __device__ void finalize_row(const VerifyLaunch &p, int64_t r, const Partial &t, int lane) {
+  constexpr int N = Chunk<BF16>::N;
   const size_t row_bytes = static_cast<size_t>(p.ld) * (BF16 ? 2 : 4);
   const u32x4 *ra = reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.va) + r * row_bytes);
   const u32x4 *rb = reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.vb) + r * row_bytes);
   const dv_row_stats &o = p.out;
-  const bool want_am = o.argmax_v || o.argmax_d || (p.greedy && (o.tok_v || o.tok_d));
+  const bool want_tok_d = o.tok_d || o.p_tok_d;
+  const bool want_am = o.argmax_v || o.argmax_d || (p.greedy && (o.tok_v || want_tok_d));
   int32_t am_v = 0, am_d = 0, tk_v = 0, tk_d = 0;
   if (want_am) {
-    am_v = refine_in_chunk<BF16, false>(ra, t.cm_v, t.m_v, p.vocab, 0.0f, 0u, lane);
-    am_d = refine_in_chunk<BF16, false>(rb, t.cm_d, t.m_d, p.vocab, 0.0f, 0u, lane);
+    am_v = refine_in_chunk<BF16, false, EXT>(ra, t.cm_v, t.m_v, p.vocab, 0.0f, 0u, lane);
+    am_d = refine_in_chunk<BF16, false, EXT>(rb, t.cm_d, t.m_d, p.vocab, 0.0f, 0u, lane);
   }
-  if (o.tok_v || o.tok_d) {
+  if (o.tok_v || want_tok_d) {
     if (p.greedy) {
       tk_v = am_v;
       tk_d = am_d;
     } else {
       const uint32_t key = row_key(p.seed_b, position_of(p, r));
-      tk_v = refine_in_chunk<BF16, true>(ra, t.cs_v, t.s_v, p.vocab, p.cT, key, lane);
-      tk_d = refine_in_chunk<BF16, true>(rb, t.cs_d, t.s_d, p.vocab, p.cT, key, lane);
+      if (o.tok_v) tk_v = refine_in_chunk<BF16, true, EXT>(ra, t.cs_v, t.s_v, p.vocab, p.cT, key, lane);
+      if (want_tok_d) tk_d = refine_in_chunk<BF16, true, EXT>(rb, t.cs_d, t.s_d, p.vocab, p.cT, key, lane);
     }
+  }
+  // the verifier's logit at the drafter's token
+  float x_tok = 0.0f;
+  if (o.p_tok_d && tk_d >= 0) {
+    float x[N];
+    widen<BF16>(read_chunk<BF16, EXT>(ra + tk_d / N), x);
+    x_tok = x[0];
+#pragma unroll
+    for (int j = 1; j < N; ++j) x_tok = (tk_d % N == j) ? x[j] : x_tok;
   }
   if (lane != 0) return;
   const double S_v = t.S_v, S_d = t.S_d;
@@ -628,6 +687,11 @@ __device__ void finalize_row(const VerifyLaunch &p, int64_t r, const Partial &t,
   kl = kl < 0.0 ? 0.0 : kl;
   ent = ent < 0.0 ? 0.0 : ent;
   conf = conf > 1.0 ? 1.0 : conf;
+  if (p.neg_inf) {
+    // a divergence this large only comes from mass where the other model
+    // has a -inf logit (raised to -2^100): it is +inf
+    if (kl >= 0x1p64) kl = INFINITY;
+  }
   if (o.lse_v) o.lse_v[r] = static_cast<float>(lse_v);
   if (o.lse_d) o.lse_d[r] = static_cast<float>(lse_d);
   if (o.kl) o.kl[r] = static_cast<float>(kl);
@@ -637,6 +701,16 @@ __device__ void finalize_row(const VerifyLaunch &p, int64_t r, const Partial &t,
   if (o.argmax_d) o.argmax_d[r] = am_d;
   if (o.tok_v) o.tok_v[r] = tk_v;
   if (o.tok_d) o.tok_d[r] = tk_d;
+  if constexpr (EXT) {
+    if (o.kl_rev) {
+      // KL(p_d || p_v) = sum p_d (b - a) - (lse_d - lse_v)
+      double klr = -static_cast<double>(t.D_d) / S_d - kLn2 * ((rho_d - rho_v) + (l2d - l2v));
+      klr = klr < 0.0 ? 0.0 : klr;
+      if (p.neg_inf && klr >= 0x1p64) klr = INFINITY;
+      o.kl_rev[r] = static_cast<float>(klr);
+    }
+  }
+  if (o.p_tok_d) o.p_tok_d[r] = tk_d >= 0 ? static_cast<float>(exp(static_cast<double>(x_tok) - lse_v)) : 0.0f;
 }
 
 template <bool BF16>
@@ -656,7 +730,7 @@ struct WaveLds {
 
 // One wave per (row, slice); the split slices of a row are consecutive waves
 // of one workgroup and are combined through LDS by the row's first wave.
-template <bool BF16, int MODE>
+template <bool BF16, int MODE, bool EXT>
 __global__ __launch_bounds__(1024) void verify_rows_kernel(VerifyLaunch p) {
   extern __shared__ WaveLds lds[];
   // the wave index is uniform across the wave: keep it (and all row
@@ -680,12 +754,12 @@ __global__ __launch_bounds__(1024) void verify_rows_kernel(VerifyLaunch p) {
     const int32_t pos = MODE == kGreedy ? 0 : position_of(p, r);
     const uint32_t key = MODE == kGreedy ? 0u : row_key(p.seed_b, pos);
     const float *gcm = MODE == kTableBound ? p.noise_cmax + static_cast<int64_t>(pos) * p.cmax_ld : nullptr;
-    scan_slice<BF16, MODE>(st, ra, rb, c0, c1, nfull, nvalid_tail, p.cT, MODE == kHashBound ? key_in_vgpr(key) : key, gcm,
+    scan_slice<BF16, MODE, EXT>(st, ra, rb, c0, c1, nfull, nvalid_tail, p.cT, MODE == kHashBound ? key_in_vgpr(key) : key, gcm,
                            MODE == kGreedy ? nullptr : &lds[wave].q, lane);
   }
   const Partial t = wave_reduce(st);
   if (split == 1) {
-    if (live) finalize_row<BF16>(p, r, t, lane);
+    if (live) finalize_row<BF16, EXT>(p, r, t, lane);
     return;
   }
   if (lane == 0) lds[wave].part = t;
@@ -700,6 +774,7 @@ __global__ __launch_bounds__(1024) void verify_rows_kernel(VerifyLaunch p) {
     m.S_v = x.S_v;
     m.W_v = x.W_v;
     m.D_v = x.D_v;
+    m.D_d = x.D_d;
     m.rho_d = x.rho_d;
     m.S_d = x.S_d;
     m.m_v = x.m_v;
@@ -711,7 +786,7 @@ __global__ __launch_bounds__(1024) void verify_rows_kernel(VerifyLaunch p) {
     m.cs_v = x.cs_v;
     m.cs_d = x.cs_d;
   }
-  finalize_row<BF16>(p, r, wave_reduce(m), lane);
+  finalize_row<BF16, EXT>(p, r, wave_reduce(m), lane);
 }
 
 // Chunk-max noise table: entry (q, c) bounds the noise of position q over the
@@ -733,13 +808,19 @@ __global__ __launch_bounds__(256) void noise_cmax_kernel(uint32_t seed_b, uint32
   cmax[t] = noise_bound_of_word(hm);
 }
 
-template <bool BF16, int MODE>
+template <bool BF16, int MODE, bool EXT>
 hipError_t launch_rows(const VerifyLaunch &p, hipStream_t stream) {
   const unsigned blocks = static_cast<unsigned>((p.rows + p.rows_per_block - 1) / p.rows_per_block);
   const int waves = p.rows_per_block * p.split;
   const size_t lds = MODE == kGreedy ? (p.split > 1 ? waves * sizeof(WaveLds) : 0) : waves * sizeof(WaveLds);
-  hipLaunchKernelGGL((verify_rows_kernel<BF16, MODE>), dim3(blocks), dim3(64 * waves), lds, stream, p);
+  hipLaunchKernelGGL((verify_rows_kernel<BF16, MODE, EXT>), dim3(blocks), dim3(64 * waves), lds, stream, p);
   return hipGetLastError();
+}
+
+template <bool BF16, bool EXT>
+hipError_t launch_noise(const VerifyLaunch &p, hipStream_t stream) {
+  if (p.noise_cmax) return launch_rows<BF16, kTableBound, EXT>(p, stream);
+  return p.greedy ? launch_rows<BF16, kGreedy, EXT>(p, stream) : launch_rows<BF16, kHashBound, EXT>(p, stream);
 }
 
 template <bool BF16>
@@ -751,9 +832,9 @@ hipError_t launch_typed(const VerifyLaunch &p, hipStream_t stream) {
                        static_cast<uint32_t>(p.cmax_ld), p.vocab, p.noise_cmax);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_rows<BF16, kTableBound>(p, stream);
   }
-  return p.greedy ? launch_rows<BF16, kGreedy>(p, stream) : launch_rows<BF16, kHashBound>(p, stream);
+  // the extended pass: -inf logits and the reverse divergence
+  return (p.neg_inf || p.out.kl_rev) ? launch_noise<BF16, true>(p, stream) : launch_noise<BF16, false>(p, stream);
 }
 
 }  // namespace

@@ -22,9 +22,13 @@ DV_OK, DV_ERR_NULL, DV_ERR_SHAPE, DV_ERR_DTYPE, DV_ERR_ALIGN, DV_ERR_ARG, \
 DV_FP32, DV_BF16 = 0, 1
 DV_NONE, DV_KEEP, DV_REPLACE, DV_REMASK = 0, 1, 2, 3
 DV_RULE_TRUST, DV_RULE_KL, DV_RULE_CONF, DV_RULE_KL_OR_CONF, DV_RULE_COVER, DV_RULE_COUPLED_ACCEPT = range(6)
-RULES = {"TRUST": 0, "KL": 1, "CONF": 2, "KL_OR_CONF": 3, "COVER": 4, "COUPLED_ACCEPT": 5}
-STAT_FIELDS = ("lse_v", "lse_d", "kl", "entropy", "conf", "argmax_v", "argmax_d", "tok_v", "tok_d")
-_FLOAT_FIELDS = {"lse_v", "lse_d", "kl", "entropy", "conf"}
+RULES = {"TRUST": 0, "KL": 1, "CONF": 2, "KL_OR_CONF": 3, "COVER": 4, "COUPLED_ACCEPT": 5, "CONF_DRAFT": 6}
+# every member of dv_row_stats, in order
+STAT_FIELDS = ("lse_v", "lse_d", "kl", "entropy", "conf", "argmax_v", "argmax_d", "tok_v", "tok_d", "kl_rev", "p_tok_d")
+# what dv_verify_rows computes unless asked otherwise (kl_rev selects the extended pass)
+CORE_FIELDS = STAT_FIELDS[:9]
+DV_LOGITS_NEG_INF = 1
+_FLOAT_FIELDS = {"lse_v", "lse_d", "kl", "entropy", "conf", "kl_rev", "p_tok_d"}
 
 
 class DVError(RuntimeError):
@@ -35,7 +39,7 @@ class DVError(RuntimeError):
 
 class dv_logits(ctypes.Structure):
     _fields_ = [("verifier", ctypes.c_void_p), ("drafter", ctypes.c_void_p), ("dtype", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("rows", ctypes.c_int64), ("vocab", ctypes.c_int64),
+                ("flags", ctypes.c_int32), ("rows", ctypes.c_int64), ("vocab", ctypes.c_int64),
                 ("ld", ctypes.c_int64)]
 
 
@@ -152,7 +156,7 @@ def _logits_desc(verifier, drafter, vocab):
     if vocab > width:
         raise ValueError(f"vocab {vocab} exceeds the row width {width}")
     return dv_logits(verifier=verifier.data_ptr(), drafter=drafter.data_ptr(),
-                     dtype=DV_BF16 if verifier.dtype == torch.bfloat16 else DV_FP32, reserved=0,
+                     dtype=DV_BF16 if verifier.dtype == torch.bfloat16 else DV_FP32, flags=0,
                      rows=rows, vocab=vocab, ld=ld)
 
 
@@ -188,10 +192,12 @@ def dv_verify_workspace_bytes(verifier, drafter, temperature=0.0, seed=0, pos=No
 
 
 def dv_verify_rows(verifier, drafter, temperature=0.0, seed=0, pos=None, pos_period=0, *, vocab=None,
-                   outputs=STAT_FIELDS, out=None, workspace=None, tuning=None):
+                   outputs=CORE_FIELDS, out=None, workspace=None, tuning=None, neg_inf=False):
     """Row statistics of [rows, ld] verifier/drafter logits. Returns a dict of
-    tensors (float32 for lse_v, lse_d, kl, entropy, conf; int32 for the rest)."""
+    tensors (float32 for lse_v, lse_d, kl, entropy, conf, kl_rev, p_tok_d; int32
+    for the rest). neg_inf: the logits may hold -inf (DV_LOGITS_NEG_INF)."""
     d = _logits_desc(verifier, drafter, vocab)
+    d.flags = DV_LOGITS_NEG_INF if neg_inf else 0
     n = _noise_desc(temperature, seed, pos, pos_period)
     t = _tuning_desc(tuning)
     rows, dev = d.rows, verifier.device

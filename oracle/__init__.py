@@ -33,12 +33,14 @@ Modules:
   commit list it yields.
 * ``attention`` COVER's influence d_in and drift sensitivity d_out from
   attention probabilities.
+* ``dual_view`` COVER's attention with the KV-cache override of seed columns
+  and the diagonal correction.
 
 Every function is pinned by tests under ``tests/`` against closed forms,
 library routines, invariants or brute force; none of the pages prints a
 worked example, so no end-to-end value is pinned by the pages themselves.
 """
 
-from . import rowstats, noise, decide, select, tree, attention  # noqa: F401
+from . import rowstats, noise, decide, select, tree, attention, dual_view  # noqa: F401
 
-__all__ = ["rowstats", "noise", "decide", "select", "tree", "attention"]
+__all__ = ["rowstats", "noise", "decide", "select", "tree", "attention", "dual_view"]

@@ -307,6 +307,38 @@ dv_status dv_influence_drift(const dv_attention *att, const uint8_t *query_maske
                              float *d_in, float *d_out, void *workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/* Shape of dv_dual_view_attention's input. */
+typedef struct dv_dual_view_args {
+  int64_t nseq;      /* 0..65535 */
+  int64_t heads;     /* query heads, 1..65535 */
+  int64_t kv_heads;  /* key/value heads, dividing heads (grouped-query attention) */
+  int64_t len;       /* positions, a multiple of 32, 32..65536 */
+  int64_t head_dim;  /* 64 or 128 */
+  float scale;       /* score scale, finite (usually 1/sqrt(head_dim)) */
+  int32_t reserved;
+} dv_dual_view_args;
+
+/* COVER's dual-view attention ([COVER] "Method: COVER" part 1, Dual-View Feed
+ * Forward through KV cache override): queries, keys and values come from the
+ * input with the seed positions masked; every seed column is read from the KV
+ * cache of the previous step (k_prev, v_prev), except by the seed's own query,
+ * whose diagonal reads the current key and value (leave-one-out, no self
+ * leakage); the softmax renormalizes over the corrected row:
+ *   k_eff(i, j) = k_prev[j] if seed[j] and j != i, else k_cur[j] (likewise v)
+ *   out_i = sum_j softmax_j(scale <q_i, k_eff(i, j)>) v_eff(i, j)
+ * Bidirectional (no causal mask). Query head h reads key/value head
+ * h / (heads / kv_heads).
+ * q: device bf16 [nseq][heads][len][head_dim]; k_cur, v_cur, k_prev, v_prev:
+ * device bf16 [nseq][kv_heads][len][head_dim]; seed: device uint8 [nseq][len]
+ * (nonzero = seed); out: device float32 [nseq][heads][len][head_dim]. All
+ * contiguous and 16-byte aligned. Products on the matrix cores in bf16 with
+ * float32 accumulation; the probabilities are rounded to bf16 for the second
+ * product (relative error of the output about 2^-9 of the values' scale).
+ * Errors: DV_ERR_NULL, DV_ERR_SHAPE, DV_ERR_ALIGN, DV_ERR_ARG, DV_ERR_HIP. */
+dv_status dv_dual_view_attention(const dv_dual_view_args *args, const void *q, const void *k_cur,
+                                 const void *v_cur, const void *k_prev, const void *v_prev,
+                                 const uint8_t *seed, float *out, hipStream_t stream);
+
 /* The noise hash words h[r][i] (uint32, device [rows][vocab]) for the
  * positions described as in dv_noise. For testing the noise generator bit
  * for bit. Errors: DV_ERR_NULL, DV_ERR_SHAPE. */

@@ -31,7 +31,8 @@ def test_exports_every_declared_function(lib):
     names = _declared_functions()
     assert names == sorted(["dv_verify_workspace_bytes", "dv_verify_rows", "dv_decide", "dv_seed_score",
                            "dv_select_topk", "dv_tree_accept", "dv_influence_drift_workspace_bytes",
-                           "dv_influence_drift", "dv_debug_hash", "dv_status_str", "dv_last_error", "dv_version"])
+                           "dv_influence_drift", "dv_dual_view_attention", "dv_debug_hash", "dv_status_str",
+                           "dv_last_error", "dv_version"])
     for n in names:
         assert hasattr(lib, n), n
     assert lib.dv_version() == 1
@@ -229,3 +230,22 @@ def test_influence_validation_and_workspace(lib):
     assert call(_att(), ws_bytes=16) == B.DV_ERR_WORKSPACE
     assert call(_att(), ws=FAKE + 16) == B.DV_ERR_ALIGN
     assert call(_att(nseq=0, probs=None), qm=None, nc=None, ws=None) == B.DV_OK   # nothing to do
+
+
+def test_dual_view_validation(lib):
+    def call(args, ptr=FAKE, seed=FAKE):
+        return lib.dv_dual_view_attention(ctypes.byref(args) if args is not None else None, ptr, ptr, ptr, ptr, ptr,
+                                          seed, ptr, None)
+    A = lambda **kw: B.dv_dual_view_args(**{**dict(nseq=1, heads=4, kv_heads=2, len=64, head_dim=128, scale=0.1,
+                                                   reserved=0), **kw})
+    assert call(None) == B.DV_ERR_NULL
+    assert call(A(heads=4, kv_heads=3)) == B.DV_ERR_SHAPE
+    assert call(A(len=48)) == B.DV_ERR_SHAPE
+    assert call(A(len=0)) == B.DV_ERR_SHAPE
+    assert call(A(head_dim=96)) == B.DV_ERR_SHAPE
+    assert call(A(nseq=-1)) == B.DV_ERR_SHAPE
+    assert call(A(scale=float("nan"))) == B.DV_ERR_ARG
+    assert call(A(), ptr=None) == B.DV_ERR_NULL
+    assert call(A(), seed=None) == B.DV_ERR_NULL
+    assert call(A(), ptr=FAKE + 8) == B.DV_ERR_ALIGN
+    assert call(A(nseq=0), ptr=None, seed=None) == B.DV_OK

@@ -345,6 +345,40 @@ dv_status dv_influence_drift(const dv_attention *att, const uint8_t *query_maske
   return hip_status(dv::launch_influence(p, stream), "dv_influence_drift launch");
 }
 
+dv_status dv_dual_view_attention(const dv_dual_view_args *a, const void *q, const void *k_cur, const void *v_cur,
+                                 const void *k_prev, const void *v_prev, const uint8_t *seed, float *out,
+                                 hipStream_t stream) {
+  if (!a) return fail(DV_ERR_NULL, "args is NULL");
+  if (a->nseq < 0 || a->nseq > 65535) return fail(DV_ERR_SHAPE, "nseq must be 0..65535");
+  if (a->heads < 1 || a->heads > 65535) return fail(DV_ERR_SHAPE, "heads must be 1..65535");
+  if (a->kv_heads < 1 || a->heads % a->kv_heads != 0) return fail(DV_ERR_SHAPE, "kv_heads must divide heads");
+  if (a->len < 32 || a->len > 65536 || a->len % 32 != 0) return fail(DV_ERR_SHAPE, "len must be a multiple of 32 in 32..65536");
+  if (a->head_dim != 64 && a->head_dim != 128) return fail(DV_ERR_SHAPE, "head_dim must be 64 or 128");
+  if (!std::isfinite(a->scale)) return fail(DV_ERR_ARG, "scale must be finite");
+  if (a->nseq == 0) return ok();
+  const void *ptrs[] = {q, k_cur, v_cur, k_prev, v_prev, out};
+  for (const void *ptr : ptrs) {
+    if (!ptr) return fail(DV_ERR_NULL, "an input or the output is NULL");
+    if (!aligned16(ptr)) return fail(DV_ERR_ALIGN, "tensors must be 16-byte aligned");
+  }
+  if (!seed) return fail(DV_ERR_NULL, "seed is NULL");
+  dv::DualViewLaunch p{};
+  p.q = static_cast<const uint16_t *>(q);
+  p.k_cur = static_cast<const uint16_t *>(k_cur);
+  p.v_cur = static_cast<const uint16_t *>(v_cur);
+  p.k_prev = static_cast<const uint16_t *>(k_prev);
+  p.v_prev = static_cast<const uint16_t *>(v_prev);
+  p.seed = seed;
+  p.out = out;
+  p.scale = a->scale;
+  p.head_dim = static_cast<int32_t>(a->head_dim);
+  p.nseq = a->nseq;
+  p.heads = a->heads;
+  p.kv_heads = a->kv_heads;
+  p.len = a->len;
+  return hip_status(dv::launch_dual_view(p, stream), "dv_dual_view_attention launch");
+}
+
 dv_status dv_tree_accept(const dv_tree_args *a, const int32_t *parent, const int32_t *node_pos,
                          const int32_t *node_tok, const uint8_t *root_masked, const float *conf,
                          const int32_t *tok_v, uint8_t *accepted, int32_t *depth, int32_t *best_node,

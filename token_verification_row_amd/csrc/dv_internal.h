@@ -133,6 +133,16 @@ struct InfluenceLaunch {
 };
 hipError_t launch_influence(const InfluenceLaunch &p, hipStream_t stream);
 
+struct DualViewLaunch {
+  const uint16_t *q, *k_cur, *v_cur, *k_prev, *v_prev;  // bf16 bits
+  const uint8_t *seed;
+  float *out;
+  float scale;
+  int32_t head_dim;  // 64 or 128
+  int64_t nseq, heads, kv_heads, len;
+};
+hipError_t launch_dual_view(const DualViewLaunch &p, hipStream_t stream);
+
 hipError_t launch_debug_hash(uint32_t seed_b, const int32_t *pos, int64_t pos_period, int64_t rows,
                              int64_t vocab, uint32_t *out, hipStream_t stream);
 

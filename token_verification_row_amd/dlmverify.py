@@ -66,6 +66,12 @@ class dv_attention(ctypes.Structure):
                 ("nseq", ctypes.c_int64), ("heads", ctypes.c_int64), ("len", ctypes.c_int64), ("ld", ctypes.c_int64)]
 
 
+class dv_dual_view_args(ctypes.Structure):
+    _fields_ = [("nseq", ctypes.c_int64), ("heads", ctypes.c_int64), ("kv_heads", ctypes.c_int64),
+                ("len", ctypes.c_int64), ("head_dim", ctypes.c_int64), ("scale", ctypes.c_float),
+                ("reserved", ctypes.c_int32)]
+
+
 class dv_tree_args(ctypes.Structure):
     _fields_ = [("ntrees", ctypes.c_int64), ("nodes", ctypes.c_int64), ("block_len", ctypes.c_int64)]
 
@@ -83,6 +89,7 @@ _SIGNATURES = {
     "dv_select_topk": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_int32, ctypes.c_float, _P, _P, _P, _P, _P]),
     "dv_tree_accept": (ctypes.c_int, [ctypes.POINTER(dv_tree_args)] + [_P] * 15),
+    "dv_dual_view_attention": (ctypes.c_int, [ctypes.POINTER(dv_dual_view_args)] + [_P] * 8),
     "dv_influence_drift_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(dv_attention), ctypes.POINTER(ctypes.c_size_t)]),
     "dv_influence_drift": (ctypes.c_int, [ctypes.POINTER(dv_attention), _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "dv_debug_hash": (ctypes.c_int, [ctypes.c_uint64, _P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P]),
@@ -389,6 +396,32 @@ def dv_influence_drift(probs, query_masked, new_cols, *, workspace=None):
                                              _ptr(d_out), ctypes.c_void_p(ws_ptr), avail, _stream_handle(dev)),
            "dv_influence_drift")
     return d_in, d_out
+
+
+def dv_dual_view_attention(q, k_cur, v_cur, k_prev, v_prev, seed, *, scale=None, out=None):
+    """COVER's dual-view attention. q: bf16 [nseq, heads, len, head_dim]; k_cur, v_cur, k_prev,
+    v_prev: bf16 [nseq, kv_heads, len, head_dim]; seed: uint8 [nseq, len]. Returns float32
+    [nseq, heads, len, head_dim]."""
+    for name, t in (("q", q), ("k_cur", k_cur), ("v_cur", v_cur), ("k_prev", k_prev), ("v_prev", v_prev)):
+        _need_cuda(t, name)
+        if t.dtype != torch.bfloat16 or t.dim() != 4 or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous bfloat16 [nseq, heads, len, head_dim] tensor")
+    B, H, L, D = q.shape
+    Hkv = k_cur.shape[1]
+    for t in (k_cur, v_cur, k_prev, v_prev):
+        if tuple(t.shape) != (B, Hkv, L, D):
+            raise ValueError("k/v tensors must be [nseq, kv_heads, len, head_dim] like each other and q")
+    _need_cuda(seed, "seed")
+    if seed.dtype != torch.uint8 or tuple(seed.shape) != (B, L) or not seed.is_contiguous():
+        raise TypeError("seed must be a contiguous uint8 [nseq, len] tensor")
+    if out is None:
+        out = torch.empty((B, H, L, D), dtype=torch.float32, device=q.device)
+    args = dv_dual_view_args(nseq=B, heads=H, kv_heads=Hkv, len=L, head_dim=D,
+                             scale=float(D ** -0.5 if scale is None else scale), reserved=0)
+    _check(load_library().dv_dual_view_attention(
+        ctypes.byref(args), _ptr(q), _ptr(k_cur), _ptr(v_cur), _ptr(k_prev), _ptr(v_prev), _ptr(seed), _ptr(out),
+        _stream_handle(q.device)), "dv_dual_view_attention")
+    return out
 
 
 def dv_debug_hash(seed, rows, vocab, *, pos=None, pos_period=0, device="cuda"):

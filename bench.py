@@ -100,6 +100,20 @@ def synthetic_tree(stats, nodes, block_len, dev):
             torch.ones((1, block_len), dtype=torch.uint8, device=dev))
 
 
+def synthetic_qkv(nseq, heads, kv_heads, length, head_dim, dev):
+    """(q, k_cur, v_cur, k_prev, v_prev, seed): standard-normal bf16 tensors drawn on the device and
+    10% seed positions."""
+    import torch
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(777)
+    q = torch.randn((nseq, heads, length, head_dim), generator=g, device=dev).to(torch.bfloat16)
+    kv = [torch.randn((nseq, kv_heads, length, head_dim), generator=g, device=dev).to(torch.bfloat16)
+          for _ in range(4)]
+    seed = (torch.rand((nseq, length), generator=g, device=dev) < 0.1).to(torch.uint8)
+    return (q, *kv, seed)
+
+
 def synthetic_attention(maps, length, dev):
     """(probs [1, maps, len, len] bf16, query_masked, new_cols): peaky softmax rows drawn on the device,
     about 40% of the queries masked and 20% of the columns newly written."""
@@ -143,6 +157,10 @@ def main() -> int:
     ap.add_argument("--influence", type=int, default=0, metavar="MAPS",
                     help="workload 3 only: compute d_in and d_out in the step from MAPS synthetic bf16 attention "
                          "maps of len x len (dv_influence_drift) and report that kernel's HBM rate")
+    ap.add_argument("--dual-view", action="store_true",
+                    help="add COVER's dual-view attention to the step (dv_dual_view_attention) over synthetic "
+                         "bf16 Q/K/V of the workload's sequences: 28 query heads, 4 key/value heads, head_dim 128, "
+                         "10%% seed positions; report its matrix-core rate")
     ap.add_argument("--tree", action="store_true",
                     help="workload 4 only: accept over a tree of the 64 candidate block states (dv_tree_accept) "
                          "instead of a prefix per candidate")
@@ -203,6 +221,11 @@ def main() -> int:
         att = synthetic_attention(args.influence, w.L, dev)
         att_ws = torch.empty(dv.dv_influence_drift_workspace_bytes(att[0]) + 256, dtype=torch.uint8, device=dev)
         att_ev = []
+    dv_in = None
+    if args.dual_view:
+        dv_in = synthetic_qkv(w.B, 28, 4, w.L, 128, dev)
+        dv_out = torch.empty((w.B, 28, w.L, 128), dtype=torch.float32, device=dev)
+        dv_ev = []
     tree = None
     if args.tree:
         if not w.group_len:
@@ -214,6 +237,14 @@ def main() -> int:
         """verify -> decide -> seed score -> select, with the workload's own rule and selection score."""
         a, b = inputs[i % copies]
         out = outs[i % 2]
+        if dv_in is not None:
+            if ev is not None:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            dv.dv_dual_view_attention(*dv_in, out=dv_out)
+            if ev is not None:
+                e1.record(stream)
+                dv_ev.append((e0, e1))
         if ev is not None:
             ev[0].record(stream)
         got = dv.dv_verify_rows(a, b, temperature=w.temperature, seed=w.seed, pos_period=period, out=out,
@@ -307,6 +338,13 @@ def main() -> int:
                      "bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
     }
+    if dv_in is not None:
+        dv_us = 1000.0 * float(np.mean([a.elapsed_time(b) for a, b in dv_ev]))
+        flop = 4.0 * w.B * 28 * w.L * w.L * 128
+        line["dual_view"] = {"nseq": w.B, "heads": 28, "kv_heads": 4, "len": w.L, "head_dim": 128, "avg_us": dv_us,
+                             "flop_per_launch": flop, "achieved_TFLOPs": flop / (dv_us * 1e-6) / 1e12,
+                             "peak_TFLOPs": 2500.0, "frac": flop / (dv_us * 1e-6) / 1e12 / 2500.0}
+        line["config"]["step"] = "dv_dual_view_attention + " + line["config"]["step"]
     if att is not None:
         att_us = 1000.0 * float(np.mean([a.elapsed_time(b) for a, b in att_ev]))
         att_bytes = att[0].numel() * 2 + 2 * 4 * R

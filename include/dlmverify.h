@@ -334,6 +334,9 @@ typedef struct dv_dual_view_args {
  * contiguous and 16-byte aligned. Products on the matrix cores in bf16 with
  * float32 accumulation; the probabilities are rounded to bf16 for the second
  * product (relative error of the output about 2^-9 of the values' scale).
+ * Inputs must be finite, and values below 2^100 in magnitude (the float32
+ * accumulator holds up to 2^24 weighted values). DV_ERR_SHAPE also when nseq * heads * ceil(len /
+ * 128) exceeds 2^24 (one workgroup per 128 queries of a head).
  * Errors: DV_ERR_NULL, DV_ERR_SHAPE, DV_ERR_ALIGN, DV_ERR_ARG, DV_ERR_HIP. */
 dv_status dv_dual_view_attention(const dv_dual_view_args *args, const void *q, const void *k_cur,
                                  const void *v_cur, const void *k_prev, const void *v_prev,

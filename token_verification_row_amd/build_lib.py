@@ -27,11 +27,12 @@ HIPCC_FLAGS = [
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
-# The verification kernels take finite logits only (documented in the header),
-# so their device code may assume no NaN: max() then needs no quieting of its
-# operands.
+# The verification and dual-view kernels take finite inputs only (documented in
+# the header), so their device code may assume no NaN: max() then needs no
+# quieting of its operands.
 PER_SOURCE_FLAGS = {
     "verify.hip": ["-Xarch_device", "-fno-honor-nans"],
+    "dual_view.hip": ["-Xarch_device", "-fno-honor-nans"],
 }
 
 

@@ -355,6 +355,8 @@ dv_status dv_dual_view_attention(const dv_dual_view_args *a, const void *q, cons
   if (a->len < 32 || a->len > 65536 || a->len % 32 != 0) return fail(DV_ERR_SHAPE, "len must be a multiple of 32 in 32..65536");
   if (a->head_dim != 64 && a->head_dim != 128) return fail(DV_ERR_SHAPE, "head_dim must be 64 or 128");
   if (!std::isfinite(a->scale)) return fail(DV_ERR_ARG, "scale must be finite");
+  if ((a->len + 127) / 128 * a->heads * a->nseq > (int64_t{1} << 24))
+    return fail(DV_ERR_SHAPE, "nseq * heads * ceil(len / 128) must be at most 2^24");
   if (a->nseq == 0) return ok();
   const void *ptrs[] = {q, k_cur, v_cur, k_prev, v_prev, out};
   for (const void *ptr : ptrs) {

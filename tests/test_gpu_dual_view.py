@@ -81,3 +81,26 @@ def test_leave_one_out_on_gpu():
         # row 37 keeps (up to the bf16 rounding of its own weight), the others move
         np.testing.assert_allclose(moved[:, :, 37], base[:, :, 37], atol=4e-3 * 8)
         assert np.abs(moved[:, :, :37] - base[:, :, :37]).max() > 1e-3
+
+
+def test_bench_shape_sampled_heads():
+    """The shape and launch the benchmark times (32 sequences x 28 heads over 4
+    key/value heads, 1024 positions, head_dim 128, 10% seeds), checked on a
+    sample of (sequence, head) pairs against the oracle run on those heads."""
+    print("case: dual view 32x28x1024x128 sampled heads", flush=True)
+    dev = _dev()
+    B, H, Hkv, L, D = 32, 28, 4, 1024, 128
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    q = torch.randn((B, H, L, D), generator=g, device=dev).to(torch.bfloat16)
+    kv = [torch.randn((B, Hkv, L, D), generator=g, device=dev).to(torch.bfloat16) for _ in range(4)]
+    sd = (torch.rand((B, L), generator=g, device=dev) < 0.1).to(torch.uint8)
+    out = dv.dv_dual_view_attention(q, *kv, sd, scale=D ** -0.5)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (13, 6), (31, 27), (20, 15)):
+        gh = h // (H // Hkv)
+        host = lambda t, i: t[b:b + 1, i:i + 1].float().cpu().numpy().astype(np.float64)
+        ref = ODV.dual_view_attention(host(q, h), *(host(t, gh) for t in kv), sd[b:b + 1].cpu().numpy(), D ** -0.5)
+        vmax = max(float(kv[1][b, gh].float().abs().max()), float(kv[3][b, gh].float().abs().max()))
+        got = out[b:b + 1, h:h + 1].cpu().numpy().astype(np.float64)
+        np.testing.assert_allclose(got, ref, rtol=4e-3, atol=4e-3 * vmax, err_msg=f"b={b} h={h}")

@@ -26,6 +26,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 STAT_BYTES_PER_ROW = 36      # 5 float32 + 4 int32 outputs
+EXT_STAT_BYTES_PER_ROW = 44  # + kl_rev and p_tok_d (float32)
 VERIFY_SOURCE = os.path.join(ROOT, "token_verification_row_amd", "csrc", "verify.hip")
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "verify_rows_traffic.json")
 
@@ -161,6 +162,9 @@ def main() -> int:
                     help="add COVER's dual-view attention to the step (dv_dual_view_attention) over synthetic "
                          "bf16 Q/K/V of the workload's sequences: 28 query heads, 4 key/value heads, head_dim 128, "
                          "10%% seed positions; report its matrix-core rate")
+    ap.add_argument("--extended", action="store_true",
+                    help="verify with the extended outputs (KL(p_d||p_v), p_v(tok_d)) and -inf logits allowed "
+                         "(the extended kernel instantiation)")
     ap.add_argument("--tree", action="store_true",
                     help="workload 4 only: accept over a tree of the 64 candidate block states (dv_tree_accept) "
                          "instead of a prefix per candidate")
@@ -207,7 +211,8 @@ def main() -> int:
     d_in = torch.from_numpy(np.ascontiguousarray(d_in_np, np.float32)).to(dev)
     d_out = torch.from_numpy(np.ascontiguousarray(d_out_np, np.float32)).to(dev)
     committed = torch.from_numpy(W.committed_rows(w)).to(dev) if w.n_committed else None
-    outs = [dv.dv_verify_rows(*inputs[0], temperature=w.temperature, seed=w.seed, pos_period=period)
+    vkw = {"outputs": dv.STAT_FIELDS, "neg_inf": True} if args.extended else {}
+    outs = [dv.dv_verify_rows(*inputs[0], temperature=w.temperature, seed=w.seed, pos_period=period, **vkw)
             for _ in range(2)]
     seq_len = w.group_len or w.L
     nseq = R // seq_len
@@ -247,7 +252,7 @@ def main() -> int:
                 dv_ev.append((e0, e1))
         if ev is not None:
             ev[0].record(stream)
-        got = dv.dv_verify_rows(a, b, temperature=w.temperature, seed=w.seed, pos_period=period, out=out,
+        got = dv.dv_verify_rows(a, b, temperature=w.temperature, seed=w.seed, pos_period=period, out=out, **vkw,
                                 workspace=out.get("_workspace"))
         if ev is not None:
             ev[1].record(stream)
@@ -294,7 +299,7 @@ def main() -> int:
     verify_ms = [s.elapsed_time(e) for s, e in events]
     ms_per_step = ms_total / args.steps
     verify_us = 1000.0 * float(np.mean(verify_ms))
-    alg_bytes = 2 * R * V * w.elt + STAT_BYTES_PER_ROW * R
+    alg_bytes = 2 * R * V * w.elt + (EXT_STAT_BYTES_PER_ROW if args.extended else STAT_BYTES_PER_ROW) * R
     achieved = alg_bytes / (verify_us * 1e-6) / 1e9
 
     cpu = None
@@ -332,12 +337,15 @@ def main() -> int:
                    "step": "dv_verify_rows + dv_seed_score + dv_select_topk + "
                            + ("dv_tree_accept" if tree is not None else "dv_decide")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(w.number),
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None if args.extended else measured_traffic(w.number),
                      "kernel": "dv_verify_rows (noise table when rows share positions + streaming verify kernel)",
                      "avg_us": verify_us,
                      "bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
     }
+    if args.extended:
+        line["config"]["outputs"] = ("extended: 11 statistics per row incl. KL(p_d||p_v) and p_v(tok_d), "
+                                     "-inf logits allowed")
     if dv_in is not None:
         dv_us = 1000.0 * float(np.mean([a.elapsed_time(b) for a, b in dv_ev]))
         flop = 4.0 * w.B * 28 * w.L * w.L * 128

@@ -339,3 +339,29 @@ def test_neg_inf_logits(dtype):
         assert np.isinf(got["kl_rev"][4:8]).all() and np.isfinite(got["kl_rev"][:4]).all()
         assert got["argmax_v"][8] == 17 and got["argmax_v"][9] == V - 1 and got["tok_d"][9] == V - 1
         assert got["conf"][8] == 1.0
+
+
+def test_extended_workload_spot_tree_full_size():
+    """The extended pass as `bench.py --extended` launches it (all eleven outputs, -inf allowed) at workload 4's
+    full size, with masked vocabulary entries (-inf) written into some rows of both models, on sampled rows."""
+    w = W.workload(4)
+    print(f"case: workload 4 ({w.name}) full size, extended pass with -inf entries", flush=True)
+    dev = _dev()
+    a, b = W.make_logits_torch(w, dev)
+    rng = np.random.default_rng(41)
+    masked = _sample_rows(w.rows, 16, 7)
+    for r in masked:                                  # a block of masked entries and scattered ones
+        cols_a = np.concatenate([np.arange(1000, 1000 + 4096), rng.choice(w.V, 64, replace=False)])
+        cols_b = rng.choice(w.V, 128, replace=False)
+        a[int(r), torch.as_tensor(cols_a, device=dev)] = float("-inf")
+        b[int(r), torch.as_tensor(cols_b, device=dev)] = float("-inf")
+    got = to_numpy(dv.dv_verify_rows(a, b, temperature=w.temperature, seed=w.seed, pos_period=w.pos_period,
+                                     outputs=ALL_OUT, neg_inf=True))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([masked, np.arange(32 * 7, 32 * 8), _sample_rows(w.rows, 24, 8)]))
+    ref = oracle_rows(_bf16_rows_to_numpy(a, rows), _bf16_rows_to_numpy(b, rows), "bf16", w.temperature, w.seed,
+                      W.positions(w)[rows], neg_inf=True)
+    rep = compare_stats({k: v[rows] for k, v in got.items()}, ref, w.temperature, w.name + " extended")
+    print(rep, flush=True)
+    del a, b
+    torch.cuda.empty_cache()

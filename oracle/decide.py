@@ -4,7 +4,7 @@ Test infrastructure: see the package docstring for who may import this.
 
 Decision codes: 0 NONE (row not decided), 1 KEEP, 2 REPLACE, 3 REMASK.
 Rule codes: 0 TRUST, 1 KL, 2 CONF, 3 KL_OR_CONF, 4 COVER, 5 COUPLED_ACCEPT,
-6 CONF_DRAFT.
+6 CONF_DRAFT, 7 KL_STOCHASTIC.
 
 Sources and readings:
 
@@ -14,6 +14,15 @@ Sources and readings:
   also mentions remasking when the divergence is "probabilistically" high;
   that clause is not specified and is not part of this rule. REMASK iff
   kl > tau (strict), else KEEP.
+* KL_STOCHASTIC, item 2 with its "probabilistically high" clause: the page
+  gives no probability, so the reading is the plainest one that contains
+  the threshold clause: one Bernoulli draw per row that remasks with
+  probability min(1, kl / tau). Its uniform u comes from the same counter
+  hash as the Gumbel noise (DV_HASH_V1, see oracle.noise), keyed on the seed
+  and the row's position, at vocabulary index 2^32 - 1, which no token uses.
+  The decision is taken in float32, as the kernel takes it:
+  REMASK iff float32(u * tau) < float32(kl). kl > tau always remasks, since
+  u < 1; kl = 0 never does, since u > 0. Requires tau > 0.
 * CONF, item 3: low verifier confidence leads to remasking. REMASK iff
   conf < theta, else KEEP.
 * KL_OR_CONF: REMASK iff either of the two conditions holds.
@@ -49,19 +58,31 @@ from __future__ import annotations
 
 import numpy as np
 
+from . import noise
+
 NONE, KEEP, REPLACE, REMASK = 0, 1, 2, 3
-TRUST, KL, CONF, KL_OR_CONF, COVER, COUPLED_ACCEPT, CONF_DRAFT = 0, 1, 2, 3, 4, 5, 6
+TRUST, KL, CONF, KL_OR_CONF, COVER, COUPLED_ACCEPT, CONF_DRAFT, KL_STOCHASTIC = 0, 1, 2, 3, 4, 5, 6, 7
+REMASK_DRAW_INDEX = 2 ** 32 - 1   # the hash index of the remask draw
 
 __all__ = ["NONE", "KEEP", "REPLACE", "REMASK", "TRUST", "KL", "CONF", "KL_OR_CONF",
-           "COVER", "COUPLED_ACCEPT", "CONF_DRAFT", "decide", "accepted_prefix", "best_group"]
+           "COVER", "COUPLED_ACCEPT", "CONF_DRAFT", "KL_STOCHASTIC", "REMASK_DRAW_INDEX",
+           "remask_uniforms", "decide", "accepted_prefix", "best_group"]
+
+
+def remask_uniforms(seed: int, pos) -> np.ndarray:
+    """The uniform of each row's remask draw (float32, exact): DV_HASH_V1 at
+    (seed, pos[r], REMASK_DRAW_INDEX)."""
+    h = noise.hash_words(seed, np.asarray(pos), 1, start=REMASK_DRAW_INDEX)[:, 0]
+    return noise.uniforms(h).astype(np.float32)
 
 
 def decide(rule: int, stats: dict, *, tau_kl: float = 0.0, conf_thr: float = 0.0,
-           mask_token: int = -1, subject=None, cur_tok=None, group_len: int = 0):
+           mask_token: int = -1, subject=None, cur_tok=None, group_len: int = 0, seed: int = 0, pos=None):
     """Apply ``rule`` to every row. Returns (decision uint8, out_tok int32).
 
     ``stats`` holds the row statistics needed by the rule (kl, conf, tok_v,
-    tok_d), as float64 / int arrays of length R.
+    tok_d), as float64 / int arrays of length R. ``seed`` and ``pos`` (int32
+    positions, default the row index) key the draws of KL_STOCHASTIC.
     """
     rule = int(rule)
     cur = np.asarray(stats["tok_d"] if cur_tok is None else cur_tok).astype(np.int32)
@@ -76,6 +97,13 @@ def decide(rule: int, stats: dict, *, tau_kl: float = 0.0, conf_thr: float = 0.0
             remask |= np.asarray(stats["kl"], dtype=np.float64) > tau_kl
         if rule in (CONF, KL_OR_CONF):
             remask |= np.asarray(stats["conf"], dtype=np.float64) < conf_thr
+        dec[subj] = np.where(remask[subj], REMASK, KEEP)
+    elif rule == KL_STOCHASTIC:
+        if not tau_kl > 0:
+            raise ValueError("KL_STOCHASTIC needs tau_kl > 0")
+        kl = np.asarray(stats["kl"]).astype(np.float32)
+        u = remask_uniforms(seed, np.arange(n) if pos is None else pos)
+        remask = (u * np.float32(tau_kl)).astype(np.float32) < kl
         dec[subj] = np.where(remask[subj], REMASK, KEEP)
     elif rule == CONF_DRAFT:
         p_tok = np.asarray(stats["p_tok"], dtype=np.float64)

@@ -203,3 +203,53 @@ def test_conf_draft_truth_table():
     assert list(dec) == [M, K, K, M] and list(out) == [-2, 4, 5, -2]
     dec, _ = D.decide(D.CONF_DRAFT, st, conf_thr=0.9, subject=[1, 0, 1, 0])
     assert list(dec) == [M, N, K, N]
+
+
+# --------------------------------------------- stochastic KL remasking ----
+
+def _kl_stats(kl):
+    kl = np.asarray(kl, np.float64)
+    return {"kl": kl, "tok_d": np.zeros(len(kl), np.int32)}
+
+
+def test_kl_stochastic_contains_the_threshold_rule():
+    # kl > tau always remasks (u < 1), kl = 0 never does (u > 0): the threshold clause of item 2
+    n = 5000
+    for seed in (0, 1, 2 ** 40 + 7):
+        above = D.decide(D.KL_STOCHASTIC, _kl_stats(np.full(n, 0.1000001)), tau_kl=0.1, seed=seed)[0]
+        assert (above == D.REMASK).all()
+        zero = D.decide(D.KL_STOCHASTIC, _kl_stats(np.zeros(n)), tau_kl=0.1, seed=seed)[0]
+        assert (zero == D.KEEP).all()
+
+
+@pytest.mark.parametrize("frac", [0.05, 0.3, 0.7, 0.95])
+def test_kl_stochastic_remask_frequency(frac):
+    # below the threshold a row remasks with probability kl / tau: binomial bound at 5 sigma
+    n, tau = 40000, 0.2
+    dec = D.decide(D.KL_STOCHASTIC, _kl_stats(np.full(n, frac * tau)), tau_kl=tau, seed=11)[0]
+    got = (dec == D.REMASK).mean()
+    assert abs(got - frac) <= 5 * np.sqrt(frac * (1 - frac) / n)
+
+
+def test_kl_stochastic_draws_are_uniform_and_keyed_by_position():
+    from scipy import stats as sst
+    pos = np.arange(50000, dtype=np.int32)
+    u = D.remask_uniforms(5, pos).astype(np.float64)
+    assert (u > 0).all() and (u < 1).all()
+    assert sst.kstest(u, "uniform").pvalue > 1e-4
+    # the draw belongs to (seed, position), not to the row: permuting rows with their positions permutes decisions
+    rng = np.random.default_rng(0)
+    kl = rng.random(4096) * 0.1
+    p = rng.permutation(4096)
+    d0 = D.decide(D.KL_STOCHASTIC, _kl_stats(kl), tau_kl=0.1, seed=9, pos=np.arange(4096))[0]
+    d1 = D.decide(D.KL_STOCHASTIC, _kl_stats(kl[p]), tau_kl=0.1, seed=9, pos=p)[0]
+    np.testing.assert_array_equal(d1, d0[p])
+    # another seed draws anew; the draw is not the Gumbel noise of any token of the row
+    assert (D.decide(D.KL_STOCHASTIC, _kl_stats(kl), tau_kl=0.1, seed=10)[0] != d0).mean() > 0.2
+    from oracle import noise as N
+    assert np.abs(np.corrcoef(u[:4096], N.uniforms(N.hash_words(5, pos[:4096], 1, start=0)[:, 0]))[0, 1]) < 0.05
+
+
+def test_kl_stochastic_needs_positive_tau():
+    with pytest.raises(ValueError):
+        D.decide(D.KL_STOCHASTIC, _kl_stats([0.1]), tau_kl=0.0)

@@ -170,8 +170,16 @@ typedef enum dv_rule {
                                  leading rows whose tok_v equals the current token,
                                  REPLACE the first disagreeing row with tok_v, REMASK
                                  the rows after it */
-  DV_RULE_CONF_DRAFT = 6      /* [DualDiffusion] §2 item 3 read as the verifier's confidence
+  DV_RULE_CONF_DRAFT = 6,     /* [DualDiffusion] §2 item 3 read as the verifier's confidence
                                  in the drafted token: REMASK iff p_tok_d < conf_thr */
+  DV_RULE_KL_STOCHASTIC = 7   /* [DualDiffusion] §2 item 2 with its "probabilistically high"
+                                 clause, read as one Bernoulli draw per row remasking with
+                                 probability min(1, kl / tau_kl): REMASK iff the float32
+                                 product u * tau_kl < kl, where u = (2 (h >> 9) + 1) 2^-24
+                                 and h is the noise hash word (DV_HASH_V1, as in dv_noise)
+                                 of (seed, the row's position) at index 2^32 - 1, which no
+                                 vocabulary entry uses. kl > tau_kl always remasks; kl = 0
+                                 never does. Needs tau_kl > 0. */
 } dv_rule;
 
 typedef struct dv_decide_args {
@@ -184,6 +192,12 @@ typedef struct dv_decide_args {
   int64_t group_len;   /* rows per candidate (consecutive rows, commit order); 0 = none.
                           Required (> 0, dividing rows) for COUPLED_ACCEPT and for
                           prefix_len / best_group. */
+  /* KL_STOCHASTIC only: the draws are keyed like dv_noise (seed; position pos[r]
+     when pos is non-NULL, device int32 [rows]; else r % pos_period when
+     pos_period > 0; else r). */
+  uint64_t seed;
+  const int32_t *pos;
+  int64_t pos_period;  /* >= 0 */
 } dv_decide_args;
 
 /* Per-position decision ([DualDiffusion] §2 verification items 1-3;

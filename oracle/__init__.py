@@ -24,8 +24,9 @@ Modules:
   max-probability confidence and argmax, each by its textbook definition.
 * ``noise``     the counter-based hash that keys the shared Gumbel noise and
   the Gumbel-max tokens of both models under that shared noise.
-* ``decide``    the per-position rules (Trust, KL threshold, confidence
-  threshold, COVER's KEEP/REPLACE/REMASK, coupled-noise acceptance) and the
+* ``decide``    the per-position rules (Trust, KL threshold, KL with its
+  probabilistic clause, confidence threshold, confidence in the drafted
+  token, COVER's KEEP/REPLACE/REMASK, coupled-noise acceptance) and the
   accepted prefix per candidate.
 * ``select``    COVER's seed score and the per-sequence top-k / threshold
   selection.

@@ -151,6 +151,11 @@ def test_decide_validation(lib):
     assert _decide(lib, rule=B.DV_RULE_COVER, stats=B.dv_row_stats(conf=FAKE, tok_d=FAKE)) == B.DV_ERR_NULL
     assert _decide(lib, stats=B.dv_row_stats(kl=FAKE)) == B.DV_ERR_NULL                # no current token
     assert _decide(lib, rows=0) == B.DV_OK
+    assert _decide(lib, rule=B.DV_RULE_KL_STOCHASTIC, tau=0.0) == B.DV_ERR_ARG             # needs tau > 0
+    assert _decide(lib, rule=B.DV_RULE_KL_STOCHASTIC, stats=B.dv_row_stats(conf=FAKE, tok_d=FAKE)) == B.DV_ERR_NULL
+    a = B.dv_decide_args(rule=B.DV_RULE_KL, tau_kl=0.1, conf_thr=0.9, rows=8, pos_period=-1)
+    st = B.dv_row_stats(kl=FAKE, conf=FAKE, tok_v=FAKE, tok_d=FAKE)
+    assert lib.dv_decide(ctypes.byref(a), ctypes.byref(st), None, None, FAKE, FAKE, None, None, None) == B.DV_ERR_SHAPE
 
 
 def test_seed_score_select_hash_validation(lib):

@@ -68,6 +68,42 @@ def test_decide_exact(rows, group_len):
                         assert int(best.cpu()[0]) == odecide.best_group(rp)
 
 
+@pytest.mark.parametrize("rows,group_len", [(7, 0), (1000, 0), (960, 32), (2048, 32), (20000, 8)])
+def test_decide_kl_stochastic_exact(rows, group_len):
+    """KL remasking with its probabilistic clause: the hash-keyed draw and the float32 decision u * tau < kl,
+    bit for bit against the oracle, with rows placed exactly on and just above u * tau."""
+    print(f"case: decide KL_STOCHASTIC rows={rows} group_len={group_len}", flush=True)
+    dev = _dev()
+    rng = np.random.default_rng(7 * rows + group_len)
+    tau = np.float32(0.1)
+    pos_arr = rng.integers(-5, 1 << 20, rows).astype(np.int32)
+    for seed, pos, period in ((0, None, 0), (2 ** 40 + 7, pos_arr, 0), (3, None, 32)):
+        rpos = pos if pos is not None else ((np.arange(rows) % period) if period else np.arange(rows))
+        u = odecide.remask_uniforms(seed, rpos)
+        kl = rng.uniform(0, 0.15, rows).astype(np.float32)
+        on = (u * tau).astype(np.float32)
+        kl[::11] = on[::11]                                   # on the boundary: KEEP (strict)
+        kl[5::11] = np.nextafter(on[5::11], np.float32(1))    # just above: REMASK
+        kl[3::29] = 0.0
+        st = dict(kl=kl, tok_v=rng.integers(0, 3, rows).astype(np.int32), tok_d=rng.integers(0, 3, rows).astype(np.int32))
+        gst = {k: _t(v, dev) for k, v in st.items()}
+        subject = (rng.random(rows) < 0.8).astype(np.uint8)
+        for subj in (None, subject):
+            d, o, pre, _ = dv.dv_decide("KL_STOCHASTIC", gst, tau_kl=float(tau), mask_token=-9,
+                                        subject=None if subj is None else _t(subj, dev), group_len=group_len,
+                                        want_prefix=group_len > 0, seed=seed,
+                                        pos=None if pos is None else _t(pos, dev), pos_period=period)
+            rd, ro = odecide.decide(odecide.KL_STOCHASTIC, st, tau_kl=tau, mask_token=-9, subject=subj,
+                                    group_len=group_len, seed=seed, pos=rpos)
+            np.testing.assert_array_equal(d.cpu().numpy(), rd, err_msg=f"seed {seed} decisions")
+            np.testing.assert_array_equal(o.cpu().numpy(), ro, err_msg=f"seed {seed} out_tok")
+            if group_len:
+                np.testing.assert_array_equal(pre.cpu().numpy(), odecide.accepted_prefix(rd, group_len, subj))
+        on_boundary = np.zeros(rows, bool)
+        on_boundary[::11] = True
+        assert (rd[on_boundary & (subject != 0)] == odecide.KEEP).all()   # u * tau < kl is strict
+
+
 def test_decide_empty_best_group():
     print("case: decide empty", flush=True)
     dev = _dev()

@@ -216,8 +216,10 @@ dv_status dv_decide(const dv_decide_args *a, const dv_row_stats *stats, const ui
   if (!a || !stats) return fail(DV_ERR_NULL, "args or stats is NULL");
   if (a->rows < 0 || a->rows > kMaxIndex) return fail(DV_ERR_SHAPE, "rows out of range");
   if (a->group_len < 0 || a->group_len > kMaxIndex) return fail(DV_ERR_SHAPE, "group_len out of range");
-  if (a->rule < DV_RULE_TRUST || a->rule > DV_RULE_CONF_DRAFT) return fail(DV_ERR_ARG, "unknown rule %d", a->rule);
+  if (a->rule < DV_RULE_TRUST || a->rule > DV_RULE_KL_STOCHASTIC) return fail(DV_ERR_ARG, "unknown rule %d", a->rule);
   if (!finite(a->tau_kl) || !finite(a->conf_thr)) return fail(DV_ERR_ARG, "thresholds must be finite");
+  if (a->rule == DV_RULE_KL_STOCHASTIC && !(a->tau_kl > 0.0f)) return fail(DV_ERR_ARG, "KL_STOCHASTIC needs tau_kl > 0");
+  if (a->pos_period < 0) return fail(DV_ERR_SHAPE, "pos_period must be >= 0");
   const bool need_groups = a->rule == DV_RULE_COUPLED_ACCEPT || prefix_len || best_group;
   if (need_groups) {
     if (a->group_len <= 0) return fail(DV_ERR_SHAPE, "group_len must be > 0 for this request");
@@ -228,7 +230,8 @@ dv_status dv_decide(const dv_decide_args *a, const dv_row_stats *stats, const ui
     if (!cur_tok && !stats->tok_d) return fail(DV_ERR_NULL, "cur_tok and stats.tok_d are both NULL");
     switch (a->rule) {
       case DV_RULE_KL:
-        if (!stats->kl) return fail(DV_ERR_NULL, "rule KL needs stats.kl");
+      case DV_RULE_KL_STOCHASTIC:
+        if (!stats->kl) return fail(DV_ERR_NULL, "this KL rule needs stats.kl");
         break;
       case DV_RULE_CONF:
         if (!stats->conf) return fail(DV_ERR_NULL, "rule CONF needs stats.conf");
@@ -278,6 +281,9 @@ dv_status dv_decide(const dv_decide_args *a, const dv_row_stats *stats, const ui
   p.out_tok = out_tok;
   p.prefix_len = prefix_len;
   p.best_group = best_group;
+  p.seed_b = dv::seed_word(a->seed);
+  p.pos = a->pos;
+  p.pos_period = a->pos_period;
   return hip_status(dv::launch_decide(p, stream), "dv_decide launch");
 }
 

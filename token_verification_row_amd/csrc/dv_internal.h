@@ -86,6 +86,9 @@ struct DecideLaunch {
   const int32_t *cur_tok;
   uint8_t *decision;
   int32_t *out_tok, *prefix_len, *best_group;
+  uint32_t seed_b;  // KL_STOCHASTIC: the seed word B of the noise hash
+  const int32_t *pos;
+  int64_t pos_period;
 };
 hipError_t launch_decide(const DecideLaunch &p, hipStream_t stream);
 

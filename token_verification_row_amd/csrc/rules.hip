@@ -10,9 +10,18 @@ namespace dv {
 namespace {
 
 // ---------------------------------------------------------------- decide ----
+// The uniform of a row's remask draw: the noise hash of (seed, position) at
+// index 2^32 - 1, mapped like the Gumbel uniforms (exact in float32).
+__device__ __forceinline__ float remask_uniform(const DecideLaunch &p, int64_t r) {
+  const int64_t ps = p.pos ? p.pos[r] : (p.pos_period > 0 ? r % p.pos_period : r);
+  const uint32_t key = mix32(p.seed_b ^ mix32(static_cast<uint32_t>(ps) ^ kPosSalt));
+  const uint32_t h = mix32(key ^ (0xFFFFFFFFu * kIndexStep));
+  return static_cast<float>(2u * (h >> 9) + 1u) * 0x1p-24f;
+}
+
 // Rule for one row in isolation ([DualDiffusion] §2 "Verification algorithms"
-// items 1-3, item 3 also read as the confidence in the drafted token;
-// [COVER] §3 "Adaptive revision outcomes").
+// items 1-3, item 2 also with its probabilistic clause, item 3 also read as the
+// confidence in the drafted token; [COVER] §3 "Adaptive revision outcomes").
 __device__ __forceinline__ uint8_t rule_of_row(const DecideLaunch &p, int64_t r, int32_t cur) {
   switch (p.rule) {
     case DV_RULE_TRUST:
@@ -28,6 +37,8 @@ __device__ __forceinline__ uint8_t rule_of_row(const DecideLaunch &p, int64_t r,
       return p.conf[r] >= p.conf_thr ? DV_REPLACE : DV_REMASK;
     case DV_RULE_CONF_DRAFT:
       return p.p_tok[r] < p.conf_thr ? DV_REMASK : DV_KEEP;
+    case DV_RULE_KL_STOCHASTIC:
+      return __fmul_rn(remask_uniform(p, r), p.tau_kl) < p.kl[r] ? DV_REMASK : DV_KEEP;
     default:
       return DV_NONE;
   }

@@ -21,8 +21,10 @@ DV_OK, DV_ERR_NULL, DV_ERR_SHAPE, DV_ERR_DTYPE, DV_ERR_ALIGN, DV_ERR_ARG, \
     DV_ERR_WORKSPACE, DV_ERR_UNSUPPORTED, DV_ERR_HIP = range(9)
 DV_FP32, DV_BF16 = 0, 1
 DV_NONE, DV_KEEP, DV_REPLACE, DV_REMASK = 0, 1, 2, 3
-DV_RULE_TRUST, DV_RULE_KL, DV_RULE_CONF, DV_RULE_KL_OR_CONF, DV_RULE_COVER, DV_RULE_COUPLED_ACCEPT = range(6)
-RULES = {"TRUST": 0, "KL": 1, "CONF": 2, "KL_OR_CONF": 3, "COVER": 4, "COUPLED_ACCEPT": 5, "CONF_DRAFT": 6}
+(DV_RULE_TRUST, DV_RULE_KL, DV_RULE_CONF, DV_RULE_KL_OR_CONF, DV_RULE_COVER, DV_RULE_COUPLED_ACCEPT,
+ DV_RULE_CONF_DRAFT, DV_RULE_KL_STOCHASTIC) = range(8)
+RULES = {"TRUST": 0, "KL": 1, "CONF": 2, "KL_OR_CONF": 3, "COVER": 4, "COUPLED_ACCEPT": 5, "CONF_DRAFT": 6,
+         "KL_STOCHASTIC": 7}
 # every member of dv_row_stats, in order
 STAT_FIELDS = ("lse_v", "lse_d", "kl", "entropy", "conf", "argmax_v", "argmax_d", "tok_v", "tok_d", "kl_rev", "p_tok_d")
 # what dv_verify_rows computes unless asked otherwise (kl_rev selects the extended pass)
@@ -58,7 +60,8 @@ class dv_tuning(ctypes.Structure):
 
 class dv_decide_args(ctypes.Structure):
     _fields_ = [("rule", ctypes.c_int32), ("tau_kl", ctypes.c_float), ("conf_thr", ctypes.c_float),
-                ("mask_token", ctypes.c_int32), ("rows", ctypes.c_int64), ("group_len", ctypes.c_int64)]
+                ("mask_token", ctypes.c_int32), ("rows", ctypes.c_int64), ("group_len", ctypes.c_int64),
+                ("seed", ctypes.c_uint64), ("pos", ctypes.c_void_p), ("pos_period", ctypes.c_int64)]
 
 
 class dv_attention(ctypes.Structure):
@@ -238,16 +241,19 @@ def dv_verify_rows(verifier, drafter, temperature=0.0, seed=0, pos=None, pos_per
 
 
 def dv_decide(rule, stats, *, rows=None, tau_kl=0.0, conf_thr=0.0, mask_token=-1, subject=None, cur_tok=None,
-              group_len=0, want_prefix=False, want_best=False):
+              group_len=0, want_prefix=False, want_best=False, seed=0, pos=None, pos_period=0):
     """Per-position decisions. ``stats`` is a dict with kl / conf / tok_v / tok_d
-    tensors. Returns (decision uint8, out_tok int32, prefix int32 or None, best int32[1] or None)."""
+    tensors. Returns (decision uint8, out_tok int32, prefix int32 or None, best int32[1] or None).
+    seed, pos (int32 [rows]) and pos_period key the draws of KL_STOCHASTIC, as in dv_verify_rows."""
     rule = RULES[rule] if isinstance(rule, str) else int(rule)
     ref = next(v for k, v in stats.items() if k in STAT_FIELDS and v is not None)
     rows = ref.numel() if rows is None else int(rows)
     dev = ref.device
-    for name, v in (("subject", subject), ("cur_tok", cur_tok)):
+    for name, v in (("subject", subject), ("cur_tok", cur_tok), ("pos", pos)):
         if v is not None:
             _need_cuda(v, name)
+    if pos is not None and (pos.dtype != torch.int32 or pos.numel() < rows or not pos.is_contiguous()):
+        raise TypeError("pos must be a contiguous int32 tensor of >= rows elements")
     if subject is not None and subject.dtype != torch.uint8:
         raise TypeError("subject must be uint8")
     if cur_tok is not None and cur_tok.dtype != torch.int32:
@@ -258,7 +264,8 @@ def dv_decide(rule, stats, *, rows=None, tau_kl=0.0, conf_thr=0.0, mask_token=-1
     prefix = torch.empty(max(ngroups, 1), dtype=torch.int32, device=dev) if (want_prefix or want_best) else None
     best = torch.empty(1, dtype=torch.int32, device=dev) if want_best else None
     args = dv_decide_args(rule=rule, tau_kl=float(tau_kl), conf_thr=float(conf_thr), mask_token=int(mask_token),
-                          rows=rows, group_len=int(group_len))
+                          rows=rows, group_len=int(group_len), seed=int(seed) & 0xFFFFFFFFFFFFFFFF,
+                          pos=None if pos is None else pos.data_ptr(), pos_period=int(pos_period))
     st = dv_row_stats(**{f: (stats[f].data_ptr() if stats.get(f) is not None else None) for f in STAT_FIELDS})
     _check(load_library().dv_decide(ctypes.byref(args), ctypes.byref(st), _ptr(subject), _ptr(cur_tok),
                                     _ptr(decision), _ptr(out_tok), _ptr(prefix), _ptr(best), _stream_handle(dev)),

@@ -118,3 +118,28 @@ def test_cover_seed_chain():
         srt = np.sort(ref_score[b][fin[b]])[::-1]
         if srt.size > k and srt[k - 1] - srt[k] > 1e-5:
             assert set(idx.cpu().numpy()[b].tolist()) == set(ri[b].tolist())
+
+
+def test_bench_shape_784_maps():
+    """The launch `bench.py --influence 784` times: 784 maps (e.g. 28 layers x 28 heads) of 512 x 512 bf16
+    softmax rows drawn on the device, 40% of the queries masked, 20% of the columns new."""
+    print("case: influence 784 x 512 x 512 bf16 (benchmark shape)", flush=True)
+    dev = _dev()
+    maps, L = 784, 512
+    g = torch.Generator(device=dev)
+    g.manual_seed(2024)
+    probs = torch.empty((1, maps, L, L), dtype=torch.bfloat16, device=dev)
+    for h in range(maps):
+        x = torch.randn((L, L), generator=g, device=dev, dtype=torch.float32) * 3.0
+        probs[0, h].copy_(torch.softmax(x, dim=-1).to(torch.bfloat16))
+    qm = (torch.rand((1, L), generator=g, device=dev) < 0.4).to(torch.uint8)
+    nc = (torch.rand((1, L), generator=g, device=dev) < 0.2).to(torch.uint8)
+    d_in, d_out = dv.dv_influence_drift(probs, qm, nc)
+    torch.cuda.synchronize()
+    host = probs.view(torch.int16).cpu().numpy().view(np.uint16)
+    r_in, r_out = OA.influence_drift(_widen(host, "bf16"), qm.cpu().numpy(), nc.cpu().numpy())
+    del host
+    np.testing.assert_allclose(d_in.cpu().numpy(), r_in, rtol=RTOL, atol=ATOL)
+    np.testing.assert_allclose(d_out.cpu().numpy(), r_out, rtol=RTOL, atol=ATOL)
+    del probs
+    torch.cuda.empty_cache()

@@ -8,19 +8,23 @@
 //   o_i = sum_j softmax_j(scale <q_i, k_eff(i, j)>) v_eff(i, j)
 //
 // Flash-attention style, bidirectional: one 4-wave workgroup per (sequence,
-// head, 128 queries), one wave per 32 queries, key tiles of 64 in LDS (K_eff and
-// V_eff rows picked by each key's seed flag), double-buffered: the next tile is
-// fetched into registers while the current one is computed, then stored to the
-// other buffer, one barrier per tile. Workgroups are renumbered so that the
-// ones sharing a K/V head run on the same XCD (L2).
-//   * S^T = K_eff Q^T with v_mfma_f32_32x32x16_bf16: a lane holds the scores
-//     of one query (32 of the 64 keys; the others in lane ^ 32), so the online
-//     softmax of a query is lane-local plus one swap of wave halves. The A
-//     operand is 16 bytes of one key row in LDS; the B operand, the query's own
-//     8 dimensions per step, stays in registers.
-//   * O^T += V_eff^T P^T: V_eff is stored transposed ([d][key]) so that an A
-//     operand is one 16-byte LDS read; the B operand is assembled from the
-//     probabilities in registers with one swap of wave halves.
+// head, 128 queries), one wave per 32 queries. Key tiles (32 keys at head_dim
+// 128, 64 at head_dim 64) go from global memory straight into LDS with
+// global_load_lds, each row picked by the key's seed flag; K and V are both
+// double-buffered, so the next tile loads while the current one is computed,
+// one barrier per tile, and no register holds a tile in transit. Rows are
+// stored row-major with their 16-byte segments XOR-swizzled so that the operand
+// reads hit distinct banks. Workgroups are renumbered so that the ones sharing
+// a K/V head run on the same XCD (L2). The kernel fits three waves per SIMD.
+//   * S^T = K_eff Q^T with v_mfma_f32_32x32x16_bf16, per block of 32 keys: a
+//     lane holds the scores of one query (16 keys; the others in lane ^ 32), so
+//     the online softmax of a query is lane-local plus one swap of wave halves.
+//     The A operand is 16 bytes of one key row in LDS; the B operand, the
+//     query's own 8 dimensions per step, stays in registers.
+//   * O^T += V_eff^T P^T: the A operand (8 keys of one dimension) comes from
+//     two transposing LDS reads (ds_read_b64_tr_b16) of the row-major V tile;
+//     the B operand is assembled from the probabilities in registers with one
+//     swap of wave halves.
 //   * the softmax reference is raised lazily (only when a score passes it by
 //     2^8), so the accumulators are rarely rescaled.
 //   * the diagonal: a seed query's own score against K_cur is computed once
@@ -73,24 +77,28 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(a) + __uint_as_float(b);
 }
 
-constexpr int kKeys = 64;     // keys per tile
 constexpr float kLazy = 8.0f;  // headroom of the softmax reference, log2 units
 
-// one tile of K_eff (row-major) and V_eff (transposed) in LDS, rows padded by 16 bytes
-template <int D>
-struct Tile {
-  uint16_t k[kKeys][D + 8];
-  uint16_t vt[D][kKeys + 8];
-};
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+#define DV_LDS __attribute__((address_space(3)))
+
+// K_eff and V_eff tiles live in LDS row-major, 64 keys x D, unpadded; a row's 16-byte
+// segment c sits at segment c ^ f(row), so that the operand reads below hit distinct
+// banks: f = row % 8 for K (eight consecutive rows per b128 read), and for V bits 0-1 of
+// the row plus bit 3 moved to bit 2 (rows r..r+3 and r+8..r+11 per transposed read)
+__device__ __forceinline__ int swz_k(int row) { return row & 7; }
+__device__ __forceinline__ int swz_v(int row) { return (row & 3) | ((row >> 1) & 4); }
 
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void dual_view_kernel(DualViewLaunch p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void dual_view_kernel(DualViewLaunch p) {
   constexpr int KS = D / 16;                  // k-steps of the score product
   constexpr int DB = D / 32;                  // 32-row blocks of O^T
   constexpr int SEG = D / 8;                  // 16-byte segments of a row
-  constexpr int PER = kKeys * SEG / 256;      // segments of a tile per thread (K and V each)
-  extern __shared__ uint4 lds_raw[];          // two tiles: one computed while the next is stored
-  Tile<D> *const tiles = reinterpret_cast<Tile<D> *>(lds_raw);
+  constexpr int RPI = 1024 / (2 * D);         // rows one wave-wide 16-byte-per-lane load fills
+  constexpr int KT = D == 64 ? 64 : 32;       // keys per tile: 32 KB of LDS for both buffers
+  constexpr int PER = KT / RPI / 4;           // such loads per wave per tile (K and V each)
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * D];  // double-buffered tiles
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KT * D];
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, n = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // workgroups are dealt to the 8 XCDs in turn; renumber them so that each XCD takes a
@@ -130,52 +138,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     own = sum_halves(part);
   }
 
-  // the next tile staged in registers, rows picked by each key's seed flag: K row-major
-  // (16-byte segments, SEG lanes per key), V one key per lane (segment wave + 4 r) so
-  // that the transposed store below pairs neighbouring keys into 32-bit words
-  u32x4 kst[PER], vst[PER];
-  // sm: the tile's seed flags, one bit per key
-  constexpr int KSTEP = 256 / SEG;            // keys between a thread's K rows
-  const int kkey = tid / SEG, kseg = tid % SEG;
-  auto fetch = [&](int32_t kb, uint64_t sm) {
-    // a tail of 32 keys (len is a multiple of 32) repeats a valid row, weighted 0
-    const bool tail = kb + kKeys > L;
-    const int32_t jl = tail ? min(kb + lane, L - 1) : kb + lane;
-    const uint64_t kbits = sm >> kkey;
+  // A tile goes from global memory straight to LDS: wave-wide load r of wave w fills rows
+  // RPI (w + 4 r) .. + RPI - 1, lane l writing row RPI (w + 4 r) + l / SEG at segment
+  // l % SEG; it reads the row picked by the key's seed flag (sm, one bit per key), at the
+  // segment the swizzle puts there. A tail of 32 keys (len is a multiple of 32) repeats a
+  // valid row, weighted 0.
+  auto load_tile = [&](uint16_t *dst, const uint16_t *cur, const uint16_t *prev, bool is_k, int32_t kb,
+                       uint64_t sm) {
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
-      const int32_t row = tail ? min(kb + kkey + KSTEP * r, L - 1) : kb + kkey + KSTEP * r;
-      const uint32_t off = static_cast<uint32_t>(row * D + 8 * kseg);
-      kst[r] = *reinterpret_cast<const u32x4 *>((((kbits >> (KSTEP * r)) & 1) ? Kp : Kc) + off);
-    }
-    const uint16_t *vrow = (((sm >> lane) & 1) ? Vp : Vc) + static_cast<uint32_t>(jl * D);
-#pragma unroll
-    for (int r = 0; r < PER; ++r) vst[r] = *reinterpret_cast<const u32x4 *>(vrow + 8 * (wave + 4 * r));
-  };
-  auto store = [&](Tile<D> &tl) {
-#pragma unroll
-    for (int r = 0; r < PER; ++r) {
-      const int e = tid + 256 * r, key = e / SEG, seg = e % SEG;
-      *reinterpret_cast<u32x4 *>(&tl.k[key][8 * seg]) = kst[r];
-    }
-    // lanes 2m and 2m + 1 hold keys 2m and 2m + 1: the even lane writes the words of
-    // the even dimensions (both keys' values), the odd lane those of the odd ones
-    const bool odd = lane & 1;
-    // bytes 0..3 are this lane's word, 4..7 the partner's: the even lane takes its own
-    // low half then the partner's, the odd lane the partner's high half then its own
-    const uint32_t pick = odd ? 0x03020706u : 0x05040100u;
-#pragma unroll
-    for (int r = 0; r < PER; ++r) {
-      const uint32_t w[4] = {vst[r].x, vst[r].y, vst[r].z, vst[r].w};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint32_t part = static_cast<uint32_t>(
-            __builtin_amdgcn_mov_dpp(static_cast<int>(w[t]), 0xB1, 0xF, 0xF, false));  // lane ^ 1
-        *reinterpret_cast<uint32_t *>(&tl.vt[8 * (wave + 4 * r) + 2 * t + odd][lane & ~1]) =
-            __builtin_amdgcn_perm(part, w[t], pick);
+      const int blk = wave + 4 * r;
+      const int row = RPI * blk + lane / SEG;
+      const int c = (lane % SEG) ^ (is_k ? swz_k(row) : swz_v(row));
+      const int32_t key = kb + row < L ? kb + row : L - 1;
+      const uint32_t boff = static_cast<uint32_t>(2 * (key * D + 8 * c));  // bytes, below 2^24
+      // one load per source under complementary lane masks: each addresses a uniform base
+      // plus a 32-bit offset, so no 64-bit per-lane pointer is kept
+      if ((sm >> row) & 1) {
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const char *>(prev) + boff,
+                                         (DV_LDS void *)(dst + blk * RPI * D), 16, 0, 0);
+      } else {
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const char *>(cur) + boff,
+                                         (DV_LDS void *)(dst + blk * RPI * D), 16, 0, 0);
       }
     }
   };
+  // per-lane LDS element offsets of the operand reads; what varies per read (key block,
+  // k-step) is a constant that goes into the instruction's offset field. K: row n (+ 32 kk),
+  // segment (2 s + half) ^ (row % 8). V, transposed reads: within each 16-lane group, lane j
+  // addresses 4 dims (from 32 c + 16 (group % 2) + 4 (j % 4)) of key row 8 (group / 2) + j / 4
+  // (+ 16 u + 4 hh); the swizzle of those rows depends on the lane only
+  int koff[KS], voff[DB];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) koff[s] = n * D + 8 * ((2 * s + half) ^ swz_k(n));
+  {
+    const int grp = lane >> 4, gl = lane & 15, rowl = 8 * (grp >> 1) + (gl >> 2);
+#pragma unroll
+    for (int c = 0; c < DB; ++c) {
+      const int dcol = 32 * c + 16 * (grp & 1) + 4 * (gl & 3);
+      voff[c] = rowl * D + 8 * ((dcol >> 3) ^ swz_v(rowl)) + (dcol & 7);
+    }
+  }
 
   f32x16 o[DB];
 #pragma unroll
@@ -183,121 +186,117 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   float m = -INFINITY, lsum = 0.0f;
   const float cs = p.scale * kLog2e;
 
-  // seed flags are read a tile ahead of the rows they pick, so that no fetch waits on them
-  uint32_t sv = seed[min(lane, L - 1)];
-  fetch(0, __ballot(sv != 0));
-  if (kKeys < L) sv = seed[min(kKeys + lane, L - 1)];
-  store(tiles[0]);
-  __syncthreads();
-  for (int32_t kb = 0, cur = 0; kb < L; kb += kKeys, cur ^= 1) {
-    const bool more = kb + kKeys < L;
-    const Tile<D> &tl = tiles[cur];
-    if (more) {
-      fetch(kb + kKeys, __ballot(sv != 0));  // lands while this tile is computed
-      if (kb + 2 * kKeys < L) sv = seed[min(kb + 2 * kKeys + lane, L - 1)];
+  // One tile of 32 keys: S^T for this wave's 32 queries, the diagonal, the online softmax
+  // and the weights as B operands. Register i of the scores holds key 8 (i / 4) + 4 half
+  // + i % 4 of the tile for this lane's query. The softmax is in the log2 domain against a
+  // reference m that is raised lazily: the weights exp2(s - m) stay at most 2^kLazy, and
+  // the accumulators are rescaled only when some query's maximum passes m + kLazy (the
+  // normalized result does not depend on m).
+  auto scores = [&](const uint16_t *kt, int32_t kb, u32x4 (&pb)[2]) {
+    f32x16 sc = f32x16{};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const u32x4 ka = *reinterpret_cast<const u32x4 *>(&kt[koff[s]]);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), qf[s], sc, 0, 0, 0);
+      if (s % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // four reads in flight at most
     }
-    if (live) {
-      // scores of 64 keys (two blocks of 32) for this wave's 32 queries: S^T[key][query];
-      // register i of block kk holds key 32 kk + 8 (i / 4) + 4 half + i % 4 of this lane's query
-      // LDS operands are read a whole key block ahead of the products that use them, so
-      // the matrix cores do not wait on LDS latency
-      f32x16 sc[2] = {f32x16{}, f32x16{}};
-      u32x4 ka[KS];
+    // the diagonal: a seed query's own score reads the current key; key n of the block
+    // holding this wave's queries sits in register 4 (n / 8) + n % 4 of the lane with
+    // half == (n / 4) % 2
+    if (qb == kb && q_seed) {
+      const int sel = ((n >> 2) & 1) == half ? 4 * (n >> 3) + (n & 3) : -1;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) ka[s] = *reinterpret_cast<const u32x4 *>(&tl.k[n][16 * s + 8 * half]);
-      __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead (the scheduler would sink them)
+      for (int i = 0; i < 16; ++i) sc[i] = sel == i ? own : sc[i];
+    }
+    float red[8];  // pairwise trees keep the dependency chains short
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[s]), qf[s], sc[0], 0, 0, 0);
-        ka[s] = *reinterpret_cast<const u32x4 *>(&tl.k[32 + n][16 * s + 8 * half]);
+    for (int i = 0; i < 16; ++i) sc[i] *= cs;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[i] = fmaxf(sc[i], sc[i + 8]);
+#pragma unroll
+    for (int w = 4; w >= 1; w /= 2)
+#pragma unroll
+      for (int i = 0; i < w; ++i) red[i] = fmaxf(red[i], red[i + w]);
+    const float tmax = max_halves(red[0]);
+    const bool raise = tmax > m + kLazy;  // true on the first block (m = -inf)
+    if (__ballot(raise) != 0) {
+      const float mn = raise ? tmax : m;
+      const float corr = __builtin_amdgcn_exp2f(m - mn);
+      lsum *= corr;
+      m = mn;
+#pragma unroll
+      for (int c = 0; c < DB; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[c][i] *= corr;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sc[i] = __builtin_amdgcn_exp2f(sc[i] - m);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[i] = sc[i] + sc[i + 8];
+#pragma unroll
+    for (int w = 4; w >= 1; w /= 2)
+#pragma unroll
+      for (int i = 0; i < w; ++i) red[i] += red[i + w];
+    lsum += sum_halves(red[0]);
+    // P^T as the B operand: k-step u of the tile covers keys 16 u + 8 half + 0..7, four
+    // held by this lane and four by its partner: the lower half keeps its registers
+    // 8 u + 0..3 and takes the partner's, the upper half keeps 8 u + 4..7 and takes the
+    // partner's; one swap of halves does both
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int r0 = 8 * u;
+      uint32_t l01 = pack_bf16(sc[r0], sc[r0 + 1]), l23 = pack_bf16(sc[r0 + 2], sc[r0 + 3]);
+      uint32_t h01 = pack_bf16(sc[r0 + 4], sc[r0 + 5]), h23 = pack_bf16(sc[r0 + 6], sc[r0 + 7]);
+      swap_halves(l01, h01);
+      swap_halves(l23, h23);
+      pb[u] = u32x4{l01, l23, h01, h23};
+    }
+  };
+  // O^T += V^T P^T over one tile of 32 keys. The A operand (row d = 32 c + lane % 32,
+  // keys 16 u + 8 (lane / 32) + 0..7) comes from two transposed reads (keys + 0..3,
+  // + 4..7): the read hands lane j of a 16-lane group element j % 4 of group lane
+  // 4 i + j / 4's word as its key i
+  auto values = [&](const uint16_t *vt, const u32x4 (&pb)[2]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int c = 0; c < DB; ++c) {
+        i16x4 t2[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          t2[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DV_LDS i16x4 *)(&vt[voff[c] + (16 * u + 4 * hh) * D]));
+        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t2[0], t2[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, as_bf16x8(pb[u]), o[c], 0, 0, 0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-        sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[s]), qf[s], sc[1], 0, 0, 0);
-      // the V operands of the first two k-steps of the second product
-      u32x4 va[2][DB];
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int c = 0; c < DB; ++c)
-          va[u][c] = *reinterpret_cast<const u32x4 *>(&tl.vt[32 * c + n][16 * u + 8 * half]);
-      __builtin_amdgcn_sched_barrier(0);
-      // the diagonal: a seed query's own score reads the current key. Key n of block
-      // (qb - kb) / 32 (this lane's query) sits in register 4 (n / 8) + n % 4 of the
-      // lane with half == (n / 4) % 2
-      if (qb >= kb && qb < kb + kKeys && q_seed) {
-        const int sel = ((n >> 2) & 1) == half ? 16 * ((qb - kb) >> 5) + 4 * (n >> 3) + (n & 3) : -1;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sc[kk][i] = sel == 16 * kk + i ? own : sc[kk][i];
-      }
-      // online softmax of this lane's query in the log2 domain, against a reference m
-      // that is raised lazily: the weights exp2(s - m) stay at most 2^kLazy, and the
-      // accumulators are rescaled only when some query's maximum passes m + kLazy (the
-      // normalized result does not depend on m)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sc[kk][i] *= cs;
-      if (kb + 32 >= L) {  // len is a multiple of 32: the last tile may hold one block of keys
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sc[1][i] = -INFINITY;
-      }
-      float red[16];  // pairwise trees keep the dependency chains short
-#pragma unroll
-      for (int i = 0; i < 16; ++i) red[i] = fmaxf(sc[0][i], sc[1][i]);
-#pragma unroll
-      for (int w = 8; w >= 1; w /= 2)
-#pragma unroll
-        for (int i = 0; i < w; ++i) red[i] = fmaxf(red[i], red[i + w]);
-      const float tmax = max_halves(red[0]);
-      const bool raise = tmax > m + kLazy;  // true on the first tile (m = -inf)
-      if (__ballot(raise) != 0) {
-        const float mn = raise ? tmax : m;
-        const float corr = __builtin_amdgcn_exp2f(m - mn);
-        lsum *= corr;
-        m = mn;
-#pragma unroll
-        for (int c = 0; c < DB; ++c)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[c][i] *= corr;
-      }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sc[kk][i] = __builtin_amdgcn_exp2f(sc[kk][i] - m);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) red[i] = sc[0][i] + sc[1][i];
-#pragma unroll
-      for (int w = 8; w >= 1; w /= 2)
-#pragma unroll
-        for (int i = 0; i < w; ++i) red[i] += red[i + w];
-      lsum += sum_halves(red[0]);
+      __builtin_amdgcn_sched_barrier(0);  // bounds the reads in flight (registers)
+    }
+  };
 
-      // P^T as the B operand: k-step u covers keys 16 u + 8 half + 0..7 (block u / 2),
-      // four of them held by this lane and four by its partner: the lower half keeps its
-      // registers 8 (u % 2) + 0..3 and takes the partner's, the upper half keeps
-      // 8 (u % 2) + 4..7 and takes the partner's; one swap of halves does both
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int kk = u >> 1, r0 = 8 * (u & 1);
-        uint32_t l01 = pack_bf16(sc[kk][r0], sc[kk][r0 + 1]), l23 = pack_bf16(sc[kk][r0 + 2], sc[kk][r0 + 3]);
-        uint32_t h01 = pack_bf16(sc[kk][r0 + 4], sc[kk][r0 + 5]), h23 = pack_bf16(sc[kk][r0 + 6], sc[kk][r0 + 7]);
-        swap_halves(l01, h01);
-        swap_halves(l23, h23);
-        const u32x4 pb = u32x4{l01, l23, h01, h23};
-#pragma unroll
-        for (int c = 0; c < DB; ++c) {
-          o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[u & 1][c]), as_bf16x8(pb), o[c], 0, 0, 0);
-          if (u < 2) va[u & 1][c] = *reinterpret_cast<const u32x4 *>(&tl.vt[32 * c + n][16 * (u + 2) + 8 * half]);
-        }
-      }
+  // Tiles are double-buffered: the loads of tile t + 1 are issued right after the barrier
+  // that opens tile t (it frees their buffer, last read in tile t - 1) and land while tile t
+  // is computed; the barrier that opens tile t + 1 waits for them. Seed flags are read a
+  // tile ahead of the rows they pick. Waves past the end of the sequence compute on a
+  // valid query and store nothing.
+  uint64_t sm = __ballot(seed[min(lane % KT, L - 1)] != 0);
+  load_tile(Ks[0], Kc, Kp, true, 0, sm);
+  load_tile(Vs[0], Vc, Vp, false, 0, sm);
+  uint32_t sv = seed[min(KT + lane % KT, L - 1)];
+  for (int32_t kb = 0, cur = 0; kb < L; kb += KT, cur ^= 1) {
+    __syncthreads();  // tile t is in LDS; every wave is done with tile t - 1
+    if (kb + KT < L) {
+      sm = __ballot(sv != 0);
+      if (kb + 2 * KT < L) sv = seed[min(kb + 2 * KT + lane % KT, L - 1)];
+      load_tile(Ks[cur ^ 1], Kc, Kp, true, kb + KT, sm);
+      load_tile(Vs[cur ^ 1], Vc, Vp, false, kb + KT, sm);
     }
-    // the other buffer was last read in the previous tile, which every wave has left
-    if (more) store(tiles[cur ^ 1]);
-    __syncthreads();
+    // blocks of 32 keys; len is a multiple of 32, so the last tile may hold fewer blocks
+#pragma unroll
+    for (int bk = 0; bk < KT / 32; ++bk) {
+      if (bk > 0 && kb + 32 * bk >= L) break;
+      u32x4 pb[2];
+      scores(Ks[cur] + 32 * bk * D, kb + 32 * bk, pb);
+      values(Vs[cur] + 32 * bk * D, pb);
+    }
   }
   if (!live) return;
   if (q_seed) {
@@ -326,24 +325,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     }
 }
 
-// two D = 128 tiles (70 KB) exceed the default 64 KB of dynamic LDS; gfx950 has 160 KB per CU
-template <typename K>
-hipError_t allow_lds(K kernel, size_t bytes) {
-  return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                             static_cast<int>(bytes));
-}
-
 }  // namespace
 
 hipError_t launch_dual_view(const DualViewLaunch &p, hipStream_t stream) {
   if (p.nseq == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((p.len + 127) / 128 * p.heads * p.nseq));
   if (p.head_dim == 128) {
-    const hipError_t attr = allow_lds(dual_view_kernel<128>, 2 * sizeof(Tile<128>));  // on the current device
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(dual_view_kernel<128>, grid, dim3(256), 2 * sizeof(Tile<128>), stream, p);
+    hipLaunchKernelGGL(dual_view_kernel<128>, grid, dim3(256), 0, stream, p);
   } else {
-    hipLaunchKernelGGL(dual_view_kernel<64>, grid, dim3(256), 2 * sizeof(Tile<64>), stream, p);
+    hipLaunchKernelGGL(dual_view_kernel<64>, grid, dim3(256), 0, stream, p);
   }
   return hipGetLastError();
 }

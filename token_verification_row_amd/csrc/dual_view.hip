@@ -82,12 +82,17 @@ constexpr float kLazy = 8.0f;  // headroom of the softmax reference, log2 units
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define DV_LDS __attribute__((address_space(3)))
 
-// K_eff and V_eff tiles live in LDS row-major, 64 keys x D, unpadded; a row's 16-byte
+// K_eff and V_eff tiles live in LDS row-major, keys x D, unpadded; a row's 16-byte
 // segment c sits at segment c ^ f(row), so that the operand reads below hit distinct
-// banks: f = row % 8 for K (eight consecutive rows per b128 read), and for V bits 0-1 of
-// the row plus bit 3 moved to bit 2 (rows r..r+3 and r+8..r+11 per transposed read)
-__device__ __forceinline__ int swz_k(int row) { return row & 7; }
-__device__ __forceinline__ int swz_v(int row) { return (row & 3) | ((row >> 1) & 4); }
+// banks of the 64-bank (256-byte) LDS. K, b128 reads of 16 consecutive rows at one
+// segment: f spreads those rows over the 16 four-bank groups (a 256-byte row at D = 128,
+// a 128-byte one at D = 64, where row parity already picks the half). V, transposed
+// reads of rows r..r+3 (and r+8..r+11), 64 bytes each: f moves each row's bytes to its
+// own quarter of the banks (bits 2-3 of the segment; at D = 64 row parity picks the half).
+template <int D>
+__device__ __forceinline__ int swz_k(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int swz_v(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
 
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void dual_view_kernel(DualViewLaunch p) {
@@ -149,7 +154,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     for (int r = 0; r < PER; ++r) {
       const int blk = wave + 4 * r;
       const int row = RPI * blk + lane / SEG;
-      const int c = (lane % SEG) ^ (is_k ? swz_k(row) : swz_v(row));
+      const int c = (lane % SEG) ^ (is_k ? swz_k<D>(row) : swz_v<D>(row));
       const int32_t key = kb + row < L ? kb + row : L - 1;
       const uint32_t boff = static_cast<uint32_t>(2 * (key * D + 8 * c));  // bytes, below 2^24
       // one load per source under complementary lane masks: each addresses a uniform base
@@ -165,18 +170,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
   };
   // per-lane LDS element offsets of the operand reads; what varies per read (key block,
   // k-step) is a constant that goes into the instruction's offset field. K: row n (+ 32 kk),
-  // segment (2 s + half) ^ (row % 8). V, transposed reads: within each 16-lane group, lane j
+  // segment (2 s + half) ^ f(row). V, transposed reads: within each 16-lane group, lane j
   // addresses 4 dims (from 32 c + 16 (group % 2) + 4 (j % 4)) of key row 8 (group / 2) + j / 4
   // (+ 16 u + 4 hh); the swizzle of those rows depends on the lane only
   int koff[KS], voff[DB];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) koff[s] = n * D + 8 * ((2 * s + half) ^ swz_k(n));
+  for (int s = 0; s < KS; ++s) koff[s] = n * D + 8 * ((2 * s + half) ^ swz_k<D>(n));
   {
     const int grp = lane >> 4, gl = lane & 15, rowl = 8 * (grp >> 1) + (gl >> 2);
 #pragma unroll
     for (int c = 0; c < DB; ++c) {
       const int dcol = 32 * c + 16 * (grp & 1) + 4 * (gl & 3);
-      voff[c] = rowl * D + 8 * ((dcol >> 3) ^ swz_v(rowl)) + (dcol & 7);
+      voff[c] = rowl * D + 8 * ((dcol >> 3) ^ swz_v<D>(rowl)) + (dcol & 7);
     }
   }
 

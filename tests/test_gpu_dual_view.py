@@ -51,7 +51,9 @@ def _check(host, gpu, sd, gsd, scale, ctx):
 
 @pytest.mark.parametrize("B,H,Hkv,L,D,p_seed", [(1, 2, 1, 32, 64, 0.3), (1, 4, 2, 96, 128, 0.3),
                                                 (2, 4, 4, 256, 128, 0.25), (1, 8, 2, 512, 64, 0.2),
-                                                (1, 2, 2, 160, 128, 0.0), (1, 2, 1, 64, 128, 1.0)])
+                                                (1, 2, 2, 160, 128, 0.0), (1, 2, 1, 64, 128, 1.0),
+                                                (1, 4, 2, 96, 64, 0.3), (2, 4, 2, 160, 64, 0.5),
+                                                (1, 3, 1, 224, 64, 1.0), (1, 2, 2, 288, 128, 0.5)])
 def test_dual_view_attention(B, H, Hkv, L, D, p_seed):
     print(f"case: dual view B={B} H={H} Hkv={Hkv} L={L} D={D} seeds={p_seed}", flush=True)
     host, gpu, sd, gsd = _case(B, H, Hkv, L, D, p_seed, seed=L + D + H)

@@ -287,7 +287,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
   load_tile(Vs[0], Vc, Vp, false, 0, sm);
   uint32_t sv = seed[min(KT + lane % KT, L - 1)];
   for (int32_t kb = 0, cur = 0; kb < L; kb += KT, cur ^= 1) {
-    __syncthreads();  // tile t is in LDS; every wave is done with tile t - 1
+    // vmcnt(0): this wave's loads of tile t have written LDS (a load to LDS counts until its
+    // data is in); the barrier then makes the whole tile visible, and every wave is done
+    // with tile t - 1
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
     if (kb + KT < L) {
       sm = __ballot(sv != 0);
       if (kb + 2 * KT < L) sv = seed[min(kb + 2 * KT + lane % KT, L - 1)];

@@ -172,8 +172,8 @@ typedef enum dv_rule {
                                  the rows after it */
   DV_RULE_CONF_DRAFT = 6,     /* [DualDiffusion] §2 item 3 read as the verifier's confidence
                                  in the drafted token: REMASK iff p_tok_d < conf_thr */
-  DV_RULE_KL_STOCHASTIC = 7   /* [DualDiffusion] §2 item 2 with its "probabilistically high"
-                                 clause, read as one Bernoulli draw per row remasking with
+  DV_RULE_KL_STOCHASTIC = 7   /* [DualDiffusion] §2 item 2 with its second, probabilistic
+                                 remask condition, read as one Bernoulli draw per row remasking with
                                  probability min(1, kl / tau_kl): REMASK iff the float32
                                  product u * tau_kl < kl, where u = (2 (h >> 9) + 1) 2^-24
                                  and h is the noise hash word (DV_HASH_V1, as in dv_noise)

@@ -11,10 +11,10 @@ Sources and readings:
 * TRUST, [DualDiffusion] §2 "Verification algorithms" item 1: every drafted
   token is accepted unchanged -> KEEP.
 * KL, item 2: a token is remasked when KL(p_v || p_d) exceeds tau. The page
-  also mentions remasking when the divergence is "probabilistically" high;
-  that clause is not specified and is not part of this rule. REMASK iff
+  also names a probabilistic remask condition without giving its
+  probability; that condition is not part of this rule. REMASK iff
   kl > tau (strict), else KEEP.
-* KL_STOCHASTIC, item 2 with its "probabilistically high" clause: the page
+* KL_STOCHASTIC, item 2 with its probabilistic remask condition: the page
   gives no probability, so the reading is the plainest one that contains
   the threshold clause: one Bernoulli draw per row that remasks with
   probability min(1, kl / tau). Its uniform u comes from the same counter

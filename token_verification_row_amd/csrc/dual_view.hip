@@ -94,14 +94,15 @@ __device__ __forceinline__ int swz_k(int row) { return D == 128 ? (row & 15) : (
 template <int D>
 __device__ __forceinline__ int swz_v(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
 
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void dual_view_kernel(DualViewLaunch p) {
+// NW waves per workgroup (32 queries each) share every tile of KT keys.
+template <int D, int NW, int KT>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) void dual_view_kernel(DualViewLaunch p) {
   constexpr int KS = D / 16;                  // k-steps of the score product
   constexpr int DB = D / 32;                  // 32-row blocks of O^T
   constexpr int SEG = D / 8;                  // 16-byte segments of a row
   constexpr int RPI = 1024 / (2 * D);         // rows one wave-wide 16-byte-per-lane load fills
-  constexpr int KT = D == 64 ? 64 : 32;       // keys per tile: 32 KB of LDS for both buffers
-  constexpr int PER = KT / RPI / 4;           // such loads per wave per tile (K and V each)
+  constexpr int LPT = KT / RPI;               // such loads per tile (K and V each)
+  constexpr int PER = (LPT + NW - 1) / NW;    // per wave, at most
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * D];  // double-buffered tiles
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KT * D];
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, n = lane & 31;
@@ -109,13 +110,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
   // workgroups are dealt to the 8 XCDs in turn; renumber them so that each XCD takes a
   // contiguous range of (sequence, kv head, head, query block), whose K/V its L2 shares
   const int32_t L = static_cast<int32_t>(p.len);
-  const uint32_t nqb = static_cast<uint32_t>(L + 127) / 128, total = gridDim.x, lin = blockIdx.x;
+  const uint32_t nqb = static_cast<uint32_t>(L + 32 * NW - 1) / (32 * NW), total = gridDim.x, lin = blockIdx.x;
   const uint32_t even = total / 8 * 8;
   const uint32_t id = lin < even ? (lin % 8) * (even / 8) + lin / 8 : lin;
   const uint32_t qblk = id % nqb, hb = id / nqb;
   const int64_t h = hb % static_cast<uint32_t>(p.heads), b = hb / static_cast<uint32_t>(p.heads);
   const int64_t g = h / (p.heads / p.kv_heads);
-  const int32_t qb = static_cast<int32_t>(qblk) * 128 + wave * 32;  // this wave's first query
+  const int32_t qb = static_cast<int32_t>(qblk) * 32 * NW + wave * 32;  // this wave's first query
   const bool live = qb < L;
   const uint16_t *Q = p.q + ((b * p.heads + h) * L) * D;
   const int64_t kvo = ((b * p.kv_heads + g) * L) * D;
@@ -152,7 +153,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
                        uint64_t sm) {
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
-      const int blk = wave + 4 * r;
+      const int blk = wave + NW * r;
+      if (LPT % NW != 0 && blk >= LPT) break;  // wave-uniform
       const int row = RPI * blk + lane / SEG;
       const int c = (lane % SEG) ^ (is_k ? swz_k<D>(row) : swz_v<D>(row));
       const int32_t key = kb + row < L ? kb + row : L - 1;
@@ -299,12 +301,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
       load_tile(Vs[cur ^ 1], Vc, Vp, false, kb + KT, sm);
     }
     // blocks of 32 keys; len is a multiple of 32, so the last tile may hold fewer blocks
+    if (live) {
 #pragma unroll
-    for (int bk = 0; bk < KT / 32; ++bk) {
-      if (bk > 0 && kb + 32 * bk >= L) break;
-      u32x4 pb[2];
-      scores(Ks[cur] + 32 * bk * D, kb + 32 * bk, pb);
-      values(Vs[cur] + 32 * bk * D, pb);
+      for (int bk = 0; bk < KT / 32; ++bk) {
+        if (bk > 0 && kb + 32 * bk >= L) break;
+        u32x4 pb[2];
+        scores(Ks[cur] + 32 * bk * D, kb + 32 * bk, pb);
+        values(Vs[cur] + 32 * bk * D, pb);
+      }
     }
   }
   if (!live) return;
@@ -338,11 +342,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
 
 hipError_t launch_dual_view(const DualViewLaunch &p, hipStream_t stream) {
   if (p.nseq == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((p.len + 127) / 128 * p.heads * p.nseq));
+  // 4 waves (128 queries) per workgroup; both K and V tiles double-buffered in 32 KB:
+  // 32-key tiles at head_dim 128, 64-key tiles at 64. (Six waves sharing 64-key tiles at
+  // head_dim 128 measured 25% slower.)
   if (p.head_dim == 128) {
-    hipLaunchKernelGGL(dual_view_kernel<128>, grid, dim3(256), 0, stream, p);
+    constexpr int NW = 4;
+    const dim3 grid(static_cast<unsigned>((p.len + 32 * NW - 1) / (32 * NW) * p.heads * p.nseq));
+    hipLaunchKernelGGL((dual_view_kernel<128, NW, 32>), grid, dim3(64 * NW), 0, stream, p);
   } else {
-    hipLaunchKernelGGL(dual_view_kernel<64>, grid, dim3(256), 0, stream, p);
+    constexpr int NW = 4;
+    const dim3 grid(static_cast<unsigned>((p.len + 32 * NW - 1) / (32 * NW) * p.heads * p.nseq));
+    hipLaunchKernelGGL((dual_view_kernel<64, NW, 64>), grid, dim3(64 * NW), 0, stream, p);
   }
   return hipGetLastError();
 }

@@ -213,7 +213,8 @@ typedef struct dv_decide_args {
  * longest prefix, lowest index on ties) or NULL; best_group requires
  * prefix_len. decision and out_tok may be NULL to skip them.
  * Errors: DV_ERR_NULL, DV_ERR_SHAPE (rows < 0, group_len < 0, group_len not
- * dividing rows), DV_ERR_ARG (unknown rule, non-finite thresholds). */
+ * dividing rows, pos_period < 0), DV_ERR_ARG (unknown rule, non-finite
+ * thresholds, tau_kl <= 0 for KL_STOCHASTIC). */
 dv_status dv_decide(const dv_decide_args *args, const dv_row_stats *stats, const uint8_t *subject,
                     const int32_t *cur_tok, uint8_t *decision, int32_t *out_tok,
                     int32_t *prefix_len, int32_t *best_group, hipStream_t stream);

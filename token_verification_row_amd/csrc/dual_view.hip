@@ -12,7 +12,12 @@
 // 128, 64 at head_dim 64) go from global memory straight into LDS with
 // global_load_lds, each row picked by the key's seed flag; K and V are both
 // double-buffered, so the next tile loads while the current one is computed,
-// one barrier per tile, and no register holds a tile in transit. Rows are
+// one barrier per tile, and no register holds a tile in transit. Each buffer is
+// an LDS variable of its own and the loop is unrolled by two tiles, so the
+// compiler sees that the reads of one buffer cannot alias the loads landing in
+// the other and does not make them wait for those loads (with one array
+// indexed by a loop-carried buffer number, every tile's first read waited for
+// the next tile's loads). Rows are
 // stored row-major with their 16-byte segments XOR-swizzled so that the operand
 // reads hit distinct banks. Workgroups are renumbered so that the ones sharing
 // a K/V head run on the same XCD (L2). The kernel fits three waves per SIMD.
@@ -103,8 +108,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
   constexpr int RPI = 1024 / (2 * D);         // rows one wave-wide 16-byte-per-lane load fills
   constexpr int LPT = KT / RPI;               // such loads per tile (K and V each)
   constexpr int PER = (LPT + NW - 1) / NW;    // per wave, at most
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * D];  // double-buffered tiles
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KT * D];
+  // double-buffered tiles, one LDS variable per buffer: every access below names its buffer
+  // statically, so the compiler can tell the reads of one buffer from the loads in flight
+  // into the other and does not make the reads wait for those loads
+  __shared__ __attribute__((aligned(16))) uint16_t K0[KT * D], K1[KT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[KT * D], V1[KT * D];
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, n = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // workgroups are dealt to the 8 XCDs in turn; renumber them so that each XCD takes a
@@ -285,20 +293,21 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
   // tile ahead of the rows they pick. Waves past the end of the sequence compute on a
   // valid query and store nothing.
   uint64_t sm = __ballot(seed[min(lane % KT, L - 1)] != 0);
-  load_tile(Ks[0], Kc, Kp, true, 0, sm);
-  load_tile(Vs[0], Vc, Vp, false, 0, sm);
+  load_tile(K0, Kc, Kp, true, 0, sm);
+  load_tile(V0, Vc, Vp, false, 0, sm);
   uint32_t sv = seed[min(KT + lane % KT, L - 1)];
-  for (int32_t kb = 0, cur = 0; kb < L; kb += KT, cur ^= 1) {
-    // vmcnt(0): this wave's loads of tile t have written LDS (a load to LDS counts until its
-    // data is in); the barrier then makes the whole tile visible, and every wave is done
-    // with tile t - 1
+  // one tile: kt/vt hold it, kn/vn receive the next one
+  auto tile = [&](int32_t kb, const uint16_t *kt, const uint16_t *vt, uint16_t *kn, uint16_t *vn) {
+    // vmcnt(0): this wave's loads of this tile have written LDS (a load to LDS counts until
+    // its data is in); the barrier then makes the whole tile visible, and every wave is done
+    // with the previous tile, whose buffers the next loads overwrite
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     if (kb + KT < L) {
       sm = __ballot(sv != 0);
       if (kb + 2 * KT < L) sv = seed[min(kb + 2 * KT + lane % KT, L - 1)];
-      load_tile(Ks[cur ^ 1], Kc, Kp, true, kb + KT, sm);
-      load_tile(Vs[cur ^ 1], Vc, Vp, false, kb + KT, sm);
+      load_tile(kn, Kc, Kp, true, kb + KT, sm);
+      load_tile(vn, Vc, Vp, false, kb + KT, sm);
     }
     // blocks of 32 keys; len is a multiple of 32, so the last tile may hold fewer blocks
     if (live) {
@@ -306,10 +315,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
       for (int bk = 0; bk < KT / 32; ++bk) {
         if (bk > 0 && kb + 32 * bk >= L) break;
         u32x4 pb[2];
-        scores(Ks[cur] + 32 * bk * D, kb + 32 * bk, pb);
-        values(Vs[cur] + 32 * bk * D, pb);
+        scores(kt + 32 * bk * D, kb + 32 * bk, pb);
+        values(vt + 32 * bk * D, pb);
       }
     }
+  };
+  for (int32_t kb = 0; kb < L; kb += 2 * KT) {
+    tile(kb, K0, V0, K1, V1);
+    if (kb + KT < L) tile(kb + KT, K1, V1, K0, V0);
   }
   if (!live) return;
   if (q_seed) {

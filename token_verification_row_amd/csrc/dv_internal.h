@@ -20,11 +20,18 @@ constexpr uint32_t kSeedSalt = 0x243F6A88u;
 constexpr uint32_t kPosSalt = 0x85A308D3u;
 constexpr uint32_t kIndexStep = 0x9E3779B9u;
 
-__host__ __device__ __forceinline__ uint32_t mix32(uint32_t x) {
+// mix32 without its last step (x ^= x >> 16), which leaves the top 16 bits as they are:
+// mix32(x) >> 16 == mix32_head(x) >> 16
+__host__ __device__ __forceinline__ uint32_t mix32_head(uint32_t x) {
   x ^= x >> 16;
   x *= 0x85EBCA6Bu;
   x ^= x >> 13;
   x *= 0xC2B2AE35u;
+  return x;
+}
+
+__host__ __device__ __forceinline__ uint32_t mix32(uint32_t x) {
+  x = mix32_head(x);
   x ^= x >> 16;
   return x;
 }

@@ -150,8 +150,8 @@ def cpu_baseline(a_rows, b_rows, w, pos, workers):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=4, choices=[2, 3, 4, 5])
     ap.add_argument("--cpu-rows", type=int, default=1024, help="rows of the workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")

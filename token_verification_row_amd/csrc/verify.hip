@@ -794,24 +794,31 @@ __global__ __launch_bounds__(1024) void verify_rows_kernel(VerifyLaunch p) {
 }
 
 // Chunk-max noise table: entry (q, c) bounds the noise of position q over the
-// valid elements of chunk c (one thread per entry), as chunk_noise_bound does
-// in registers. Entries number below 2^28 (the table is at most 1 GiB).
+// valid elements of chunk c, as chunk_noise_bound does in registers (from the
+// hash words without their last step). Each thread fills kCmaxPerThread entries
+// of one position, 256 apart, so that a launch has few workgroups. Entries
+// number below 2^28 (the table is at most 1 GiB).
 // Grid: x covers the chunks of a position, y the positions (strided past 65535), so
 // the position's key is uniform across the workgroup (scalar unit) and no thread divides.
+constexpr uint32_t kCmaxPerThread = 4;
+
 template <int N>
 __global__ __launch_bounds__(256) void noise_cmax_kernel(uint32_t seed_b, uint32_t rows, uint32_t ld, int64_t vocab,
                                                         float *cmax) {
-  const uint32_t c = blockIdx.x * 256u + threadIdx.x;
-  if (c >= ld) return;
   for (uint32_t q = blockIdx.y; q < rows; q += gridDim.y) {
     const uint32_t key = row_key(seed_b, static_cast<int32_t>(q));
-    uint32_t hm = 0;
 #pragma unroll
-    for (int j = 0; j < N; ++j) {
-      const uint32_t i = c * N + j;  // vocab < 2^31
-      if (i < vocab) hm = max(hm, mix32(key ^ (i * kIndexStep)));
+    for (uint32_t k = 0; k < kCmaxPerThread; ++k) {
+      const uint32_t c = (blockIdx.x * kCmaxPerThread + k) * 256u + threadIdx.x;
+      if (c >= ld) break;
+      uint32_t hm = 0;
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        const uint32_t i = c * N + j;  // vocab < 2^31
+        if (i < vocab) hm = max(hm, mix32_head(key ^ (i * kIndexStep)));
+      }
+      cmax[static_cast<size_t>(q) * ld + c] = noise_bound_of_word(hm | 0xFFFFu);
     }
-    cmax[static_cast<size_t>(q) * ld + c] = noise_bound_of_word(hm);
   }
 }
 
@@ -834,7 +841,7 @@ template <bool BF16>
 hipError_t launch_typed(const VerifyLaunch &p, hipStream_t stream) {
   constexpr int N = Chunk<BF16>::N;
   if (p.noise_cmax) {
-    const dim3 grid(static_cast<unsigned>((p.cmax_ld + 255) / 256),
+    const dim3 grid(static_cast<unsigned>((p.cmax_ld + 256 * kCmaxPerThread - 1) / (256 * kCmaxPerThread)),
                     static_cast<unsigned>(p.cmax_rows < 65535 ? p.cmax_rows : 65535));
     hipLaunchKernelGGL(noise_cmax_kernel<N>, grid, dim3(256), 0, stream, p.seed_b,
                        static_cast<uint32_t>(p.cmax_rows), static_cast<uint32_t>(p.cmax_ld), p.vocab, p.noise_cmax);

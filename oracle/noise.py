@@ -24,7 +24,24 @@ row, candidate or shard carries it:
 * word for vocabulary index i: h_i = mix32(k ^ (i * 0x9E3779B9 mod 2^32)).
 * uniform: u_i = (2 * (h_i >> 9) + 1) * 2^-24, i.e. 23 random bits placed at
   the centres of 2^23 equal cells of (0, 1); never 0 or 1.
-* Gumbel: g_i = -ln(-ln u_i).
+
+The Gumbel values (DV_NOISE_V2) come in groups of 8 consecutive vocabulary
+indices, group c holding indices 8c .. 8c+7. Any set of n i.i.d. standard
+Gumbel values can be drawn largest first: their maximum is Gumbel shifted by
+ln n (its CDF is F(x)^n with F(x) = exp(-e^-x)), it sits at a uniformly
+chosen place, and given it the other n - 1 are i.i.d. Gumbel truncated above
+at it (CDF F(x)/F(max)). The joint law is exactly that of n independent
+draws, so Gumbel-max sampling is unchanged; what it buys is that a group's
+largest noise value comes from one hash word. Per row:
+
+* group key: kg = mix32(k ^ 0x6A09E667);
+* group word: w_c = mix32(kg ^ (c * 0x9E3779B9 mod 2^32));
+* for a full group (8c + 8 <= vocab): the maximum sits at j* = w_c & 7 and
+  is g_max = -ln(-ln(u_max) / 8) with u_max = (2 * (w_c >> 9) + 1) * 2^-24;
+  index i = 8c + j with j != j* gets g_i = -ln(-(ln u_i + ln(u_max) / 8)),
+  the inverse of the truncated CDF at u_i;
+* the last group when it is partial (vocab not a multiple of 8): each index
+  gets g_i = -ln(-ln u_i), independent draws.
 
 Temperature T = 0 means greedy decoding: the token is the argmax of the
 logits (lowest index on ties) and no noise is drawn. Ties of the perturbed
@@ -36,9 +53,9 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "MIX_C1", "MIX_C2", "SEED_SALT", "POS_SALT", "INDEX_STEP",
-    "mix32", "seed_words", "row_keys", "hash_words", "uniforms", "gumbel",
-    "perturbed_scores", "gumbel_tokens",
+    "MIX_C1", "MIX_C2", "SEED_SALT", "POS_SALT", "INDEX_STEP", "GROUP_SALT", "GROUP",
+    "mix32", "seed_words", "row_keys", "hash_words", "group_words", "uniforms", "gumbel",
+    "noise", "perturbed_scores", "gumbel_tokens",
 ]
 
 MIX_C1 = 0x85EBCA6B
@@ -46,6 +63,8 @@ MIX_C2 = 0xC2B2AE35
 SEED_SALT = 0x243F6A88
 POS_SALT = 0x85A308D3
 INDEX_STEP = 0x9E3779B9
+GROUP_SALT = 0x6A09E667
+GROUP = 8  # vocabulary indices per noise group
 _M32 = np.uint64(0xFFFFFFFF)
 
 
@@ -84,6 +103,14 @@ def hash_words(seed: int, pos, vocab: int, start: int = 0) -> np.ndarray:
     return mix32(k.astype(np.uint64)[:, None] ^ step[None, :])
 
 
+def group_words(seed: int, pos, ngroups: int) -> np.ndarray:
+    """uint32 group words w[r, c] for groups 0 .. ngroups-1."""
+    kg = mix32(row_keys(seed, pos) ^ np.uint32(GROUP_SALT))
+    c = np.arange(ngroups, dtype=np.uint64)
+    step = (c * np.uint64(INDEX_STEP)) & _M32
+    return mix32(kg.astype(np.uint64)[:, None] ^ step[None, :])
+
+
 def uniforms(h: np.ndarray) -> np.ndarray:
     """u = (2 * (h >> 9) + 1) * 2^-24 as float64 (exact)."""
     h = np.asarray(h, dtype=np.uint32)
@@ -93,6 +120,26 @@ def uniforms(h: np.ndarray) -> np.ndarray:
 def gumbel(u: np.ndarray) -> np.ndarray:
     """Standard Gumbel variate from a uniform: g = -ln(-ln u)."""
     return -np.log(-np.log(np.asarray(u, dtype=np.float64)))
+
+
+def noise(seed: int, pos, vocab: int) -> np.ndarray:
+    """The Gumbel values g[r, i] of rows at positions ``pos`` over a vocabulary of ``vocab``
+    (DV_NOISE_V2, module docstring), float64."""
+    pos = np.asarray(pos)
+    u = uniforms(hash_words(seed, pos, vocab))
+    g = gumbel(u)
+    nfull = vocab // GROUP
+    if nfull:
+        w = group_words(seed, pos, nfull)
+        umax = uniforms(w)
+        lm = np.log(umax)[:, :, None] / GROUP                       # ln F(g_max)
+        lu = np.log(u[:, :GROUP * nfull]).reshape(len(pos), nfull, GROUP)
+        gf = -np.log(-(lu + lm))                                    # truncated below the maximum
+        jstar = (w & np.uint32(GROUP - 1)).astype(np.int64)
+        gmax = -np.log(-np.log(umax) / GROUP)
+        np.put_along_axis(gf, jstar[:, :, None], gmax[:, :, None], axis=2)
+        g[:, :GROUP * nfull] = gf.reshape(len(pos), GROUP * nfull)
+    return g
 
 
 def perturbed_scores(x: np.ndarray, temperature: float, g: np.ndarray) -> np.ndarray:
@@ -128,7 +175,7 @@ def gumbel_tokens(a: np.ndarray, b: np.ndarray, temperature: float, seed: int, p
     if t == 0.0:
         sa, sb = a, b
     else:
-        g = gumbel(uniforms(hash_words(seed, pos, a.shape[1])))
+        g = noise(seed, pos, a.shape[1])
         sa = perturbed_scores(a, t, g)
         sb = perturbed_scores(b, t, g)
     tok_v, margin_v = _argmax_and_margin(sa)

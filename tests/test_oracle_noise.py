@@ -159,10 +159,17 @@ def test_zero_temperature_is_argmax_and_small_temperature_limit():
     t0 = noise.gumbel_tokens(a, b, 0.0, 1, pos)
     np.testing.assert_array_equal(t0["tok_v"], np.argmax(a, axis=1))
     np.testing.assert_array_equal(t0["tok_d"], np.argmax(b, axis=1))
-    # g lies in [-2.8116, 16.6356], so a top-2 logit gap above T * 19.4471 fixes the token
+    # g lies in [-2.9293, 18.7150] (a group maximum reaches -ln(-ln(1 - 2^-24) / 8), the value
+    # truncated below the smallest maximum -ln(-(1 + 1/8) ln 2^-24)), so a top-2 logit gap above
+    # T * 21.6443 fixes the token
+    lo = -math.log(-(1 + 1 / 8) * math.log(2.0 ** -24))
+    hi = -math.log(-math.log(1 - 2.0 ** -24) / 8)
+    assert lo == pytest.approx(-2.92932, abs=1e-5) and hi == pytest.approx(18.71497, abs=1e-5)
+    g = noise.noise(1, pos, 300)
+    assert g.min() >= lo and g.max() <= hi
     srt = np.sort(a, axis=1)
     gap = srt[:, -1] - srt[:, -2]
-    T = float(gap.min()) / 19.45
+    T = float(gap.min()) / (hi - lo + 1e-3)
     tt = noise.gumbel_tokens(a, b, T, 1, pos)
     np.testing.assert_array_equal(tt["tok_v"], np.argmax(a, axis=1))
 
@@ -196,3 +203,70 @@ def test_seed_words_use_both_halves():
     assert noise.seed_words(1) != noise.seed_words(1 + (1 << 32))
     assert noise.seed_words(0)[0] == int(noise.mix32(noise.SEED_SALT))
     assert math.isfinite(float(noise.gumbel(np.array([0.5]))[0]))
+
+
+def _gumbel_ks(x, loc=0.0):
+    return scipy.stats.kstest(np.ravel(x), scipy.stats.gumbel_r(loc=loc).cdf).pvalue
+
+
+def test_grouped_noise_is_iid_gumbel_in_law():
+    """DV_NOISE_V2 draws each full group of 8 largest first; the values must still be i.i.d.
+    standard Gumbel: marginals, group maxima (Gumbel shifted by ln 8), the place of the maximum
+    (uniform) and pairs inside a group (independent)."""
+    R, V = 256, 4096
+    g = noise.noise(77, np.arange(R, dtype=np.int32), V)
+    assert _gumbel_ks(g) > 1e-4
+    grp = g.reshape(R, V // 8, 8)
+    assert _gumbel_ks(grp.max(axis=2), loc=math.log(8)) > 1e-4
+    assert scipy.stats.chisquare(np.bincount(grp.argmax(axis=2).ravel(), minlength=8)).pvalue > 1e-4
+    # every place j of a group has the standard law, not only the pooled values
+    for j in (0, 3, 7):
+        assert _gumbel_ks(grp[:, :, j]) > 1e-4
+    # pairs of places: their CDF values fall uniformly on an 8 x 8 grid
+    cdf = scipy.stats.gumbel_r.cdf
+    for j, k in ((0, 1), (2, 7)):
+        a = np.minimum((cdf(grp[:, :, j]) * 8).astype(np.int64), 7).ravel()
+        b = np.minimum((cdf(grp[:, :, k]) * 8).astype(np.int64), 7).ravel()
+        assert scipy.stats.chisquare(np.bincount(a * 8 + b, minlength=64)).pvalue > 1e-4
+
+
+def test_grouped_noise_follows_its_definition():
+    """The maximum sits where the group word says; the others are the truncated inverse CDF of
+    their own words; a partial last group draws each value on its own."""
+    pos = np.array([0, 5, -3], dtype=np.int32)
+    V = 8 * 37 + 5
+    g = noise.noise(9, pos, V)
+    w = noise.group_words(9, pos, 37)
+    u = noise.uniforms(noise.hash_words(9, pos, V))
+    um = noise.uniforms(w)
+    for r in range(len(pos)):
+        for c in range(37):
+            js = int(w[r, c]) & 7
+            for j in range(8):
+                i = 8 * c + j
+                if j == js:
+                    want = -math.log(-math.log(um[r, c]) / 8)
+                else:
+                    want = -math.log(-(math.log(u[r, i]) + math.log(um[r, c]) / 8))
+                    assert g[r, i] < g[r, 8 * c + js]
+                assert g[r, i] == pytest.approx(want, rel=1e-13, abs=1e-13)
+    np.testing.assert_array_equal(g[:, 8 * 37:], noise.gumbel(u[:, 8 * 37:]))
+    # the group key differs from the row key: group words are not element words
+    assert not np.any(noise.group_words(9, pos, 37) == noise.hash_words(9, pos, 37))
+
+
+def test_grouped_noise_tests_reject_plausible_mistakes():
+    """The law tests above have the power to catch a wrong construction: a maximum without the
+    ln 8 shift, or a truncation at the maximum's own uniform instead of its 1/8 power."""
+    R, V = 256, 4096
+    pos = np.arange(R, dtype=np.int32)
+    w = noise.group_words(77, pos, V // 8)
+    u = noise.uniforms(noise.hash_words(77, pos, V)).reshape(R, V // 8, 8)
+    um = noise.uniforms(w)[:, :, None]
+    js = (w & 7).astype(np.int64)[:, :, None]
+    no_shift = -np.log(-(np.log(u) + np.log(um)))
+    np.put_along_axis(no_shift, js, -np.log(-np.log(um)), axis=2)
+    assert _gumbel_ks(no_shift) < 1e-6
+    wrong_trunc = -np.log(-(np.log(u) + np.log(um)))
+    np.put_along_axis(wrong_trunc, js, -np.log(-np.log(um) / 8), axis=2)
+    assert _gumbel_ks(wrong_trunc) < 1e-6

@@ -16,9 +16,15 @@ namespace dv {
 //   A = mix32(seed_hi ^ kSeedSalt), B = mix32(A ^ seed_lo)
 //   key(pos) = mix32(B ^ mix32(pos ^ kPosSalt))
 //   word(pos, i) = mix32(key(pos) ^ (i * kIndexStep))
+// and each full group of kNoiseGroup consecutive indices is drawn largest first
+// from a group word (verify.hip has the construction):
+//   gkey(pos) = mix32(key(pos) ^ kGroupSalt)
+//   gword(pos, c) = mix32(gkey(pos) ^ (c * kIndexStep))
 constexpr uint32_t kSeedSalt = 0x243F6A88u;
 constexpr uint32_t kPosSalt = 0x85A308D3u;
 constexpr uint32_t kIndexStep = 0x9E3779B9u;
+constexpr uint32_t kGroupSalt = 0x6A09E667u;
+constexpr int kNoiseGroup = 8;
 
 // mix32 without its last step (x ^= x >> 16), which leaves the top 16 bits as they are:
 // mix32(x) >> 16 == mix32_head(x) >> 16

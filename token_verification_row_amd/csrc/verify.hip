@@ -124,8 +124,42 @@ __device__ __forceinline__ uint32_t row_key(uint32_t seed_b, int32_t pos) {
   return mix32(seed_b ^ mix32(static_cast<uint32_t>(pos) ^ kPosSalt));
 }
 
-__device__ __forceinline__ float noise_at(uint32_t key, uint32_t i) {
-  return gumbel_log2(mix32(key ^ (i * kIndexStep)));
+// The noise of a row is drawn in groups of kNoiseGroup = 8 consecutive vocabulary indices,
+// largest first: a full group's maximum, G_max = -log2(-log2(u_max) / 8) (the law of the
+// largest of 8 independent Gumbels), sits at place w & 7 of its group word w; every other
+// index takes the Gumbel truncated below that maximum at its own uniform u,
+// G = -log2(-(log2 u + log2(u_max) / 8)). Together these are 8 independent Gumbels. A partial
+// last group draws each index on its own. The key pair of a row: kw for the index words, kg
+// for the group words.
+struct NoiseKey {
+  uint32_t kw, kg;
+};
+
+__device__ __forceinline__ NoiseKey noise_key(uint32_t kw) { return NoiseKey{kw, mix32(kw ^ kGroupSalt)}; }
+
+// uniform of a hash word: 23 bits as the mantissa of a float in [1, 2), minus 1 - 2^-24 (exact)
+__device__ __forceinline__ float uniform_of(uint32_t h) {
+  return __uint_as_float(0x3F800000u | (h >> 9)) - kOneMinusHalfUlp;
+}
+
+// log2(u_max) / 8 of a group word (exact scaling of the hardware log2)
+__device__ __forceinline__ float group_lm8(uint32_t w) { return __builtin_amdgcn_logf(uniform_of(w)) * 0.125f; }
+__device__ __forceinline__ float group_max_g(float lm8) { return -__builtin_amdgcn_logf(-lm8); }
+__device__ __forceinline__ float truncated_g(uint32_t h, float lm8) {
+  return -__builtin_amdgcn_logf(-(__builtin_amdgcn_logf(uniform_of(h)) + lm8));
+}
+__device__ __forceinline__ bool full_group(uint32_t grp, int64_t vocab) {
+  return (static_cast<int64_t>(grp) + 1) * kNoiseGroup <= vocab;
+}
+
+// The noise of vocabulary index i, computed exactly as noise_chunk computes it.
+__device__ __forceinline__ float noise_at(const NoiseKey &k, uint32_t i, int64_t vocab) {
+  const uint32_t grp = i / kNoiseGroup;
+  if (!full_group(grp, vocab)) return gumbel_log2(mix32(k.kw ^ (i * kIndexStep)));
+  const uint32_t w = mix32(k.kg ^ (grp * kIndexStep));
+  const float lm8 = group_lm8(w);
+  if ((i & (kNoiseGroup - 1)) == (w & (kNoiseGroup - 1))) return group_max_g(lm8);
+  return truncated_g(mix32(k.kw ^ (i * kIndexStep)), lm8);
 }
 
 __device__ __forceinline__ int32_t position_of(const VerifyLaunch &p, int64_t r) {
@@ -162,12 +196,28 @@ __device__ __forceinline__ void widen(const u32x4 &w, float (&x)[Chunk<BF16>::N]
   }
 }
 
+// The noise of the N elements of chunk c (one group word per chunk: a chunk never spans two
+// groups, since N divides the group size).
 template <bool BF16>
-__device__ __forceinline__ void noise_chunk(float (&g)[Chunk<BF16>::N], int32_t c, uint32_t key) {
+__device__ __forceinline__ void noise_chunk(float (&g)[Chunk<BF16>::N], int32_t c, const NoiseKey &k, int64_t vocab) {
   constexpr int N = Chunk<BF16>::N;
+  static_assert(kNoiseGroup % N == 0, "a chunk lies inside one noise group");
   const uint32_t i0 = static_cast<uint32_t>(c) * N;
+  const uint32_t grp = i0 / kNoiseGroup;
+  if (full_group(grp, vocab)) {
+    const uint32_t w = mix32(k.kg ^ (grp * kIndexStep));
+    const float lm8 = group_lm8(w);
+    const float gmax = group_max_g(lm8);
+    const uint32_t js = w & (kNoiseGroup - 1);
 #pragma unroll
-  for (int j = 0; j < N; ++j) g[j] = noise_at(key, i0 + j);
+    for (int j = 0; j < N; ++j) {
+      const uint32_t i = i0 + j;
+      g[j] = (i & (kNoiseGroup - 1)) == js ? gmax : truncated_g(mix32(k.kw ^ (i * kIndexStep)), lm8);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < N; ++j) g[j] = gumbel_log2(mix32(k.kw ^ ((i0 + j) * kIndexStep)));
+  }
 }
 
 // Upper bound of the noise of chunk c: u, and with it G, grows with the hash
@@ -186,16 +236,21 @@ __device__ __forceinline__ uint32_t key_in_vgpr(uint32_t key) {
   return key;
 }
 
-// The bound needs only an upper bound of the chunk's largest hash word. The last step of
-// the hash keeps a word's top 16 bits, so the largest word before that step, with its low
-// 16 bits set, is one: two operations fewer per element, and the noise value it gives
-// exceeds the chunk's largest by at most a 2^-16 step of u.
+// Upper bound of the noise of chunk c (every element valid). In a full group it is the
+// group's maximum itself, from one hash word, plus the slack that covers a hardware log2
+// that is not exactly monotone. In a partial group the bound needs only an upper bound of
+// the chunk's largest index word: the last step of the hash keeps a word's top 16 bits, so
+// the largest word before that step, with its low 16 bits set, is one.
+__device__ __forceinline__ float with_slack(float g) { return g + __builtin_fabsf(g) * 0x1p-20f + 0x1p-20f; }
+
 template <int N>
-__device__ __forceinline__ float chunk_noise_bound(int32_t c, uint32_t key) {
+__device__ __forceinline__ float chunk_noise_bound(int32_t c, const NoiseKey &k, int64_t vocab) {
   const uint32_t i0 = static_cast<uint32_t>(c) * N;
+  const uint32_t grp = i0 / kNoiseGroup;
+  if (full_group(grp, vocab)) return with_slack(group_max_g(group_lm8(mix32(k.kg ^ (grp * kIndexStep)))));
   uint32_t hm = 0;
 #pragma unroll
-  for (int j = 0; j < N; ++j) hm = max(hm, mix32_head(key ^ ((i0 + j) * kIndexStep)));
+  for (int j = 0; j < N; ++j) hm = max(hm, mix32_head(k.kw ^ ((i0 + j) * kIndexStep)));
   return noise_bound_of_word(hm | 0xFFFFu);
 }
 
@@ -419,8 +474,8 @@ __device__ __forceinline__ void fold_stats(Lane &st, float (&a)[N], float (&b)[N
 // Chunks reach the token bookkeeping out of index order (queued scoring), so
 // ties compare chunk indices.
 template <bool BF16, int MODE, bool MASKED, bool EXT>
-__device__ __forceinline__ void fold_chunk(Lane &st, const u32x4 &wa, const u32x4 &wb, int32_t c, uint32_t key,
-                                           float cT, int nvalid) {
+__device__ __forceinline__ void fold_chunk(Lane &st, const u32x4 &wa, const u32x4 &wb, int32_t c, const NoiseKey &key,
+                                           int64_t vocab, float cT, int nvalid) {
   constexpr int N = Chunk<BF16>::N;
   float x[N], y[N], cma, cmb;
   widen<BF16>(wa, x);
@@ -428,7 +483,7 @@ __device__ __forceinline__ void fold_chunk(Lane &st, const u32x4 &wa, const u32x
   fold_stats<N, MASKED, EXT>(st, x, y, c, nvalid, cma, cmb);
   if constexpr (MODE != kGreedy) {
     float g[N];
-    noise_chunk<BF16>(g, c, key);
+    noise_chunk<BF16>(g, c, key, vocab);
     fold_tokens<N, MASKED, true>(st, x, y, g, c, cT, nvalid);
   }
 }
@@ -442,7 +497,8 @@ struct ScoreQueue {
 
 // Score the queued chunks, one per lane, and raise the wave's bounds.
 template <bool BF16>
-__device__ __forceinline__ void flush_queue(Lane &st, ScoreQueue &q, int n, uint32_t key, float cT, int lane) {
+__device__ __forceinline__ void flush_queue(Lane &st, ScoreQueue &q, int n, const NoiseKey &key, int64_t vocab, float cT,
+                                            int lane) {
   constexpr int N = Chunk<BF16>::N;
   __builtin_amdgcn_wave_barrier();  // lanes read entries other lanes of the wave wrote
   if (lane < n) {
@@ -450,7 +506,7 @@ __device__ __forceinline__ void flush_queue(Lane &st, ScoreQueue &q, int n, uint
     float x[N], y[N], g[N];
     widen<BF16>(q.a[lane], x);
     widen<BF16>(q.b[lane], y);
-    noise_chunk<BF16>(g, c, key);
+    noise_chunk<BF16>(g, c, key, vocab);
     fold_tokens<N, false, true>(st, x, y, g, c, cT, N);
   }
   st.wb_v = wave_max(st.s_v);
@@ -485,8 +541,8 @@ struct StepRegs {
   // the end of the slice ran the loop with the others but fold nothing). The
   // queue operations are wave-wide, so every lane must reach them.
   template <int MODE>
-  __device__ __forceinline__ void fold(Lane &st, int32_t c, int32_t cend, uint32_t key, float cT, ScoreQueue *q,
-                                       int &nq, int lane) const {
+  __device__ __forceinline__ void fold(Lane &st, int32_t c, int32_t cend, const NoiseKey &key, int64_t vocab, float cT,
+                                       ScoreQueue *q, int &nq, int lane) const {
     constexpr int N = Chunk<BF16>::N;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
@@ -503,14 +559,14 @@ struct StepRegs {
           widen<BF16>(a[k], x);
           widen<BF16>(b[k], y);
           fold_stats<N, false, EXT>(st, x, y, ck, N, cma, cmb);
-          const float g = MODE == kTableBound ? gm[k] : chunk_noise_bound<N>(ck, key);
+          const float g = MODE == kTableBound ? gm[k] : chunk_noise_bound<N>(ck, key, vocab);
           need = __builtin_fmaf(cma, cT, g) >= st.wb_v || __builtin_fmaf(cmb, cT, g) >= st.wb_d;
         }
         const unsigned long long mask = __ballot(need);
         if (mask) {
           const int cnt = __popcll(mask);
           if (nq + cnt > 64) {
-            flush_queue<BF16>(st, *q, nq, key, cT, lane);
+            flush_queue<BF16>(st, *q, nq, key, vocab, cT, lane);
             nq = 0;
           }
           if (need) {
@@ -523,7 +579,7 @@ struct StepRegs {
           nq += cnt;
         }
       } else {
-        if (valid) fold_chunk<BF16, kGreedy, false, EXT>(st, a[k], b[k], ck, key, cT, N);
+        if (valid) fold_chunk<BF16, kGreedy, false, EXT>(st, a[k], b[k], ck, key, vocab, cT, N);
       }
     }
   }
@@ -540,7 +596,7 @@ struct StepRegs {
 // copy forces a wait at the back edge.
 template <bool BF16, int MODE, bool EXT>
 __device__ __forceinline__ void scan_slice(Lane &st, const u32x4 *ra, const u32x4 *rb, int32_t c0, int32_t c1,
-                                           int32_t nfull, int nvalid_tail, float cT, uint32_t key,
+                                           int32_t nfull, int nvalid_tail, float cT, const NoiseKey &key, int64_t vocab,
                                            const float *g_cmax, ScoreQueue *q, int lane) {
   constexpr int32_t kSpan = 64 * kStep;
   const int32_t cend = c1 < nfull ? c1 : nfull;  // whole chunks of the slice
@@ -555,23 +611,23 @@ __device__ __forceinline__ void scan_slice(Lane &st, const u32x4 *ra, const u32x
     for (int32_t t = 0;;) {
       ++t;
       Y.load(ra, rb, g_cmax, t < nsteps ? c + kSpan : c, at);
-      X.template fold<MODE>(st, c, cend, key, cT, q, nq, lane);
+      X.template fold<MODE>(st, c, cend, key, vocab, cT, q, nq, lane);
       if (t == nsteps) break;
       c += kSpan;
       ++t;
       X.load(ra, rb, g_cmax, t < nsteps ? c + kSpan : c, at);
-      Y.template fold<MODE>(st, c, cend, key, cT, q, nq, lane);
+      Y.template fold<MODE>(st, c, cend, key, vocab, cT, q, nq, lane);
       if (t == nsteps) break;
       c += kSpan;
     }
   }
   if constexpr (MODE != kGreedy) {
-    if (nq > 0) flush_queue<BF16>(st, *q, nq, key, cT, lane);
+    if (nq > 0) flush_queue<BF16>(st, *q, nq, key, vocab, cT, lane);
   }
   // the last, partly filled chunk of the row (vocab not a multiple of N)
   if (nvalid_tail > 0 && nfull >= c0 && nfull < c1 && lane == ((nfull - c0) & 63))
     fold_chunk<BF16, MODE, true, EXT>(st, read_chunk<BF16, EXT>(ra + nfull), read_chunk<BF16, EXT>(rb + nfull), nfull, key,
-                                      cT, nvalid_tail);
+                                      vocab, cT, nvalid_tail);
 }
 
 // Reduce the lane states of a wave into one partial (valid in every lane).
@@ -622,7 +678,7 @@ __device__ __forceinline__ Partial wave_reduce(const Lane &st) {
 // is not supported) gives -1 without touching memory.
 template <bool BF16, bool SCORE, bool EXT>
 __device__ __forceinline__ int32_t refine_in_chunk(const u32x4 *row, int32_t c, float target, int64_t vocab, float cT,
-                                                   uint32_t key, int lane) {
+                                                   const NoiseKey &key, int lane) {
   constexpr int N = Chunk<BF16>::N;
   if (c < 0 || static_cast<int64_t>(c) * N >= vocab) return -1;
   float x[N];
@@ -633,7 +689,7 @@ __device__ __forceinline__ int32_t refine_in_chunk(const u32x4 *row, int32_t c, 
   const int64_t i = static_cast<int64_t>(c) * N + lane;
   bool hit = false;
   if (lane < N && i < vocab) {
-    if constexpr (SCORE) v = __builtin_fmaf(v, cT, noise_at(key, static_cast<uint32_t>(i)));
+    if constexpr (SCORE) v = __builtin_fmaf(v, cT, noise_at(key, static_cast<uint32_t>(i), vocab));
     hit = v == target;
   }
   const unsigned long long m = __ballot(hit);
@@ -653,15 +709,15 @@ __device__ void finalize_row(const VerifyLaunch &p, int64_t r, const Partial &t,
   const bool want_am = o.argmax_v || o.argmax_d || (p.greedy && (o.tok_v || want_tok_d));
   int32_t am_v = 0, am_d = 0, tk_v = 0, tk_d = 0;
   if (want_am) {
-    am_v = refine_in_chunk<BF16, false, EXT>(ra, t.cm_v, t.m_v, p.vocab, 0.0f, 0u, lane);
-    am_d = refine_in_chunk<BF16, false, EXT>(rb, t.cm_d, t.m_d, p.vocab, 0.0f, 0u, lane);
+    am_v = refine_in_chunk<BF16, false, EXT>(ra, t.cm_v, t.m_v, p.vocab, 0.0f, NoiseKey{0u, 0u}, lane);
+    am_d = refine_in_chunk<BF16, false, EXT>(rb, t.cm_d, t.m_d, p.vocab, 0.0f, NoiseKey{0u, 0u}, lane);
   }
   if (o.tok_v || want_tok_d) {
     if (p.greedy) {
       tk_v = am_v;
       tk_d = am_d;
     } else {
-      const uint32_t key = row_key(p.seed_b, position_of(p, r));
+      const NoiseKey key = noise_key(row_key(p.seed_b, position_of(p, r)));
       if (o.tok_v) tk_v = refine_in_chunk<BF16, true, EXT>(ra, t.cs_v, t.s_v, p.vocab, p.cT, key, lane);
       if (want_tok_d) tk_d = refine_in_chunk<BF16, true, EXT>(rb, t.cs_d, t.s_d, p.vocab, p.cT, key, lane);
     }
@@ -756,9 +812,10 @@ __global__ __launch_bounds__(1024) void verify_rows_kernel(VerifyLaunch p) {
     const u32x4 *ra = reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.va) + r * row_bytes);
     const u32x4 *rb = reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.vb) + r * row_bytes);
     const int32_t pos = MODE == kGreedy ? 0 : position_of(p, r);
-    const uint32_t key = MODE == kGreedy ? 0u : row_key(p.seed_b, pos);
+    NoiseKey key = MODE == kGreedy ? NoiseKey{0u, 0u} : noise_key(row_key(p.seed_b, pos));
+    if constexpr (MODE == kHashBound) key = NoiseKey{key_in_vgpr(key.kw), key_in_vgpr(key.kg)};
     const float *gcm = MODE == kTableBound ? p.noise_cmax + static_cast<int64_t>(pos) * p.cmax_ld : nullptr;
-    scan_slice<BF16, MODE, EXT>(st, ra, rb, c0, c1, nfull, nvalid_tail, p.cT, MODE == kHashBound ? key_in_vgpr(key) : key, gcm,
+    scan_slice<BF16, MODE, EXT>(st, ra, rb, c0, c1, nfull, nvalid_tail, p.cT, key, p.vocab, gcm,
                            MODE == kGreedy ? nullptr : &lds[wave].q, lane);
   }
   const Partial t = wave_reduce(st);
@@ -794,30 +851,38 @@ __global__ __launch_bounds__(1024) void verify_rows_kernel(VerifyLaunch p) {
 }
 
 // Chunk-max noise table: entry (q, c) bounds the noise of position q over the
-// valid elements of chunk c, as chunk_noise_bound does in registers (from the
-// hash words without their last step). Each thread fills kCmaxPerThread entries
-// of one position, 256 apart, so that a launch has few workgroups. Entries
-// number below 2^28 (the table is at most 1 GiB).
+// valid elements of chunk c, as chunk_noise_bound does in registers: a full
+// group's maximum from its group word, or for the partial last group the largest
+// index word without the hash's last step. Each thread fills kCmaxPerThread
+// entries of one position, 256 apart, so that a launch has few workgroups.
+// Entries number below 2^28 (the table is at most 1 GiB).
 // Grid: x covers the chunks of a position, y the positions (strided past 65535), so
-// the position's key is uniform across the workgroup (scalar unit) and no thread divides.
+// the position's keys are uniform across the workgroup (scalar unit) and no thread divides.
 constexpr uint32_t kCmaxPerThread = 4;
 
 template <int N>
 __global__ __launch_bounds__(256) void noise_cmax_kernel(uint32_t seed_b, uint32_t rows, uint32_t ld, int64_t vocab,
                                                         float *cmax) {
   for (uint32_t q = blockIdx.y; q < rows; q += gridDim.y) {
-    const uint32_t key = row_key(seed_b, static_cast<int32_t>(q));
+    const NoiseKey key = noise_key(row_key(seed_b, static_cast<int32_t>(q)));
 #pragma unroll
     for (uint32_t k = 0; k < kCmaxPerThread; ++k) {
       const uint32_t c = (blockIdx.x * kCmaxPerThread + k) * 256u + threadIdx.x;
       if (c >= ld) break;
-      uint32_t hm = 0;
+      const uint32_t grp = c * N / kNoiseGroup;  // vocab < 2^31
+      float bound;
+      if (full_group(grp, vocab)) {
+        bound = with_slack(group_max_g(group_lm8(mix32(key.kg ^ (grp * kIndexStep)))));
+      } else {
+        uint32_t hm = 0;
 #pragma unroll
-      for (int j = 0; j < N; ++j) {
-        const uint32_t i = c * N + j;  // vocab < 2^31
-        if (i < vocab) hm = max(hm, mix32_head(key ^ (i * kIndexStep)));
+        for (int j = 0; j < N; ++j) {
+          const uint32_t i = c * N + j;
+          if (i < vocab) hm = max(hm, mix32_head(key.kw ^ (i * kIndexStep)));
+        }
+        bound = noise_bound_of_word(hm | 0xFFFFu);
       }
-      cmax[static_cast<size_t>(q) * ld + c] = noise_bound_of_word(hm | 0xFFFFu);
+      cmax[static_cast<size_t>(q) * ld + c] = bound;
     }
   }
 }

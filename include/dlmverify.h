@@ -82,6 +82,13 @@ typedef struct dv_logits {
 /* Shared Gumbel noise ([SPOT] §1 and §3, coupled-noise verification): at
  * temperature > 0 both models draw token argmax_i(x_i / T + g_i) with the SAME
  * standard Gumbel g_i, which depends only on (seed, position, vocabulary index).
+ * The g_i are drawn from counter hash words (DV_HASH_V1: MurmurHash3's 32-bit
+ * finalizer over (seed, position, index)), in groups of 8 consecutive indices
+ * largest first (DV_NOISE_V2): a full group's maximum, Gumbel shifted by ln 8,
+ * sits at a place given by the group's own hash word, and the other seven are
+ * Gumbel truncated below it at their index words' uniforms; the indices of a
+ * partial last group draw on their own. In law these are i.i.d. standard
+ * Gumbel values, so the tokens are exact samples of softmax(x / T).
  * temperature == 0 means greedy decoding (token = argmax, no noise).
  * Position of row r: pos[r] when pos != NULL (device int32 [rows]); else
  * r % pos_period when pos_period > 0; else r. Rows with equal positions see
@@ -357,9 +364,9 @@ dv_status dv_dual_view_attention(const dv_dual_view_args *args, const void *q, c
                                  const void *v_cur, const void *k_prev, const void *v_prev,
                                  const uint8_t *seed, float *out, hipStream_t stream);
 
-/* The noise hash words h[r][i] (uint32, device [rows][vocab]) for the
- * positions described as in dv_noise. For testing the noise generator bit
- * for bit. Errors: DV_ERR_NULL, DV_ERR_SHAPE. */
+/* The index hash words h[r][i] (uint32, device [rows][vocab], DV_HASH_V1)
+ * for the positions described as in dv_noise. For testing the noise generator
+ * bit for bit. Errors: DV_ERR_NULL, DV_ERR_SHAPE. */
 dv_status dv_debug_hash(uint64_t seed, const int32_t *pos, int64_t pos_period, int64_t rows,
                         int64_t vocab, uint32_t *out, hipStream_t stream);
 

@@ -1,7 +1,9 @@
 """CPU checks of the arithmetic behind the Gumbel pruning bound of the verify kernel.
 
 The kernel skips scoring a 16-byte chunk when max(x)/T plus an upper bound of the
-chunk's noise cannot reach the best score seen. That bound is taken from the largest
+chunk's noise cannot reach the best score seen. In a full noise group of 8 indices
+the bound is the group's maximum, which its group word gives directly; in a partial
+last group, whose indices draw on their own, it is taken from the largest index
 hash word of the chunk, computed without the finalizer's last step
 (x ^= x >> 16): the step keeps the top 16 bits, so the largest word before it, with
 its low 16 bits set, is at least every final word of the chunk, and the uniform

@@ -81,8 +81,8 @@ typedef struct dv_logits {
 
 /* Shared Gumbel noise ([SPOT] §1 and §3, coupled-noise verification): at
  * temperature > 0 both models draw token argmax_i(x_i / T + g_i) with the SAME
- * standard Gumbel g_i, which depends only on (seed, position, vocabulary index).
- * The g_i are drawn from counter hash words (DV_HASH_V1: MurmurHash3's 32-bit
+ * standard Gumbel g_i, which depends only on (seed, position, vocabulary index)
+ * and, for the indices of a partial last group, on the vocabulary size. The g_i are drawn from counter hash words (DV_HASH_V1: MurmurHash3's 32-bit
  * finalizer over (seed, position, index)), in groups of 8 consecutive indices
  * largest first (DV_NOISE_V2): a full group's maximum, Gumbel shifted by ln 8,
  * sits at a place given by the group's own hash word, and the other seven are

@@ -54,14 +54,15 @@ def measured_traffic(workload: int):
 
 
 def _oracle_block(args):
-    """CPU oracle over a block of rows (runs in a worker process)."""
-    a, b, temperature, seed, pos, group_len = args
+    """CPU oracle over a block of rows (runs in a worker process): row statistics, shared-noise tokens and,
+    for candidate workloads, coupled acceptance."""
+    a, b, dtype, temperature, seed, pos, group_len = args
     from oracle import decide as odecide
     from oracle import noise as onoise
     from oracle import rowstats
 
-    a64 = rowstats.as_float64(a, "bf16")
-    b64 = rowstats.as_float64(b, "bf16")
+    a64 = rowstats.as_float64(a, dtype)
+    b64 = rowstats.as_float64(b, dtype)
     st = rowstats.row_stats(a64, b64)
     st.update(onoise.gumbel_tokens(a64, b64, temperature, seed, pos))
     if group_len:
@@ -131,20 +132,78 @@ def synthetic_attention(maps, length, dev):
     return probs, qm, nc
 
 
-def cpu_baseline(a_rows, b_rows, w, pos, workers):
-    """Time the oracle (as it is) on the given rows across ``workers`` processes."""
+def oracle_sample(w, dev, n):
+    """The first n rows of workload w as the device holds them (bf16 bits or float32), and their positions."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+
+    seqs = range(-(-n // w.L))
+    a, b = W.make_logits_torch(w, dev, seqs=seqs)
+    view = (lambda t: t[:n].view(torch.int16).cpu().numpy().view(np.uint16)) if w.dtype == "bf16" else \
+        (lambda t: t[:n].cpu().numpy())
+    return view(a), view(b), W.positions(w)[:n]
+
+
+def cpu_baseline(a_rows, b_rows, w, pos, pool, workers):
+    """Time the oracle (as it is) on the given rows across the pool's worker processes; rows/s and wall s."""
+    G = w.group_len or 32
+    tasks = [(a_rows[s:s + G], b_rows[s:s + G], w.dtype, w.temperature, w.seed, pos[s:s + G], w.group_len)
+             for s in range(0, len(a_rows), G)]
+    pool.map(_oracle_block, tasks[:workers])          # warm the workers up (imports, first touches)
+    t0 = time.perf_counter()
+    n = sum(pool.map(_oracle_block, tasks))
+    dt = time.perf_counter() - t0
+    return n, dt
+
+
+def cpu_baselines(w_main, a_main, b_main, pos_main, dev, workers, host_cores):
+    """The oracle timed on the host: the headline workload's sample (the reported value), a sample of every
+    other workload, and workload 1 whole on a single core."""
     import multiprocessing as mp
 
-    G = w.group_len or 32
-    tasks = [(a_rows[s:s + G], b_rows[s:s + G], w.temperature, w.seed, pos[s:s + G], w.group_len)
-             for s in range(0, len(a_rows), G)]
-    ctx = mp.get_context("spawn")
-    with ctx.Pool(workers) as pool:
-        pool.map(_oracle_block, tasks[:workers])          # warm the workers up (imports)
-        t0 = time.perf_counter()
-        n = sum(pool.map(_oracle_block, tasks))
-        dt = time.perf_counter() - t0
-    return n, dt
+    import workloads as W
+
+    samples = {2: 256, 3: 256, 4: 512, 5: 512}
+    per = {}
+    with mp.get_context("spawn").Pool(workers) as pool:
+        done, dt = cpu_baseline(a_main, b_main, w_main, pos_main, pool, workers)
+        main = {"value": done / dt, "unit": "rows/s", "cores": workers, "host_cores": host_cores,
+                "workers": workers, "kind": "oracle",
+                "sample": f"first {done} rows ({done // (w_main.group_len or w_main.L) or 1} "
+                          f"{'candidates' if w_main.group_len else 'sequences'}) of the same workload: row "
+                          f"statistics, shared-Gumbel tokens{' and coupled acceptance' if w_main.group_len else ''} "
+                          f"in float64, {workers} worker processes, {dt:.1f} s wall"}
+        for num, n in samples.items():
+            if num == w_main.number:
+                per[str(num)] = {"rows": done, "rows_per_s": done / dt, "wall_s": dt}
+                continue
+            w = W.workload(num)
+            a, b, pos = oracle_sample(w, dev, n)
+            m, t = cpu_baseline(a, b, w, pos, pool, workers)
+            per[str(num)] = {"rows": m, "rows_per_s": m / t, "wall_s": t}
+    w1 = W.workload(1)
+    a, b = W.make_logits_numpy(w1)
+    t0 = time.perf_counter()
+    _oracle_block((a, b, "fp32", w1.temperature, w1.seed, W.positions(w1), 0))
+    t1 = time.perf_counter() - t0
+    per["1"] = {"rows": w1.rows, "rows_per_s": w1.rows / t1, "wall_s": t1, "cores": 1}
+    main["per_workload"] = per
+    return main
+
+
+def _durations_us(pairs):
+    import numpy as np
+
+    return np.array([1000.0 * a.elapsed_time(b) for a, b in pairs])
+
+
+def _summary(us):
+    import numpy as np
+
+    return {"median_us": float(np.median(us)), "mean_us": float(np.mean(us)), "min_us": float(np.min(us)),
+            "max_us": float(np.max(us))}
 
 
 def main() -> int:
@@ -152,6 +211,10 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup-seconds", type=float, default=1.0,
+                    help="after the --warmup steps, keep running untimed steps until this much wall time has "
+                         "passed since warm-up began: the device's clocks take several milliseconds of sustained "
+                         "load to settle, longer than a few steps")
     ap.add_argument("--workload", type=int, default=4, choices=[2, 3, 4, 5])
     ap.add_argument("--cpu-rows", type=int, default=1024, help="rows of the workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -172,6 +235,9 @@ def main() -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the path, run a plain device copy of MIB MiB --steps times (reference for "
                          "the HBM byte counters of a profiler)")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="instead of the path, time the read-only streaming probe (dv_debug_read_probe) over the "
+                         "workload's logits in the verify pass's launch shape: the attainable read rate")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; the verification path has no multi-GPU mode (asked for --gpus {args.gpus})",
@@ -205,6 +271,38 @@ def main() -> int:
     inputs = [W.make_logits_torch(w, dev)]
     for _ in range(copies - 1):
         inputs.append((inputs[0][0].clone(), inputs[0][1].clone()))
+    stream = torch.cuda.current_stream(dev)
+    read_bytes = 2 * R * V * w.elt
+
+    def warm(run_one):
+        """--warmup steps, then more until --warmup-seconds of wall time have passed; returns the count."""
+        t0 = time.perf_counter()
+        i = 0
+        while i < args.warmup or time.perf_counter() - t0 < args.warmup_seconds:
+            run_one(i)
+            i += 1
+            if i % 64 == 0:
+                torch.cuda.synchronize()        # keep the queue short so the wall clock tracks the device
+        torch.cuda.synchronize()
+        return i
+
+    if args.read_probe:
+        sink = torch.empty((R, 16), dtype=torch.int32, device=dev)
+        n_warm = warm(lambda i: dv.dv_debug_read_probe(*inputs[i % copies], sink=sink))
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            dv.dv_debug_read_probe(*inputs[i % copies], sink=sink)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        st = _summary(_durations_us(ev))
+        print(json.dumps({"read_probe": {"workload": w.name, "rows": R, "vocab": V, "bytes_per_launch": read_bytes,
+                                         "steps": args.steps, "warmup_steps_run": n_warm, **st,
+                                         "GBps_median": read_bytes / (st["median_us"] * 1e-6) / 1e9,
+                                         "frac_of_8TBps": read_bytes / (st["median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS}}),
+              flush=True)
+        return 0
+
     period = w.pos_period
     d_in_np, d_out_np = W.diffusion_inputs(w) if w.n_committed else \
         tuple(np.random.default_rng(1).random(R, dtype=np.float32) for _ in range(2))
@@ -212,12 +310,12 @@ def main() -> int:
     d_out = torch.from_numpy(np.ascontiguousarray(d_out_np, np.float32)).to(dev)
     committed = torch.from_numpy(W.committed_rows(w)).to(dev) if w.n_committed else None
     vkw = {"outputs": dv.STAT_FIELDS, "neg_inf": True} if args.extended else {}
-    outs = [dv.dv_verify_rows(*inputs[0], temperature=w.temperature, seed=w.seed, pos_period=period, **vkw)
-            for _ in range(2)]
+    # two prepared verify calls with their own outputs and workspace, used in turn
+    plans = [dv.VerifyPlan(*inputs[0], temperature=w.temperature, seed=w.seed, pos_period=period, **vkw)
+             for _ in range(2)]
     seq_len = w.group_len or w.L
     nseq = R // seq_len
     k = min(w.topk or 8, seq_len)
-    stream = torch.cuda.current_stream(dev)
     att = None
     if args.influence:
         if not w.n_committed:
@@ -236,34 +334,28 @@ def main() -> int:
         if not w.group_len:
             print("--tree needs a workload of candidate block states (workload 4)", file=sys.stderr)
             return 2
-        tree = synthetic_tree(outs[0], nseq, seq_len, dev)
+        tree = synthetic_tree(plans[0](*inputs[0]), nseq, seq_len, dev)
+
+    def timed(ev_list, fn):
+        if ev_list is None:
+            return fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        r = fn()
+        e1.record(stream)
+        ev_list.append((e0, e1))
+        return r
 
     def step(i, ev=None):
         """verify -> decide -> seed score -> select, with the workload's own rule and selection score."""
         a, b = inputs[i % copies]
-        out = outs[i % 2]
+        plan = plans[i % 2]
         if dv_in is not None:
-            if ev is not None:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-            dv.dv_dual_view_attention(*dv_in, out=dv_out)
-            if ev is not None:
-                e1.record(stream)
-                dv_ev.append((e0, e1))
-        if ev is not None:
-            ev[0].record(stream)
-        got = dv.dv_verify_rows(a, b, temperature=w.temperature, seed=w.seed, pos_period=period, out=out, **vkw,
-                                workspace=out.get("_workspace"))
-        if ev is not None:
-            ev[1].record(stream)
+            timed(dv_ev if ev is not None else None, lambda: dv.dv_dual_view_attention(*dv_in, out=dv_out))
+        got = timed(ev, lambda: plan(a, b))
         if att is not None:
-            if ev is not None:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-            di, do = dv.dv_influence_drift(*att, workspace=att_ws)
-            if ev is not None:
-                e1.record(stream)
-                att_ev.append((e0, e1))
+            di, do = timed(att_ev if ev is not None else None,
+                           lambda: dv.dv_influence_drift(*att, workspace=att_ws))
             score = dv.dv_seed_score(got["entropy"], di.view(-1), do.view(-1), committed)
         else:
             score = dv.dv_seed_score(got["entropy"], d_in, d_out, committed)
@@ -283,24 +375,21 @@ def main() -> int:
         # workload 5 ranks positions by KL; the others by the seed score
         dv.dv_select_topk((got["kl"] if w.number == 5 else score).view(nseq, seq_len), k)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    n_warm = warm(step)
+    events = []
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i, events[i])
+        step(n_warm + i, events)
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
-    verify_ms = [s.elapsed_time(e) for s, e in events]
+    verify = _summary(_durations_us(events))
     ms_per_step = ms_total / args.steps
-    verify_us = 1000.0 * float(np.mean(verify_ms))
-    alg_bytes = 2 * R * V * w.elt + (EXT_STAT_BYTES_PER_ROW if args.extended else STAT_BYTES_PER_ROW) * R
-    achieved = alg_bytes / (verify_us * 1e-6) / 1e9
+    alg_bytes = read_bytes + (EXT_STAT_BYTES_PER_ROW if args.extended else STAT_BYTES_PER_ROW) * R
+    achieved = alg_bytes / (verify["median_us"] * 1e-6) / 1e9
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -309,13 +398,11 @@ def main() -> int:
         a_rows = inputs[0][0][rows].view(torch.int16).cpu().numpy().view(np.uint16)
         b_rows = inputs[0][1][rows].view(torch.int16).cpu().numpy().view(np.uint16)
         pos = W.positions(w)[:n]
-        workers = max(1, min(16, len(os.sched_getaffinity(0))))
-        done, dt = cpu_baseline(a_rows, b_rows, w, pos, workers)
-        cpu = {"value": done / dt, "unit": "rows/s", "cores": workers, "kind": "oracle",
-               "sample": f"first {done} rows ({done // (w.group_len or w.L)} "
-                         f"{'candidates' if w.group_len else 'sequences'}) of the same workload: row statistics, "
-                         f"shared-Gumbel tokens{' and coupled acceptance' if w.group_len else ''} in float64, "
-                         f"{workers} worker processes, {dt:.1f} s wall"}
+        host_cores = len(os.sched_getaffinity(0))
+        workers = max(1, min(16, host_cores))
+        del inputs, plans
+        torch.cuda.empty_cache()
+        cpu = cpu_baselines(w, a_rows, b_rows, pos, dev, workers, host_cores)
 
     line = {
         "metric": "verified rows/s and achieved HBM GB/s (% of peak), fused verify kernel",
@@ -324,6 +411,8 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": n_warm,
+        "warmup_seconds": args.warmup_seconds,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -339,7 +428,9 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": None if args.extended else measured_traffic(w.number),
                      "kernel": "dv_verify_rows (noise table when rows share positions + streaming verify kernel)",
-                     "avg_us": verify_us,
+                     "timing": "HIP events around each dv_verify_rows call on its stream; achieved from the median",
+                     **verify, "avg_us": verify["mean_us"],
+                     "frac_of_mean": alg_bytes / (verify["mean_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS,
                      "bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
     }
@@ -347,17 +438,20 @@ def main() -> int:
         line["config"]["outputs"] = ("extended: 11 statistics per row incl. KL(p_d||p_v) and p_v(tok_d), "
                                      "-inf logits allowed")
     if dv_in is not None:
-        dv_us = 1000.0 * float(np.mean([a.elapsed_time(b) for a, b in dv_ev]))
+        dv_us = _summary(_durations_us(dv_ev))
         flop = 4.0 * w.B * 28 * w.L * w.L * 128
-        line["dual_view"] = {"nseq": w.B, "heads": 28, "kv_heads": 4, "len": w.L, "head_dim": 128, "avg_us": dv_us,
-                             "flop_per_launch": flop, "achieved_TFLOPs": flop / (dv_us * 1e-6) / 1e12,
-                             "peak_TFLOPs": 2500.0, "frac": flop / (dv_us * 1e-6) / 1e12 / 2500.0}
+        t = dv_us["median_us"] * 1e-6
+        line["dual_view"] = {"nseq": w.B, "heads": 28, "kv_heads": 4, "len": w.L, "head_dim": 128, **dv_us,
+                             "avg_us": dv_us["mean_us"], "flop_per_launch": flop,
+                             "achieved_TFLOPs": flop / t / 1e12, "peak_TFLOPs": 2500.0,
+                             "frac": flop / t / 1e12 / 2500.0}
         line["config"]["step"] = "dv_dual_view_attention + " + line["config"]["step"]
     if att is not None:
-        att_us = 1000.0 * float(np.mean([a.elapsed_time(b) for a, b in att_ev]))
+        att_us = _summary(_durations_us(att_ev))
         att_bytes = att[0].numel() * 2 + 2 * 4 * R
-        line["influence"] = {"maps": args.influence, "len": w.L, "avg_us": att_us, "bytes_per_launch": att_bytes,
-                             "achieved_GBps": att_bytes / (att_us * 1e-6) / 1e9}
+        line["influence"] = {"maps": args.influence, "len": w.L, **att_us, "avg_us": att_us["mean_us"],
+                             "bytes_per_launch": att_bytes,
+                             "achieved_GBps": att_bytes / (att_us["median_us"] * 1e-6) / 1e9}
         line["config"]["step"] = "dv_verify_rows + dv_influence_drift + dv_seed_score + dv_select_topk + dv_decide"
     print(json.dumps(line), flush=True)
     return 0

@@ -366,9 +366,58 @@ dv_status dv_dual_view_attention(const dv_dual_view_args *args, const void *q, c
 
 /* The index hash words h[r][i] (uint32, device [rows][vocab], DV_HASH_V1)
  * for the positions described as in dv_noise. For testing the noise generator
- * bit for bit. Errors: DV_ERR_NULL, DV_ERR_SHAPE. */
+ * bit for bit; the same as dv_debug_noise with DV_DEBUG_INDEX_WORDS.
+ * Errors: DV_ERR_NULL, DV_ERR_SHAPE. */
 dv_status dv_debug_hash(uint64_t seed, const int32_t *pos, int64_t pos_period, int64_t rows,
                         int64_t vocab, uint32_t *out, hipStream_t stream);
+
+/* What dv_debug_noise writes, per row r (positions as in dv_noise). Every
+ * mode is computed by the same device functions the verification kernels use.
+ *   DV_DEBUG_INDEX_WORDS  uint32 [rows][vocab]: index word h of each index
+ *   DV_DEBUG_GROUP_WORDS  uint32 [rows][vocab / 8]: group word w_c of each
+ *                         full group of 8 indices (DV_NOISE_V2, see dv_noise)
+ *   DV_DEBUG_NOISE_LOG2   float32 [rows][vocab]: the Gumbel value of each
+ *                         index in log2 units, G = g log2(e) + log2(ln 2)
+ *                         for the standard Gumbel g the definition gives
+ *   DV_DEBUG_CHUNK_BOUND  float32 [rows][ceil(vocab / chunk_elems)]: the
+ *                         upper bound of a 16-byte chunk's noise that the
+ *                         streaming pass computes in registers (+inf for a
+ *                         partly filled last chunk, which is never bounded)
+ *   DV_DEBUG_TABLE_BOUND  float32 [rows][ceil(vocab / chunk_elems)]: the
+ *                         noise table dv_verify_rows builds in its workspace
+ *                         when rows share positions, over positions
+ *                         0 .. rows-1 (needs pos == NULL, pos_period == 0)
+ * chunk_elems: elements per 16-byte chunk, 8 (bf16 logits) or 4 (fp32). */
+typedef enum dv_debug_noise_mode {
+  DV_DEBUG_INDEX_WORDS = 0,
+  DV_DEBUG_GROUP_WORDS = 1,
+  DV_DEBUG_NOISE_LOG2 = 2,
+  DV_DEBUG_CHUNK_BOUND = 3,
+  DV_DEBUG_TABLE_BOUND = 4
+} dv_debug_noise_mode;
+
+/* Test-only dump of the shared noise and of the bounds the Gumbel pruning
+ * takes from it (modes above), so that the noise can be checked word for word
+ * and the bounds against every value they cover. out: device, the mode's
+ * element type and shape. Errors: DV_ERR_NULL (out NULL with a non-empty
+ * result), DV_ERR_SHAPE (sizes out of range), DV_ERR_ARG (unknown mode,
+ * chunk_elems not 4 or 8, pos or pos_period given with DV_DEBUG_TABLE_BOUND),
+ * DV_ERR_HIP. */
+dv_status dv_debug_noise(uint64_t seed, const int32_t *pos, int64_t pos_period, int64_t rows,
+                         int64_t vocab, int32_t mode, int32_t chunk_elems, void *out,
+                         hipStream_t stream);
+
+/* Measurement-only: a read-only streaming probe over both logit matrices in
+ * dv_verify_rows's launch shape for these sizes (and tuning.split, if given):
+ * the same 16-byte non-temporal loads and wave-per-(row, slice) layout, with
+ * no arithmetic but an xor fold, so that its rate is the read ceiling of the
+ * verify pass's access pattern on the device. Writes an xor of what each wave
+ * read to sink (device uint32 [rows][16], entry [r][slice]; entries of slices
+ * past the row's split are left as they are). Errors: as dv_verify_rows for
+ * the logits; DV_ERR_ARG for tuning.shared_noise = 1; DV_ERR_NULL (sink NULL
+ * with rows > 0). */
+dv_status dv_debug_read_probe(const dv_logits *logits, const dv_tuning *tuning, uint32_t *sink,
+                              hipStream_t stream);
 
 const char *dv_status_str(dv_status status);
 const char *dv_last_error(void);

@@ -31,7 +31,7 @@ def test_exports_every_declared_function(lib):
     names = _declared_functions()
     assert names == sorted(["dv_verify_workspace_bytes", "dv_verify_rows", "dv_decide", "dv_seed_score",
                            "dv_select_topk", "dv_tree_accept", "dv_influence_drift_workspace_bytes",
-                           "dv_influence_drift", "dv_dual_view_attention", "dv_debug_hash", "dv_status_str",
+                           "dv_influence_drift", "dv_dual_view_attention", "dv_debug_hash", "dv_debug_noise", "dv_debug_read_probe", "dv_status_str",
                            "dv_last_error", "dv_version"])
     for n in names:
         assert hasattr(lib, n), n
@@ -174,6 +174,46 @@ def test_seed_score_select_hash_validation(lib):
     assert lib.dv_debug_hash(0, None, -1, 1, 4, FAKE, None) == B.DV_ERR_SHAPE
     assert lib.dv_debug_hash(0, None, 0, 2, 4, None, None) == B.DV_ERR_NULL
     assert lib.dv_debug_hash(0, None, 0, 0, 4, None, None) == B.DV_OK
+
+
+def test_debug_noise_validation(lib):
+    assert lib.dv_debug_noise(0, None, 0, -1, 4, 0, 8, FAKE, None) == B.DV_ERR_SHAPE
+    assert lib.dv_debug_noise(0, None, -1, 1, 4, 0, 8, FAKE, None) == B.DV_ERR_SHAPE
+    assert lib.dv_debug_noise(0, None, 0, 1, 4, 5, 8, FAKE, None) == B.DV_ERR_ARG       # unknown mode
+    assert lib.dv_debug_noise(0, None, 0, 1, 4, -1, 8, FAKE, None) == B.DV_ERR_ARG
+    assert lib.dv_debug_noise(0, None, 0, 1, 4, 0, 2, FAKE, None) == B.DV_ERR_ARG       # chunk_elems
+    assert lib.dv_debug_noise(0, FAKE, 0, 1, 64, 4, 8, FAKE, None) == B.DV_ERR_ARG     # table: positions are rows
+    assert lib.dv_debug_noise(0, None, 3, 1, 64, 4, 8, FAKE, None) == B.DV_ERR_ARG
+    assert lib.dv_debug_noise(0, None, 0, 2, 64, 1, 8, None, None) == B.DV_ERR_NULL
+    # group words of a vocabulary shorter than one group: an empty result, nothing launched
+    assert lib.dv_debug_noise(0, None, 0, 2, 7, 1, 8, None, None) == B.DV_OK
+    assert lib.dv_debug_noise(0, None, 0, 0, 64, 2, 4, None, None) == B.DV_OK
+
+
+def test_read_probe_validation(lib):
+    lg = _logits(rows=4, vocab=64, ld=64)
+    assert lib.dv_debug_read_probe(ctypes.byref(lg), None, None, None) == B.DV_ERR_NULL
+    bad = _logits(rows=4, vocab=64, ld=60)
+    assert lib.dv_debug_read_probe(ctypes.byref(bad), None, FAKE, None) == B.DV_ERR_SHAPE
+    t = B.dv_tuning(split=0, shared_noise=1)
+    assert lib.dv_debug_read_probe(ctypes.byref(lg), ctypes.byref(t), FAKE, None) == B.DV_ERR_ARG
+    t = B.dv_tuning(split=17, shared_noise=0)
+    assert lib.dv_debug_read_probe(ctypes.byref(lg), ctypes.byref(t), FAKE, None) == B.DV_ERR_ARG
+    empty = _logits(rows=0)
+    assert lib.dv_debug_read_probe(ctypes.byref(empty), None, None, None) == B.DV_OK
+
+
+def test_binding_rejects_short_pos(monkeypatch):
+    """A pos tensor with fewer entries than rows is refused before any launch (the kernels would read past it)."""
+    import torch
+
+    monkeypatch.setattr(B, "_need_cuda", lambda t, name: None)   # a CPU tensor stands in for a device one
+    pos = torch.zeros(3, dtype=torch.int32)
+    with pytest.raises(ValueError, match="3 positions for 4 rows"):
+        B._check_pos(pos, 4)
+    B._check_pos(pos, 3)
+    with pytest.raises(TypeError):
+        B._check_pos(torch.zeros(4, dtype=torch.int64), 4)
 
 
 def test_binding_refuses_cpu_tensors():

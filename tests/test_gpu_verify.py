@@ -113,6 +113,26 @@ def test_large_vocab_ragged(dtype, V):
             compare_stats(got, ref, T, f"large vocab {dtype} T={T} period={period} {tuning}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("T", [0.1, 0.02])
+def test_low_temperature_flat_rows(dtype, T):
+    """Small temperatures on flat (unpeaked) rows, where x/T dominates the perturbed score and its float32
+    rounding grows: tokens agree outside the score's rounding band, through the per-row hash bound and the
+    shared-noise table."""
+    print(f"case: low temperature {dtype} T={T}", flush=True)
+    rows, V = 48, 20000
+    rng = np.random.default_rng(int(T * 1000) + (dtype == "fp32"))
+    a = rng.standard_normal((rows, V), dtype=np.float32)
+    b = a + rng.standard_normal((rows, V), dtype=np.float32) * np.float32(0.5)
+    if dtype == "bf16":
+        a, b = W.round_bf16_bits(a), W.round_bf16_bits(b)
+    for period, tuning in ((0, None), (8, {"shared_noise": 1}), (8, {"shared_noise": 0})):
+        got = _run(a, b, dtype, T, seed=13, period=period, tuning=tuning)
+        rep = compare_stats(got, oracle_rows(a, b, dtype, T, 13, _positions(rows, None, period)), T,
+                            f"low T {dtype} T={T} period={period} {tuning}")
+        print(rep, flush=True)
+
+
 def test_explicit_positions_and_period():
     print("case: explicit positions / period", flush=True)
     a, b = _peaked(40, 3001, 11, "bf16")

@@ -426,8 +426,51 @@ dv_status dv_debug_hash(uint64_t seed, const int32_t *pos, int64_t pos_period, i
   if (rows < 0 || rows > kMaxIndex || vocab < 0 || vocab > kMaxIndex) return fail(DV_ERR_SHAPE, "size out of range");
   if (pos_period < 0 || pos_period > kMaxIndex) return fail(DV_ERR_SHAPE, "pos_period out of range");
   if (rows > 0 && vocab > 0 && !out) return fail(DV_ERR_NULL, "out is NULL");
-  return hip_status(dv::launch_debug_hash(dv::seed_word(seed), pos, pos_period, rows, vocab, out, stream),
+  return hip_status(dv::launch_debug_noise(dv::seed_word(seed), pos, pos_period, rows, vocab, DV_DEBUG_INDEX_WORDS, 8,
+                                           out, stream),
                     "dv_debug_hash launch");
+}
+
+dv_status dv_debug_noise(uint64_t seed, const int32_t *pos, int64_t pos_period, int64_t rows, int64_t vocab,
+                         int32_t mode, int32_t chunk_elems, void *out, hipStream_t stream) {
+  if (rows < 0 || rows > kMaxIndex || vocab < 0 || vocab > kMaxIndex) return fail(DV_ERR_SHAPE, "size out of range");
+  if (pos_period < 0 || pos_period > kMaxIndex) return fail(DV_ERR_SHAPE, "pos_period out of range");
+  if (mode < DV_DEBUG_INDEX_WORDS || mode > DV_DEBUG_TABLE_BOUND) return fail(DV_ERR_ARG, "unknown mode %d", mode);
+  if (chunk_elems != 4 && chunk_elems != 8) return fail(DV_ERR_ARG, "chunk_elems must be 4 or 8");
+  if (mode == DV_DEBUG_TABLE_BOUND) {
+    if (pos || pos_period) return fail(DV_ERR_ARG, "the table covers positions 0 .. rows-1: pos must be NULL, pos_period 0");
+    if (rows * ((vocab + chunk_elems - 1) / chunk_elems) >= (int64_t{1} << 28)) return fail(DV_ERR_SHAPE, "table too large");
+  }
+  const int64_t width = mode == DV_DEBUG_GROUP_WORDS ? vocab / 8
+                        : (mode == DV_DEBUG_CHUNK_BOUND || mode == DV_DEBUG_TABLE_BOUND) ? (vocab + chunk_elems - 1) / chunk_elems
+                                                                                        : vocab;
+  if (rows > 0 && width > 0 && !out) return fail(DV_ERR_NULL, "out is NULL");
+  return hip_status(dv::launch_debug_noise(dv::seed_word(seed), pos, pos_period, rows, vocab, mode, chunk_elems, out,
+                                           stream),
+                    "dv_debug_noise launch");
+}
+
+dv_status dv_debug_read_probe(const dv_logits *logits, const dv_tuning *tuning, uint32_t *sink, hipStream_t stream) {
+  dv_status s = check_logits(logits, true);
+  if (s != DV_OK) return s;
+  if (tuning && tuning->shared_noise == 1) return fail(DV_ERR_ARG, "the probe reads no noise table");
+  const dv_noise greedy{};
+  Geometry g;
+  if ((s = choose_geometry(logits, &greedy, tuning, g)) != DV_OK) return s;
+  static_assert(kMaxSplit <= dv::kMaxProbeSplit, "the sink holds a word per slice");
+  if (logits->rows == 0) return ok();
+  if (!sink) return fail(DV_ERR_NULL, "sink is NULL");
+  dv::VerifyLaunch p{};
+  p.va = logits->verifier;
+  p.vb = logits->drafter;
+  p.rows = logits->rows;
+  p.vocab = logits->vocab;
+  p.ld = logits->ld;
+  p.bf16 = logits->dtype == DV_BF16;
+  p.split = g.split;
+  p.slice_chunks = g.slice_chunks;
+  p.rows_per_block = g.rows_per_block;
+  return hip_status(dv::launch_read_probe(p, sink, stream), "dv_debug_read_probe launch");
 }
 
 const char *dv_status_str(dv_status s) {

@@ -88,6 +88,10 @@ struct VerifyLaunch {
 
 hipError_t launch_verify(const VerifyLaunch &p, hipStream_t stream);
 
+// the read-only streaming probe (dv_debug_read_probe): sink holds kMaxProbeSplit words per row
+constexpr int kMaxProbeSplit = 16;
+hipError_t launch_read_probe(const VerifyLaunch &p, uint32_t *sink, hipStream_t stream);
+
 struct DecideLaunch {
   int32_t rule;
   float tau_kl, conf_thr;
@@ -159,7 +163,8 @@ struct DualViewLaunch {
 };
 hipError_t launch_dual_view(const DualViewLaunch &p, hipStream_t stream);
 
-hipError_t launch_debug_hash(uint32_t seed_b, const int32_t *pos, int64_t pos_period, int64_t rows,
-                             int64_t vocab, uint32_t *out, hipStream_t stream);
+// what: a dv_debug_noise mode; chunk_elems: 8 (bf16 chunks) or 4 (fp32 chunks)
+hipError_t launch_debug_noise(uint32_t seed_b, const int32_t *pos, int64_t pos_period, int64_t rows, int64_t vocab,
+                              int32_t what, int32_t chunk_elems, void *out, hipStream_t stream);
 
 }  // namespace dv

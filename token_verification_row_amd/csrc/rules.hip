@@ -1,5 +1,5 @@
-// Per-position decisions, COVER seed score, per-sequence top-k selection and
-// the noise-hash dump (gfx950). All are light next to the verification pass:
+// Per-position decisions, COVER seed score and per-sequence top-k selection
+// (gfx950). All are light next to the verification pass:
 // they touch tens of bytes per row.
 #include <climits>
 #include <cmath>
@@ -272,18 +272,6 @@ __global__ __launch_bounds__(1024) void select_topk_kernel(SelectLaunch p, int32
 }
 
 // ------------------------------------------------------------- noise dump ----
-__global__ __launch_bounds__(256) void debug_hash_kernel(uint32_t seed_b, const int32_t *pos, int64_t pos_period,
-                                                        int64_t rows, int64_t vocab, uint32_t *out) {
-  const int64_t n = rows * vocab;
-  for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < n;
-       t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t r = t / vocab, i = t % vocab;
-    const int32_t ps = pos ? pos[r] : (pos_period > 0 ? static_cast<int32_t>(r % pos_period) : static_cast<int32_t>(r));
-    const uint32_t key = mix32(seed_b ^ mix32(static_cast<uint32_t>(ps) ^ kPosSalt));
-    out[t] = mix32(key ^ (static_cast<uint32_t>(i) * kIndexStep));
-  }
-}
-
 }  // namespace
 
 hipError_t launch_decide(const DecideLaunch &p, hipStream_t stream) {
@@ -322,17 +310,6 @@ hipError_t launch_select_topk(const SelectLaunch &p, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const int threads = pow2 >= 2048 ? 1024 : (pow2 / 2 < 64 ? 64 : pow2 / 2);
   hipLaunchKernelGGL(select_topk_kernel, dim3(static_cast<unsigned>(p.nseq)), dim3(threads), lds, stream, p, pow2);
-  return hipGetLastError();
-}
-
-hipError_t launch_debug_hash(uint32_t seed_b, const int32_t *pos, int64_t pos_period, int64_t rows, int64_t vocab,
-                             uint32_t *out, hipStream_t stream) {
-  const int64_t n = rows * vocab;
-  if (n == 0) return hipSuccess;
-  int64_t blocks = (n + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(debug_hash_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, seed_b, pos,
-                     pos_period, rows, vocab, out);
   return hipGetLastError();
 }
 

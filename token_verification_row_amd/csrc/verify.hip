@@ -887,6 +887,116 @@ __global__ __launch_bounds__(256) void noise_cmax_kernel(uint32_t seed_b, uint32
   }
 }
 
+// Read-only streaming probe: the streaming kernel's access pattern (a wave per
+// (row, slice) in the same launch shape, 16-byte non-temporal loads of both
+// rows, kStep chunks per lane per step in two register sets) with no
+// arithmetic but an xor fold. It measures the read rate this pattern can
+// reach on the device, the ceiling of the verify pass. Each wave writes one
+// word (the xor of everything it read) to sink[row * kMaxSplit + slice].
+__device__ __forceinline__ uint32_t wave_xor(uint32_t x) {
+  int32_t v = static_cast<int32_t>(x);
+  v ^= dpp_i<kRowShr1, 0xF>(0, v);
+  v ^= dpp_i<kRowShr2, 0xF>(0, v);
+  v ^= dpp_i<kRowShr4, 0xF>(0, v);
+  v ^= dpp_i<kRowShr8, 0xF>(0, v);
+  v ^= dpp_i<kRowBcast15, 0xA>(0, v);
+  v ^= dpp_i<kRowBcast31, 0xC>(0, v);
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(v, 63));
+}
+
+__global__ __launch_bounds__(1024) void read_probe_kernel(VerifyLaunch p, uint32_t *sink) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int split = p.split;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * p.rows_per_block + wave / split;
+  const int32_t s = wave % split;
+  if (r >= p.rows) return;
+  const int32_t per = p.bf16 ? 8 : 4;
+  const int32_t nch = static_cast<int32_t>((p.vocab + per - 1) / per);
+  const int32_t c0 = s * p.slice_chunks;
+  const int32_t c1 = min(c0 + p.slice_chunks, nch);
+  const size_t row_bytes = static_cast<size_t>(p.ld) * (p.bf16 ? 2 : 4);
+  const u32x4 *ra = reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.va) + r * row_bytes);
+  const u32x4 *rb = reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.vb) + r * row_bytes);
+  constexpr int32_t kSpan = 64 * kStep;
+  const int32_t nsteps = c1 > c0 ? (c1 - c0 + kSpan - 1) / kSpan : 0;
+  auto at = [&](int32_t cc) { return cc < c1 ? cc : c0; };
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  if (nsteps > 0) {
+    u32x4 xa[kStep], xb[kStep], ya[kStep], yb[kStep];
+    int32_t c = c0 + lane;
+#pragma unroll
+    for (int k = 0; k < kStep; ++k) {
+      xa[k] = load_stream(ra + at(c + 64 * k));
+      xb[k] = load_stream(rb + at(c + 64 * k));
+    }
+    for (int32_t t = 0;;) {
+      ++t;
+      const int32_t cy = t < nsteps ? c + kSpan : c;
+#pragma unroll
+      for (int k = 0; k < kStep; ++k) {
+        ya[k] = load_stream(ra + at(cy + 64 * k));
+        yb[k] = load_stream(rb + at(cy + 64 * k));
+      }
+#pragma unroll
+      for (int k = 0; k < kStep; ++k) acc ^= xa[k] ^ xb[k];
+      if (t == nsteps) break;
+      c += kSpan;
+      ++t;
+      const int32_t cx = t < nsteps ? c + kSpan : c;
+#pragma unroll
+      for (int k = 0; k < kStep; ++k) {
+        xa[k] = load_stream(ra + at(cx + 64 * k));
+        xb[k] = load_stream(rb + at(cx + 64 * k));
+      }
+#pragma unroll
+      for (int k = 0; k < kStep; ++k) acc ^= ya[k] ^ yb[k];
+      if (t == nsteps) break;
+      c += kSpan;
+    }
+  }
+  const uint32_t x = wave_xor(acc.x ^ acc.y ^ acc.z ^ acc.w);
+  if (lane == 0) sink[r * kMaxProbeSplit + s] = x;
+}
+
+// Test-only dump of the noise exactly as the kernels above derive it, so that
+// it can be checked word for word: the index words, the group words, the
+// Gumbel values in log2 units (noise_at), and the two per-chunk bounds the
+// pruning uses (in registers, and the table). One thread per output entry of
+// a row; rows on the grid's y dimension (strided past 65535).
+template <int N>
+__global__ __launch_bounds__(256) void debug_noise_kernel(uint32_t seed_b, const int32_t *pos, int64_t pos_period,
+                                                         int64_t rows, int64_t vocab, int64_t width, int32_t what,
+                                                         void *out) {
+  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+    const int32_t ps = pos ? pos[r] : (pos_period > 0 ? static_cast<int32_t>(r % pos_period) : static_cast<int32_t>(r));
+    const NoiseKey key = noise_key(row_key(seed_b, ps));
+    for (int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; j < width;
+         j += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+      const int64_t o = r * width + j;
+      const uint32_t i = static_cast<uint32_t>(j);
+      switch (what) {
+        case DV_DEBUG_INDEX_WORDS:
+          static_cast<uint32_t *>(out)[o] = mix32(key.kw ^ (i * kIndexStep));
+          break;
+        case DV_DEBUG_GROUP_WORDS:
+          static_cast<uint32_t *>(out)[o] = mix32(key.kg ^ (i * kIndexStep));
+          break;
+        case DV_DEBUG_NOISE_LOG2:
+          static_cast<float *>(out)[o] = noise_at(key, i, vocab);
+          break;
+        case DV_DEBUG_CHUNK_BOUND: {
+          // the tail chunk is scored whole, never bounded: its entry is +inf
+          const bool whole = (static_cast<int64_t>(j) + 1) * N <= vocab;
+          static_cast<float *>(out)[o] = whole ? chunk_noise_bound<N>(static_cast<int32_t>(j), key, vocab) : INFINITY;
+          break;
+        }
+        default:
+          break;
+      }
+    }
+  }
+}
+
 template <bool BF16, int MODE, bool EXT>
 hipError_t launch_rows(const VerifyLaunch &p, hipStream_t stream) {
   const unsigned blocks = static_cast<unsigned>((p.rows + p.rows_per_block - 1) / p.rows_per_block);
@@ -918,6 +1028,43 @@ hipError_t launch_typed(const VerifyLaunch &p, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_debug_noise(uint32_t seed_b, const int32_t *pos, int64_t pos_period, int64_t rows, int64_t vocab,
+                              int32_t what, int32_t chunk_elems, void *out, hipStream_t stream) {
+  const int64_t nch = (vocab + chunk_elems - 1) / chunk_elems;
+  int64_t width = vocab;
+  if (what == DV_DEBUG_GROUP_WORDS) width = vocab / kNoiseGroup;
+  if (what == DV_DEBUG_CHUNK_BOUND || what == DV_DEBUG_TABLE_BOUND) width = nch;
+  if (rows == 0 || width == 0) return hipSuccess;
+  if (what == DV_DEBUG_TABLE_BOUND) {
+    // the table as dv_verify_rows builds it, over positions 0 .. rows-1
+    const dim3 grid(static_cast<unsigned>((nch + 256 * kCmaxPerThread - 1) / (256 * kCmaxPerThread)),
+                    static_cast<unsigned>(rows < 65535 ? rows : 65535));
+    if (chunk_elems == 8)
+      hipLaunchKernelGGL(noise_cmax_kernel<8>, grid, dim3(256), 0, stream, seed_b, static_cast<uint32_t>(rows),
+                         static_cast<uint32_t>(nch), vocab, static_cast<float *>(out));
+    else
+      hipLaunchKernelGGL(noise_cmax_kernel<4>, grid, dim3(256), 0, stream, seed_b, static_cast<uint32_t>(rows),
+                         static_cast<uint32_t>(nch), vocab, static_cast<float *>(out));
+    return hipGetLastError();
+  }
+  int64_t bx = (width + 255) / 256;
+  if (bx > 4096) bx = 4096;
+  const dim3 grid(static_cast<unsigned>(bx), static_cast<unsigned>(rows < 65535 ? rows : 65535));
+  if (chunk_elems == 8)
+    hipLaunchKernelGGL(debug_noise_kernel<8>, grid, dim3(256), 0, stream, seed_b, pos, pos_period, rows, vocab, width,
+                       what, out);
+  else
+    hipLaunchKernelGGL(debug_noise_kernel<4>, grid, dim3(256), 0, stream, seed_b, pos, pos_period, rows, vocab, width,
+                       what, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_read_probe(const VerifyLaunch &p, uint32_t *sink, hipStream_t stream) {
+  const unsigned blocks = static_cast<unsigned>((p.rows + p.rows_per_block - 1) / p.rows_per_block);
+  hipLaunchKernelGGL(read_probe_kernel, dim3(blocks), dim3(64 * p.rows_per_block * p.split), 0, stream, p, sink);
+  return hipGetLastError();
+}
 
 hipError_t launch_verify(const VerifyLaunch &p, hipStream_t stream) {
   return p.bf16 ? launch_typed<true>(p, stream) : launch_typed<false>(p, stream);

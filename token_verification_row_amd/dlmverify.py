@@ -96,6 +96,9 @@ _SIGNATURES = {
     "dv_influence_drift_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(dv_attention), ctypes.POINTER(ctypes.c_size_t)]),
     "dv_influence_drift": (ctypes.c_int, [ctypes.POINTER(dv_attention), _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "dv_debug_hash": (ctypes.c_int, [ctypes.c_uint64, _P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P]),
+    "dv_debug_noise": (ctypes.c_int, [ctypes.c_uint64, _P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_int32, ctypes.c_int32, _P, _P]),
+    "dv_debug_read_probe": (ctypes.c_int, [ctypes.POINTER(dv_logits), ctypes.POINTER(dv_tuning), _P, _P]),
     "dv_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "dv_last_error": (ctypes.c_char_p, []),
     "dv_version": (ctypes.c_int, []),
@@ -170,11 +173,19 @@ def _logits_desc(verifier, drafter, vocab):
                      rows=rows, vocab=vocab, ld=ld)
 
 
-def _noise_desc(temperature, seed, pos, pos_period):
-    if pos is not None:
-        _need_cuda(pos, "pos")
-        if pos.dtype != torch.int32 or not pos.is_contiguous():
-            raise TypeError("pos must be a contiguous int32 tensor")
+def _check_pos(pos, rows):
+    """pos: None, or a contiguous device int32 tensor with an entry for each of ``rows`` rows."""
+    if pos is None:
+        return
+    _need_cuda(pos, "pos")
+    if pos.dtype != torch.int32 or not pos.is_contiguous():
+        raise TypeError("pos must be a contiguous int32 tensor")
+    if pos.numel() < rows:
+        raise ValueError(f"pos holds {pos.numel()} positions for {rows} rows")
+
+
+def _noise_desc(temperature, seed, pos, pos_period, rows):
+    _check_pos(pos, rows)
     return dv_noise(temperature=float(temperature), reserved=0, seed=int(seed) & 0xFFFFFFFFFFFFFFFF,
                     pos=None if pos is None else pos.data_ptr(), pos_period=int(pos_period))
 
@@ -192,7 +203,7 @@ def _tuning_desc(tuning):
 def dv_verify_workspace_bytes(verifier, drafter, temperature=0.0, seed=0, pos=None, pos_period=0, *,
                               vocab=None, tuning=None) -> int:
     d = _logits_desc(verifier, drafter, vocab)
-    n = _noise_desc(temperature, seed, pos, pos_period)
+    n = _noise_desc(temperature, seed, pos, pos_period, d.rows)
     t = _tuning_desc(tuning)
     out = ctypes.c_size_t(0)
     _check(load_library().dv_verify_workspace_bytes(ctypes.byref(d), ctypes.byref(n),
@@ -208,7 +219,7 @@ def dv_verify_rows(verifier, drafter, temperature=0.0, seed=0, pos=None, pos_per
     for the rest). neg_inf: the logits may hold -inf (DV_LOGITS_NEG_INF)."""
     d = _logits_desc(verifier, drafter, vocab)
     d.flags = DV_LOGITS_NEG_INF if neg_inf else 0
-    n = _noise_desc(temperature, seed, pos, pos_period)
+    n = _noise_desc(temperature, seed, pos, pos_period, d.rows)
     t = _tuning_desc(tuning)
     rows, dev = d.rows, verifier.device
     res = {k: v for k, v in (out or {}).items() if not k.startswith("_")}
@@ -238,6 +249,46 @@ def dv_verify_rows(verifier, drafter, temperature=0.0, seed=0, pos=None, pos_per
                               ctypes.byref(st), ws_ptr, ws_bytes, _stream_handle(dev)), "dv_verify_rows")
     res["_workspace"] = workspace  # keep the scratch alive until the caller drops the result
     return res
+
+
+class VerifyPlan:
+    """A dv_verify_rows call whose marshalling is done once: descriptors, output tensors and workspace are
+    built at construction, and each call only points the descriptor at new logits of the same shape, dtype
+    and row pitch (on the same device) and enters the library. For loops that verify batch after batch."""
+
+    def __init__(self, verifier, drafter, temperature=0.0, seed=0, pos=None, pos_period=0, *, vocab=None,
+                 outputs=CORE_FIELDS, tuning=None, neg_inf=False):
+        self.out = dv_verify_rows(verifier, drafter, temperature, seed, pos, pos_period, vocab=vocab,
+                                  outputs=outputs, tuning=tuning, neg_inf=neg_inf)
+        self._desc = _logits_desc(verifier, drafter, vocab)
+        self._desc.flags = DV_LOGITS_NEG_INF if neg_inf else 0
+        self._noise = _noise_desc(temperature, seed, pos, pos_period, self._desc.rows)
+        self._pos = pos                                   # kept alive with the plan
+        self._tuning = _tuning_desc(tuning)
+        self._stats = dv_row_stats(**{f: (self.out[f].data_ptr() if f in self.out else None) for f in STAT_FIELDS})
+        ws = self.out.get("_workspace")
+        self._ws_ptr, self._ws_bytes = None, 0
+        if ws is not None:
+            base = ws.data_ptr()
+            off = (-base) % 256
+            self._ws_ptr, self._ws_bytes = base + off, ws.numel() - off
+        self._key = (tuple(verifier.shape), verifier.dtype, tuple(verifier.stride()), verifier.device)
+        self._stream = _stream_handle(verifier.device)
+        self._lib = load_library()
+        self._args = (ctypes.byref(self._desc), ctypes.byref(self._noise),
+                      None if self._tuning is None else ctypes.byref(self._tuning), ctypes.byref(self._stats),
+                      self._ws_ptr, self._ws_bytes)
+
+    def __call__(self, verifier, drafter):
+        """Verify these logits (same shape, dtype, pitch and device as at construction) on the current stream;
+        returns the plan's output dict (overwritten by each call)."""
+        for t in (verifier, drafter):
+            if (tuple(t.shape), t.dtype, tuple(t.stride()), t.device) != self._key:
+                raise ValueError("logits differ in shape, dtype, pitch or device from the plan's")
+        self._desc.verifier = verifier.data_ptr()
+        self._desc.drafter = drafter.data_ptr()
+        _check(self._lib.dv_verify_rows(*self._args, _stream_handle(verifier.device)), "dv_verify_rows")
+        return self.out
 
 
 def dv_decide(rule, stats, *, rows=None, tau_kl=0.0, conf_thr=0.0, mask_token=-1, subject=None, cur_tok=None,
@@ -431,14 +482,46 @@ def dv_dual_view_attention(q, k_cur, v_cur, k_prev, v_prev, seed, *, scale=None,
     return out
 
 
+DV_DEBUG_INDEX_WORDS, DV_DEBUG_GROUP_WORDS, DV_DEBUG_NOISE_LOG2, DV_DEBUG_CHUNK_BOUND, DV_DEBUG_TABLE_BOUND = range(5)
+DEBUG_NOISE_MODES = {"index_words": 0, "group_words": 1, "noise_log2": 2, "chunk_bound": 3, "table_bound": 4}
+
+
 def dv_debug_hash(seed, rows, vocab, *, pos=None, pos_period=0, device="cuda"):
     """Noise hash words [rows, vocab] (returned as int32 tensor holding the uint32 bits)."""
+    _check_pos(pos, rows)
     if pos is not None:
-        _need_cuda(pos, "pos")
-        if pos.dtype != torch.int32:
-            raise TypeError("pos must be int32")
         device = pos.device
     out = torch.empty((rows, vocab), dtype=torch.int32, device=device)
     _check(load_library().dv_debug_hash(int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(pos), int(pos_period), int(rows),
                                         int(vocab), _ptr(out), _stream_handle(out.device)), "dv_debug_hash")
     return out
+
+
+def dv_debug_noise(seed, rows, vocab, mode, *, chunk_elems=8, pos=None, pos_period=0, device="cuda"):
+    """The shared noise as the kernels derive it (include/dlmverify.h, dv_debug_noise). mode: a name of
+    DEBUG_NOISE_MODES. Words come back as int32 tensors holding the uint32 bits, values and bounds as float32:
+    [rows, vocab] for index words and noise values, [rows, vocab // 8] for group words, [rows, chunks] for bounds."""
+    m = DEBUG_NOISE_MODES[mode] if isinstance(mode, str) else int(mode)
+    _check_pos(pos, rows)
+    if pos is not None:
+        device = pos.device
+    nch = -(-int(vocab) // int(chunk_elems))
+    width = {0: vocab, 1: vocab // 8, 2: vocab, 3: nch, 4: nch}.get(m, 0)
+    dt = torch.int32 if m in (0, 1) else torch.float32
+    out = torch.empty((rows, width), dtype=dt, device=device)
+    _check(load_library().dv_debug_noise(int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(pos), int(pos_period), int(rows),
+                                         int(vocab), m, int(chunk_elems), _ptr(out), _stream_handle(out.device)),
+           "dv_debug_noise")
+    return out
+
+
+def dv_debug_read_probe(verifier, drafter, *, sink=None, tuning=None):
+    """Read-only streaming probe over both logit matrices in dv_verify_rows's launch shape (measurement only).
+    Returns the sink, int32 [rows, 16] holding the uint32 xor of what each wave read."""
+    d = _logits_desc(verifier, drafter, None)
+    t = _tuning_desc(tuning)
+    if sink is None:
+        sink = torch.empty((d.rows, 16), dtype=torch.int32, device=verifier.device)
+    _check(load_library().dv_debug_read_probe(ctypes.byref(d), None if t is None else ctypes.byref(t), _ptr(sink),
+                                              _stream_handle(verifier.device)), "dv_debug_read_probe")
+    return sink

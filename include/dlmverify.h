@@ -166,6 +166,24 @@ dv_status dv_verify_rows(const dv_logits *logits, const dv_noise *noise, const d
                          const dv_row_stats *out, void *workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same as
+ * dv_verify_rows (same kernels, launch shape and results, bit for bit) but
+ * with no workspace argument: the noise table dv_verify_rows builds in its
+ * workspace when rows share positions goes into a fixed scratch array of
+ * DV_NOALLOC_SCRATCH_BYTES that the library holds on each device (resolved on
+ * the first call on that device and kept until the process ends). The call
+ * allocates nothing. Every call on one device shares that scratch and
+ * overwrites it, so calls that overlap on one device (concurrent streams,
+ * threads) race; calls ordered on one stream do not. Errors: those of
+ * dv_verify_rows, except DV_ERR_WORKSPACE; DV_ERR_UNSUPPORTED when the table
+ * would exceed DV_NOALLOC_SCRATCH_BYTES (pass tuning.shared_noise = 0, which
+ * needs no table, or call dv_verify_rows with a workspace); DV_ERR_HIP when
+ * the scratch address cannot be resolved. */
+#define DV_NOALLOC_SCRATCH_BYTES (8u << 20)
+dv_status dv_verify_rows_noalloc(const dv_logits *logits, const dv_noise *noise, const dv_tuning *tuning,
+                                 const dv_row_stats *out, hipStream_t stream);
+
 typedef enum dv_rule {
   DV_RULE_TRUST = 0,          /* [DualDiffusion] §2 verification item 1: accept all */
   DV_RULE_KL = 1,             /* item 2: REMASK iff kl > tau_kl */

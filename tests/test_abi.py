@@ -29,7 +29,7 @@ def _declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = _declared_functions()
-    assert names == sorted(["dv_verify_workspace_bytes", "dv_verify_rows", "dv_decide", "dv_seed_score",
+    assert names == sorted(["dv_verify_workspace_bytes", "dv_verify_rows", "dv_verify_rows_noalloc", "dv_decide", "dv_seed_score",
                            "dv_select_topk", "dv_tree_accept", "dv_influence_drift_workspace_bytes",
                            "dv_influence_drift", "dv_dual_view_attention", "dv_debug_hash", "dv_debug_noise", "dv_debug_read_probe", "dv_status_str",
                            "dv_last_error", "dv_version"])
@@ -201,6 +201,27 @@ def test_read_probe_validation(lib):
     assert lib.dv_debug_read_probe(ctypes.byref(lg), ctypes.byref(t), FAKE, None) == B.DV_ERR_ARG
     empty = _logits(rows=0)
     assert lib.dv_debug_read_probe(ctypes.byref(empty), None, None, None) == B.DV_OK
+
+
+def test_noalloc_validation(lib):
+    """dv_verify_rows_noalloc rejects bad arguments, and a noise table larger than its fixed scratch, before any
+    HIP call."""
+    st = B.dv_row_stats(kl=FAKE)
+    call = lambda lg, nz, t=None: lib.dv_verify_rows_noalloc(ctypes.byref(lg), ctypes.byref(nz),
+                                                             None if t is None else ctypes.byref(t), ctypes.byref(st),
+                                                             None)
+    assert call(_logits(ld=60), _noise()) == B.DV_ERR_SHAPE
+    assert call(_logits(), _noise(T=-1.0)) == B.DV_ERR_ARG
+    assert call(_logits(), _noise(T=1e-45)) == B.DV_ERR_ARG            # log2(e) / T overflows
+    assert lib.dv_verify_rows_noalloc(ctypes.byref(_logits()), ctypes.byref(_noise()), None, None, None) == B.DV_ERR_NULL
+    # 128 positions x 19008 chunks x 4 bytes = 9.7 MB of table > 8 MiB of scratch
+    big = _logits(rows=256, vocab=152064, ld=152064)
+    assert call(big, _noise(T=1.0, period=128)) == B.DV_ERR_UNSUPPORTED
+    assert "scratch" in lib.dv_last_error().decode()
+    assert call(big, _noise(T=1.0, period=128), B.dv_tuning(split=0, shared_noise=1)) == B.DV_ERR_UNSUPPORTED
+    # 8 MiB holds 64 positions of that vocabulary; empty batches launch nothing
+    assert call(_logits(rows=0, vocab=152064, ld=152064), _noise(T=1.0, period=64)) == B.DV_OK
+    assert B.DV_NOALLOC_SCRATCH_BYTES == 8 << 20
 
 
 def test_binding_rejects_short_pos(monkeypatch):

@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdlmverify.so")
-SOURCES = ["api.cpp", "verify.hip", "rules.hip", "tree.hip", "attn.hip", "dual_view.hip"]
+SOURCES = ["api.cpp", "verify.hip", "rules.hip", "tree.hip", "attn.hip", "dual_view.hip", "noalloc.hip"]
 BUILD_DIR = os.path.join(HERE, "_build")
 
 # gfx950 only; packed fp32 arithmetic is switched off for the device code and

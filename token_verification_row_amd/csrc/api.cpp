@@ -70,6 +70,8 @@ dv_status check_noise(const dv_noise *n) {
   if (!n) return fail(DV_ERR_NULL, "noise descriptor is NULL");
   if (!std::isfinite(n->temperature) || n->temperature < 0.0f)
     return fail(DV_ERR_ARG, "temperature must be finite and >= 0");
+  if (n->temperature > 0.0f && !std::isfinite(1.44269504088896340736f / n->temperature))
+    return fail(DV_ERR_ARG, "temperature too small");
   if (n->pos_period < 0 || n->pos_period > kMaxIndex) return fail(DV_ERR_SHAPE, "pos_period out of range");
   return DV_OK;
 }
@@ -156,6 +158,33 @@ dv_status influence_geometry(const dv_attention *a, bool need_ptrs, dv::Influenc
   return DV_OK;
 }
 
+// The launch of a validated dv_verify_rows call, with its noise table (if any) at `table`.
+dv_status launch_verify_rows(const dv_logits *logits, const dv_noise *noise, const Geometry &g, const dv_row_stats *out,
+                             void *table, hipStream_t stream) {
+  dv::VerifyLaunch p{};
+  p.va = logits->verifier;
+  p.vb = logits->drafter;
+  p.rows = logits->rows;
+  p.vocab = logits->vocab;
+  p.ld = logits->ld;
+  p.bf16 = logits->dtype == DV_BF16;
+  p.greedy = noise->temperature == 0.0f;
+  p.neg_inf = (logits->flags & DV_LOGITS_NEG_INF) != 0;
+  p.cT = p.greedy ? 0.0f : 1.44269504088896340736f / noise->temperature;
+  if (!p.greedy && !std::isfinite(p.cT)) return fail(DV_ERR_ARG, "temperature too small");
+  p.seed_b = dv::seed_word(noise->seed);
+  p.pos = noise->pos;
+  p.pos_period = noise->pos_period;
+  p.split = g.split;
+  p.slice_chunks = g.slice_chunks;
+  p.rows_per_block = g.rows_per_block;
+  p.noise_cmax = g.pruned ? static_cast<float *>(table) : nullptr;
+  p.cmax_rows = g.cmax_rows;
+  p.cmax_ld = g.cmax_ld;
+  p.out = *out;
+  return hip_status(dv::launch_verify(p, stream), "dv_verify_rows launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -187,28 +216,29 @@ dv_status dv_verify_rows(const dv_logits *logits, const dv_noise *noise, const d
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(DV_ERR_ALIGN, "workspace must be 256-byte aligned");
   }
   if (logits->rows == 0) return ok();
-  dv::VerifyLaunch p{};
-  p.va = logits->verifier;
-  p.vb = logits->drafter;
-  p.rows = logits->rows;
-  p.vocab = logits->vocab;
-  p.ld = logits->ld;
-  p.bf16 = logits->dtype == DV_BF16;
-  p.greedy = noise->temperature == 0.0f;
-  p.neg_inf = (logits->flags & DV_LOGITS_NEG_INF) != 0;
-  p.cT = p.greedy ? 0.0f : 1.44269504088896340736f / noise->temperature;
-  if (!p.greedy && !std::isfinite(p.cT)) return fail(DV_ERR_ARG, "temperature too small");
-  p.seed_b = dv::seed_word(noise->seed);
-  p.pos = noise->pos;
-  p.pos_period = noise->pos_period;
-  p.split = g.split;
-  p.slice_chunks = g.slice_chunks;
-  p.rows_per_block = g.rows_per_block;
-  p.noise_cmax = g.pruned ? static_cast<float *>(workspace) : nullptr;
-  p.cmax_rows = g.cmax_rows;
-  p.cmax_ld = g.cmax_ld;
-  p.out = *out;
-  return hip_status(dv::launch_verify(p, stream), "dv_verify_rows launch");
+  return launch_verify_rows(logits, noise, g, out, workspace, stream);
+}
+
+dv_status dv_verify_rows_noalloc(const dv_logits *logits, const dv_noise *noise, const dv_tuning *tuning,
+                                 const dv_row_stats *out, hipStream_t stream) {
+  dv_status s = check_logits(logits, true);
+  if (s != DV_OK) return s;
+  if ((s = check_noise(noise)) != DV_OK) return s;
+  if (!out) return fail(DV_ERR_NULL, "output descriptor is NULL");
+  Geometry g;
+  if ((s = choose_geometry(logits, noise, tuning, g)) != DV_OK) return s;
+  if (g.workspace > DV_NOALLOC_SCRATCH_BYTES)
+    return fail(DV_ERR_UNSUPPORTED,
+                "the noise table needs %zu bytes, more than the library's fixed scratch of %zu bytes: pass "
+                "tuning.shared_noise = 0 (no table) or call dv_verify_rows with a workspace",
+                g.workspace, static_cast<size_t>(DV_NOALLOC_SCRATCH_BYTES));
+  if (logits->rows == 0) return ok();
+  void *table = nullptr;
+  if (g.workspace > 0) {
+    const hipError_t e = dv::noalloc_scratch(stream, &table);
+    if (e != hipSuccess) return hip_status(e, "dv_verify_rows_noalloc scratch address");
+  }
+  return launch_verify_rows(logits, noise, g, out, table, stream);
 }
 
 dv_status dv_decide(const dv_decide_args *a, const dv_row_stats *stats, const uint8_t *subject, const int32_t *cur_tok,

@@ -88,6 +88,10 @@ struct VerifyLaunch {
 
 hipError_t launch_verify(const VerifyLaunch &p, hipStream_t stream);
 
+// Device address of the library's fixed scratch on the device of `stream` (noalloc.hip): resolved once per
+// device, DV_NOALLOC_SCRATCH_BYTES long, shared by every call on that device.
+hipError_t noalloc_scratch(hipStream_t stream, void **ptr);
+
 // the read-only streaming probe (dv_debug_read_probe): sink holds kMaxProbeSplit words per row
 constexpr int kMaxProbeSplit = 16;
 hipError_t launch_read_probe(const VerifyLaunch &p, uint32_t *sink, hipStream_t stream);

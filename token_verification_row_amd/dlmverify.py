@@ -86,6 +86,8 @@ _SIGNATURES = {
     "dv_verify_rows": (ctypes.c_int, [ctypes.POINTER(dv_logits), ctypes.POINTER(dv_noise),
                                       ctypes.POINTER(dv_tuning), ctypes.POINTER(dv_row_stats), _P,
                                       ctypes.c_size_t, _P]),
+    "dv_verify_rows_noalloc": (ctypes.c_int, [ctypes.POINTER(dv_logits), ctypes.POINTER(dv_noise),
+                                              ctypes.POINTER(dv_tuning), ctypes.POINTER(dv_row_stats), _P]),
     "dv_decide": (ctypes.c_int, [ctypes.POINTER(dv_decide_args), ctypes.POINTER(dv_row_stats), _P, _P, _P, _P,
                                  _P, _P, _P]),
     "dv_seed_score": (ctypes.c_int, [ctypes.c_int64, _P, _P, _P, _P, _P, _P]),
@@ -248,6 +250,36 @@ def dv_verify_rows(verifier, drafter, temperature=0.0, seed=0, pos=None, pos_per
     _check(lib.dv_verify_rows(ctypes.byref(d), ctypes.byref(n), None if t is None else ctypes.byref(t),
                               ctypes.byref(st), ws_ptr, ws_bytes, _stream_handle(dev)), "dv_verify_rows")
     res["_workspace"] = workspace  # keep the scratch alive until the caller drops the result
+    return res
+
+
+DV_NOALLOC_SCRATCH_BYTES = 8 << 20
+
+
+def dv_verify_rows_noalloc(verifier, drafter, temperature=0.0, seed=0, pos=None, pos_period=0, *, vocab=None,
+                           outputs=CORE_FIELDS, out=None, tuning=None, neg_inf=False):
+    """dv_verify_rows without a workspace: the library's fixed per-device scratch holds the noise table (the
+    C entry point allocates nothing; pass ``out`` to have this wrapper allocate nothing either)."""
+    d = _logits_desc(verifier, drafter, vocab)
+    d.flags = DV_LOGITS_NEG_INF if neg_inf else 0
+    n = _noise_desc(temperature, seed, pos, pos_period, d.rows)
+    t = _tuning_desc(tuning)
+    rows, dev = d.rows, verifier.device
+    res = {k: v for k, v in (out or {}).items() if not k.startswith("_")}
+    for f in outputs:
+        if f not in STAT_FIELDS:
+            raise KeyError(f)
+        if f not in res:
+            res[f] = torch.empty(rows, dtype=torch.float32 if f in _FLOAT_FIELDS else torch.int32, device=dev)
+    for f, v in res.items():
+        _need_cuda(v, f)
+        want = torch.float32 if f in _FLOAT_FIELDS else torch.int32
+        if v.dtype != want or v.numel() < rows or not v.is_contiguous():
+            raise TypeError(f"output {f} must be a contiguous {want} tensor of >= {rows} elements")
+    st = dv_row_stats(**{f: (res[f].data_ptr() if f in res else None) for f in STAT_FIELDS})
+    _check(load_library().dv_verify_rows_noalloc(ctypes.byref(d), ctypes.byref(n),
+                                                 None if t is None else ctypes.byref(t), ctypes.byref(st),
+                                                 _stream_handle(dev)), "dv_verify_rows_noalloc")
     return res
 
 

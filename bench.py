@@ -216,6 +216,9 @@ def main() -> int:
                          "passed since warm-up began: the device's clocks take several milliseconds of sustained "
                          "load to settle, longer than a few steps")
     ap.add_argument("--workload", type=int, default=4, choices=[2, 3, 4, 5])
+    ap.add_argument("--temperature", type=float, default=None,
+                    help="measurement variant: verify at this temperature instead of the workload's (0 = greedy); "
+                         "the line then names it in config")
     ap.add_argument("--cpu-rows", type=int, default=1024, help="rows of the workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--influence", type=int, default=0, metavar="MAPS",
@@ -265,6 +268,10 @@ def main() -> int:
         print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": args.steps}), flush=True)
         return 0
     w = W.workload(args.workload)
+    if args.temperature is not None:
+        import dataclasses
+
+        w = dataclasses.replace(w, temperature=float(args.temperature))
     R, V = w.rows, w.V
     # rotate enough copies that one step never finds its inputs in the 256 MB last-level cache
     copies = args.copies or max(2, -(-1_000_000_000 // w.input_bytes) + 1)

@@ -111,6 +111,9 @@ dv_status choose_geometry(const dv_logits *x, const dv_noise *n, const dv_tuning
   if (split > kMaxSplit) split = kMaxSplit;
   if (split > nch) split = nch;
   if (split < 1) split = 1;
+  // a slice is read through a buffer resource, whose byte range is 32 bits: at most 2^28 - 1 chunks
+  const int64_t max_slice = (int64_t(1) << 28) - 1;
+  if (split < (nch + max_slice - 1) / max_slice) split = (nch + max_slice - 1) / max_slice;
   g.split = static_cast<int32_t>(split);
   g.slice_chunks = static_cast<int32_t>((nch + split - 1) / split);
   // a workgroup holds whole rows: 4 waves when split divides 4, else one row

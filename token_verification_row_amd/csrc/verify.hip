@@ -66,7 +66,19 @@ struct Chunk {
   static constexpr int N = BF16 ? 8 : 4;  // elements per 16-byte chunk
 };
 
-__device__ __forceinline__ u32x4 load_stream(const u32x4 *p) { return __builtin_nontemporal_load(p); }
+// A slice of a row as a buffer resource: loads address it with a 32-bit byte
+// offset from a base held in scalar registers (one VALU operation per load
+// instead of a 64-bit address), and a load at or past `bytes` returns zeros
+// without touching memory. The third word is the gfx9 buffer format (raw
+// 32-bit data).
+constexpr int kBufferFormat = 0x00020000;
+constexpr int kLoadNontemporal = 2;  // the nt bit of a buffer load's cache policy
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), kBufferFormat);
+}
+__device__ __forceinline__ u32x4 load_stream_at(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kLoadNontemporal);
+}
 
 // Logits that may hold -inf (masked vocabulary entries): every value at or
 // below -2^100, -inf included, is raised to -2^100 on the raw bits, before any
@@ -96,14 +108,9 @@ __device__ __forceinline__ u32x4 clamp_neg(u32x4 w) {
   return u32x4{e[0], e[1], e[2], e[3]};
 }
 
-// The streaming read of a chunk, and a plain read (the tail chunk, the
-// argmax refinement); with EXT the -inf clamp is applied to both, so every
-// later comparison sees the same values.
-template <bool BF16, bool EXT>
-__device__ __forceinline__ u32x4 load_chunk(const u32x4 *p) {
-  const u32x4 w = load_stream(p);
-  return EXT ? clamp_neg<BF16>(w) : w;
-}
+// A plain read of a chunk (the tail chunk, the argmax refinement); with EXT
+// the -inf clamp is applied, as to the streaming reads, so every later
+// comparison sees the same values.
 template <bool BF16, bool EXT>
 __device__ __forceinline__ u32x4 read_chunk(const u32x4 *p) {
   const u32x4 w = *p;
@@ -526,24 +533,39 @@ struct StepRegs {
   u32x4 a[K], b[K];
   float gm[K];
 
-  template <typename At>
-  __device__ __forceinline__ void load(const u32x4 *ra, const u32x4 *rb, const float *g_cmax, int32_t c, At at) {
+  // The chunks at offsets o, o + 64, ... (in chunks, from the start of the slice) of both rows
+  // and of the noise table; past the end of the slice the buffers return zeros (not used).
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rg,
+                                       int32_t o) {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      const int32_t ck = at(c + 64 * k);
-      a[k] = load_chunk<BF16, EXT>(ra + ck);
-      b[k] = load_chunk<BF16, EXT>(rb + ck);
-      if constexpr (PRUNE) gm[k] = g_cmax[ck];
+      const uint32_t off = static_cast<uint32_t>(o + 64 * k) * 16u;
+      a[k] = load_stream_at(ra, off);
+      b[k] = load_stream_at(rb, off);
+      if constexpr (EXT) {
+        a[k] = clamp_neg<BF16>(a[k]);
+        b[k] = clamp_neg<BF16>(b[k]);
+      }
+      if constexpr (PRUNE) gm[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, off / 4u, 0, 0));
     }
   }
 
   // Fold the K chunks in; chunk k exists only when c + 64 k < cend (lanes past
-  // the end of the slice ran the loop with the others but fold nothing). The
+  // the end of the slice ran the step with the others but fold nothing). The
+  // loaded registers are first read on every path (an empty asm that takes
+  // them as inputs): were they read only inside the per-lane branch, the
+  // compiler could not rule out a path on which a load is still in flight at
+  // the loop's back edge, and would drain every load in flight there. The
   // queue operations are wave-wide, so every lane must reach them.
   template <int MODE>
   __device__ __forceinline__ void fold(Lane &st, int32_t c, int32_t cend, const NoiseKey &key, int64_t vocab, float cT,
                                        ScoreQueue *q, int &nq, int lane) const {
     constexpr int N = Chunk<BF16>::N;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      asm volatile("" ::"v"(a[k]), "v"(b[k]));
+      if constexpr (PRUNE) asm volatile("" ::"v"(gm[k]));
+    }
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const int32_t ck = c + 64 * k;
@@ -590,10 +612,14 @@ struct StepRegs {
 // steps in every lane (lanes past the end of the slice load a valid chunk and
 // fold nothing), so wave-wide operations inside it see all lanes. Two register
 // sets, X and Y, work in ping-pong: while one step of chunks is folded in, the
-// loads of the next step land in the other set; the next loads are issued on
-// every path (the last step re-reads its own chunks, which hit in cache), so
-// the wait counts never have to cover a path without them and no register
-// copy forces a wait at the back edge.
+// loads of the next step land in the other set. The next loads are issued on
+// every path (past the end of the slice the buffer returns zeros without a
+// memory access), so the wait counts never have to cover a path without them
+// and no register copy forces a wait at the back edge. The scheduling barrier
+// after each step's loads keeps them ahead of the arithmetic on the other set:
+// without it the compiler starts unpacking the set that is due before the next
+// loads are issued, and the wave waits for its data with one step of loads in
+// flight instead of two.
 template <bool BF16, int MODE, bool EXT>
 __device__ __forceinline__ void scan_slice(Lane &st, const u32x4 *ra, const u32x4 *rb, int32_t c0, int32_t c1,
                                            int32_t nfull, int nvalid_tail, float cT, const NoiseKey &key, int64_t vocab,
@@ -603,21 +629,24 @@ __device__ __forceinline__ void scan_slice(Lane &st, const u32x4 *ra, const u32x
   const int32_t nsteps = cend > c0 ? (cend - c0 + kSpan - 1) / kSpan : 0;
   int nq = 0;
   if (nsteps > 0) {
-    // in-bounds address for chunks past the end (their data is not used)
-    auto at = [&](int32_t cc) { return cc < cend ? cc : c0; };
+    // the slice's whole chunks as buffers: chunks past the end read as zeros and are not folded
+    const uint32_t nbytes = static_cast<uint32_t>(cend - c0) * 16u;
+    const __amdgpu_buffer_rsrc_t ba = slice_rsrc(ra + c0, nbytes), bb = slice_rsrc(rb + c0, nbytes);
+    const __amdgpu_buffer_rsrc_t bg = slice_rsrc(MODE == kTableBound ? g_cmax + c0 : nullptr,
+                                                 MODE == kTableBound ? nbytes / 4u : 0u);
     StepRegs<BF16, MODE == kTableBound, kStep, EXT> X, Y;
     int32_t c = c0 + lane;
-    X.load(ra, rb, g_cmax, c, at);
+    X.load(ba, bb, bg, c - c0);
     for (int32_t t = 0;;) {
-      ++t;
-      Y.load(ra, rb, g_cmax, t < nsteps ? c + kSpan : c, at);
+      Y.load(ba, bb, bg, c + kSpan - c0);
+      __builtin_amdgcn_sched_barrier(0);
       X.template fold<MODE>(st, c, cend, key, vocab, cT, q, nq, lane);
-      if (t == nsteps) break;
+      if (++t == nsteps) break;
       c += kSpan;
-      ++t;
-      X.load(ra, rb, g_cmax, t < nsteps ? c + kSpan : c, at);
+      X.load(ba, bb, bg, c + kSpan - c0);
+      __builtin_amdgcn_sched_barrier(0);
       Y.template fold<MODE>(st, c, cend, key, vocab, cT, q, nq, lane);
-      if (t == nsteps) break;
+      if (++t == nsteps) break;
       c += kSpan;
     }
   }
@@ -672,17 +701,17 @@ __device__ __forceinline__ Partial wave_reduce(const Lane &st) {
 // ---- per-row epilogue (double precision) ----
 
 // Lowest index inside chunk c of a row whose value equals target, found by the
-// whole wave: lane j < N looks at element c*N + j. For scores the perturbed
-// score is recomputed with exactly the arithmetic of the streaming pass. A
-// chunk index outside the row (only possible when the logits hold NaN, which
-// is not supported) gives -1 without touching memory.
-template <bool BF16, bool SCORE, bool EXT>
-__device__ __forceinline__ int32_t refine_in_chunk(const u32x4 *row, int32_t c, float target, int64_t vocab, float cT,
+// whole wave from the chunk's 16 bytes w (the same for every lane): lane j < N
+// looks at element c*N + j. For scores the perturbed score is recomputed with
+// exactly the arithmetic of the streaming pass. A chunk index outside the row
+// (only possible when the logits hold NaN, which is not supported) gives -1.
+template <bool BF16, bool SCORE>
+__device__ __forceinline__ int32_t refine_in_chunk(const u32x4 &w, int32_t c, float target, int64_t vocab, float cT,
                                                    const NoiseKey &key, int lane) {
   constexpr int N = Chunk<BF16>::N;
   if (c < 0 || static_cast<int64_t>(c) * N >= vocab) return -1;
   float x[N];
-  widen<BF16>(read_chunk<BF16, EXT>(row + c), x);  // the same 16 bytes for every lane: one request
+  widen<BF16>(w, x);
   float v = x[0];
 #pragma unroll
   for (int j = 1; j < N; ++j) v = (lane == j) ? x[j] : v;
@@ -696,6 +725,16 @@ __device__ __forceinline__ int32_t refine_in_chunk(const u32x4 *row, int32_t c, 
   return m ? static_cast<int32_t>(static_cast<int64_t>(c) * N + __ffsll(m) - 1) : -1;
 }
 
+// The 16 bytes of chunk c of a row (chunk 0 for an index outside the row, whose
+// refinement gives -1 anyway), so that every chunk the epilogue needs can be
+// requested before the first one is used.
+template <bool BF16, bool EXT>
+__device__ __forceinline__ u32x4 fetch_chunk(const u32x4 *row, int32_t c, int64_t vocab) {
+  constexpr int N = Chunk<BF16>::N;
+  const bool inside = c >= 0 && static_cast<int64_t>(c) * N < vocab;
+  return read_chunk<BF16, EXT>(row + (inside ? c : 0));
+}
+
 // Row results from the reduced state of a whole row; every lane of the wave
 // calls it (the refinements use the lanes), lane 0 writes.
 template <bool BF16, bool EXT>
@@ -707,10 +746,21 @@ __device__ void finalize_row(const VerifyLaunch &p, int64_t r, const Partial &t,
   const dv_row_stats &o = p.out;
   const bool want_tok_d = o.tok_d || o.p_tok_d;
   const bool want_am = o.argmax_v || o.argmax_d || (p.greedy && (o.tok_v || want_tok_d));
+  const bool want_tok = !p.greedy && (o.tok_v || want_tok_d);
+  // every chunk the refinements read is requested before the first is used: one memory round trip, not four
+  u32x4 wm_v{}, wm_d{}, ws_v{}, ws_d{};
+  if (want_am) {
+    wm_v = fetch_chunk<BF16, EXT>(ra, t.cm_v, p.vocab);
+    wm_d = fetch_chunk<BF16, EXT>(rb, t.cm_d, p.vocab);
+  }
+  if (want_tok) {
+    ws_v = fetch_chunk<BF16, EXT>(ra, t.cs_v, p.vocab);
+    ws_d = fetch_chunk<BF16, EXT>(rb, t.cs_d, p.vocab);
+  }
   int32_t am_v = 0, am_d = 0, tk_v = 0, tk_d = 0;
   if (want_am) {
-    am_v = refine_in_chunk<BF16, false, EXT>(ra, t.cm_v, t.m_v, p.vocab, 0.0f, NoiseKey{0u, 0u}, lane);
-    am_d = refine_in_chunk<BF16, false, EXT>(rb, t.cm_d, t.m_d, p.vocab, 0.0f, NoiseKey{0u, 0u}, lane);
+    am_v = refine_in_chunk<BF16, false>(wm_v, t.cm_v, t.m_v, p.vocab, 0.0f, NoiseKey{0u, 0u}, lane);
+    am_d = refine_in_chunk<BF16, false>(wm_d, t.cm_d, t.m_d, p.vocab, 0.0f, NoiseKey{0u, 0u}, lane);
   }
   if (o.tok_v || want_tok_d) {
     if (p.greedy) {
@@ -718,8 +768,8 @@ __device__ void finalize_row(const VerifyLaunch &p, int64_t r, const Partial &t,
       tk_d = am_d;
     } else {
       const NoiseKey key = noise_key(row_key(p.seed_b, position_of(p, r)));
-      if (o.tok_v) tk_v = refine_in_chunk<BF16, true, EXT>(ra, t.cs_v, t.s_v, p.vocab, p.cT, key, lane);
-      if (want_tok_d) tk_d = refine_in_chunk<BF16, true, EXT>(rb, t.cs_d, t.s_d, p.vocab, p.cT, key, lane);
+      if (o.tok_v) tk_v = refine_in_chunk<BF16, true>(ws_v, t.cs_v, t.s_v, p.vocab, p.cT, key, lane);
+      if (want_tok_d) tk_d = refine_in_chunk<BF16, true>(ws_d, t.cs_d, t.s_d, p.vocab, p.cT, key, lane);
     }
   }
   // the verifier's logit at the drafter's token
@@ -919,39 +969,36 @@ __global__ __launch_bounds__(1024) void read_probe_kernel(VerifyLaunch p, uint32
   const u32x4 *rb = reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.vb) + r * row_bytes);
   constexpr int32_t kSpan = 64 * kStep;
   const int32_t nsteps = c1 > c0 ? (c1 - c0 + kSpan - 1) / kSpan : 0;
-  auto at = [&](int32_t cc) { return cc < c1 ? cc : c0; };
   u32x4 acc = {0u, 0u, 0u, 0u};
   if (nsteps > 0) {
+    const uint32_t nbytes = static_cast<uint32_t>(c1 - c0) * 16u;
+    const __amdgpu_buffer_rsrc_t ba = slice_rsrc(ra + c0, nbytes), bb = slice_rsrc(rb + c0, nbytes);
     u32x4 xa[kStep], xb[kStep], ya[kStep], yb[kStep];
-    int32_t c = c0 + lane;
+    int32_t o = lane;
 #pragma unroll
     for (int k = 0; k < kStep; ++k) {
-      xa[k] = load_stream(ra + at(c + 64 * k));
-      xb[k] = load_stream(rb + at(c + 64 * k));
+      xa[k] = load_stream_at(ba, static_cast<uint32_t>(o + 64 * k) * 16u);
+      xb[k] = load_stream_at(bb, static_cast<uint32_t>(o + 64 * k) * 16u);
     }
     for (int32_t t = 0;;) {
-      ++t;
-      const int32_t cy = t < nsteps ? c + kSpan : c;
 #pragma unroll
       for (int k = 0; k < kStep; ++k) {
-        ya[k] = load_stream(ra + at(cy + 64 * k));
-        yb[k] = load_stream(rb + at(cy + 64 * k));
+        ya[k] = load_stream_at(ba, static_cast<uint32_t>(o + kSpan + 64 * k) * 16u);
+        yb[k] = load_stream_at(bb, static_cast<uint32_t>(o + kSpan + 64 * k) * 16u);
       }
 #pragma unroll
       for (int k = 0; k < kStep; ++k) acc ^= xa[k] ^ xb[k];
-      if (t == nsteps) break;
-      c += kSpan;
-      ++t;
-      const int32_t cx = t < nsteps ? c + kSpan : c;
+      if (++t == nsteps) break;
+      o += kSpan;
 #pragma unroll
       for (int k = 0; k < kStep; ++k) {
-        xa[k] = load_stream(ra + at(cx + 64 * k));
-        xb[k] = load_stream(rb + at(cx + 64 * k));
+        xa[k] = load_stream_at(ba, static_cast<uint32_t>(o + kSpan + 64 * k) * 16u);
+        xb[k] = load_stream_at(bb, static_cast<uint32_t>(o + kSpan + 64 * k) * 16u);
       }
 #pragma unroll
       for (int k = 0; k < kStep; ++k) acc ^= ya[k] ^ yb[k];
-      if (t == nsteps) break;
-      c += kSpan;
+      if (++t == nsteps) break;
+      o += kSpan;
     }
   }
   const uint32_t x = wave_xor(acc.x ^ acc.y ^ acc.z ^ acc.w);

@@ -55,21 +55,49 @@ def _run(cmd, verbose):
         print(err, file=sys.stderr)
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile the library; returns its path. Always recompiles."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+# The host side (argument validation, launch geometry, error text) built with
+# AddressSanitizer and UndefinedBehaviorSanitizer, for checking the C ABI on
+# the CPU. Each -fsanitize= applies to the host compilation only; the device
+# code is built as usual.
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+SANITIZED_LIB = os.path.join(BUILD_DIR, "sanitize", "libdlmverify.so")
+
+
+def asan_runtime() -> str:
+    """The AddressSanitizer runtime of hipcc's clang (preloaded into an uninstrumented Python)."""
+    out = subprocess.run([os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang"),
+                          "--print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = out.stdout.strip()
+    if out.returncode != 0 or not os.path.isabs(path):
+        raise RuntimeError("could not locate libclang_rt.asan-x86_64.so")
+    return path
+
+
+def build(verbose: bool = False, extra_flags=(), sanitize: bool = False) -> str:
+    """Compile the library; returns its path. Always recompiles. With sanitize, the host code is
+    instrumented and the library goes to SANITIZED_LIB (never over the product library)."""
+    out_dir = os.path.dirname(SANITIZED_LIB) if sanitize else BUILD_DIR
+    target = SANITIZED_LIB if sanitize else LIB
+    flags = [*extra_flags, *(SANITIZE_FLAGS if sanitize else [])]
+    os.makedirs(out_dir, exist_ok=True)
     cc = hipcc()
     objs = []
     for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, src.rsplit(".", 1)[0] + ".o")
-        _run([cc, *HIPCC_FLAGS, *PER_SOURCE_FLAGS.get(src, []), *extra_flags, "-I", os.path.join(ROOT, "include"),
+        obj = os.path.join(out_dir, src.rsplit(".", 1)[0] + ".o")
+        _run([cc, *HIPCC_FLAGS, *PER_SOURCE_FLAGS.get(src, []), *flags, "-I", os.path.join(ROOT, "include"),
               "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         objs.append(obj)
-    tmp = LIB + ".tmp"
-    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    tmp = target + ".tmp"
+    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *(SANITIZE_FLAGS if sanitize else []), *objs, "-o", tmp],
+         verbose)
+    os.replace(tmp, target)
+    return target
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if "--sanitize" in sys.argv[1:]:
+        print(build(verbose=True, sanitize=True))
+        print(f"ASAN runtime: {asan_runtime()}")
+    else:
+        print(build(verbose=True))

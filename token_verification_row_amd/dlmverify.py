@@ -15,7 +15,8 @@ import os
 import torch  # loads the HIP runtime the library binds to (same soname)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdlmverify.so")
+# DV_LIBRARY may name another build of the same library (the sanitizer build of build_lib.py)
+LIB_PATH = os.environ.get("DV_LIBRARY") or os.path.join(_HERE, "libdlmverify.so")
 
 DV_OK, DV_ERR_NULL, DV_ERR_SHAPE, DV_ERR_DTYPE, DV_ERR_ALIGN, DV_ERR_ARG, \
     DV_ERR_WORKSPACE, DV_ERR_UNSUPPORTED, DV_ERR_HIP = range(9)

@@ -343,18 +343,63 @@ def main() -> int:
             return 2
         tree = synthetic_tree(plans[0](*inputs[0]), nseq, seq_len, dev)
 
-    def timed(ev_list, fn):
-        if ev_list is None:
+    def timed(ev, fn):
+        """fn() between the events of the pair ev (a list of pairs: a new pair is appended), if any."""
+        if ev is None:
             return fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+        if isinstance(ev, list):
+            ev.append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+            ev = ev[-1]
+        ev[0].record(stream)
         r = fn()
-        e1.record(stream)
-        ev_list.append((e0, e1))
+        ev[1].record(stream)
         return r
+
+    # Without the optional extras, every call of a step is marshalled once, before the timed loop (one
+    # prepared call list per combination of input copy and output set), so that the host enqueues a step
+    # faster than the device runs it and the events around the verify call see no launch gaps.
+    prepared = None
+    if att is None and dv_in is None and tree is None:
+        prepared = {}
+        bufs = []
+        for oi in range(2):
+            got = plans[oi].out
+            z = lambda *shape, dt=torch.int32: torch.empty(shape, dtype=dt, device=dev)
+            bf = dict(score=z(R, dt=torch.float32), decision=z(R, dt=torch.uint8), out_tok=z(R),
+                      prefix=z(max(1, R // (w.group_len or R))), best=z(1), idx=z(nseq, k),
+                      val=z(nseq, k, dt=torch.float32), cnt=z(nseq), mask=z(nseq, seq_len, dt=torch.uint8))
+            bufs.append(bf)
+            calls = [dv.prepare_seed_score(got["entropy"], d_in, d_out, committed, bf["score"])]
+            if w.n_committed:
+                calls.append(dv.prepare_select_topk(bf["score"].view(nseq, seq_len), k, bf["idx"], bf["val"], bf["cnt"],
+                                                    eligible=committed.view(nseq, seq_len), mask=bf["mask"]))
+                calls.append(dv.prepare_decide("COVER", got, bf["decision"], bf["out_tok"], rows=R,
+                                               conf_thr=w.conf_thr, subject=bf["mask"].view(-1)))
+            else:
+                if w.group_len:
+                    calls.append(dv.prepare_decide("COUPLED_ACCEPT", got, bf["decision"], bf["out_tok"], rows=R,
+                                                   group_len=w.group_len, prefix=bf["prefix"], best=bf["best"]))
+                else:
+                    calls.append(dv.prepare_decide("KL_OR_CONF", got, bf["decision"], bf["out_tok"], rows=R,
+                                                   tau_kl=w.tau_kl or 0.05, conf_thr=w.conf_thr or 0.9))
+                sel = got["kl"] if w.number == 5 else bf["score"]
+                calls.append(dv.prepare_select_topk(sel.view(nseq, seq_len), k, bf["idx"], bf["val"], bf["cnt"]))
+            for ci in range(copies):
+                prepared[(ci, oi)] = (plans[oi].prepared(*inputs[ci]), calls)
 
     def step(i, ev=None):
         """verify -> decide -> seed score -> select, with the workload's own rule and selection score."""
+        if prepared is not None:
+            verify, rest = prepared[(i % copies, i % 2)]
+            if ev is not None:
+                ev[0].record(stream)
+                verify()
+                ev[1].record(stream)
+            else:
+                verify()
+            for c in rest:
+                c()
+            return
         a, b = inputs[i % copies]
         plan = plans[i % 2]
         if dv_in is not None:
@@ -383,13 +428,13 @@ def main() -> int:
         dv.dv_select_topk((got["kl"] if w.number == 5 else score).view(nseq, seq_len), k)
 
     n_warm = warm(step)
-    events = []
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
-        step(n_warm + i, events)
+        step(n_warm + i, events[i])
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)

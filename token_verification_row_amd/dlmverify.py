@@ -312,6 +312,15 @@ class VerifyPlan:
                       None if self._tuning is None else ctypes.byref(self._tuning), ctypes.byref(self._stats),
                       self._ws_ptr, self._ws_bytes)
 
+    def prepared(self, verifier, drafter) -> "Prepared":
+        """The call on these logits with every argument marshalled (a descriptor of its own), to be repeated."""
+        for t in (verifier, drafter):
+            if (tuple(t.shape), t.dtype, tuple(t.stride()), t.device) != self._key:
+                raise ValueError("logits differ in shape, dtype, pitch or device from the plan's")
+        d = dv_logits.from_buffer_copy(self._desc)
+        d.verifier, d.drafter = verifier.data_ptr(), drafter.data_ptr()
+        return Prepared("dv_verify_rows", ctypes.byref(d), *self._args[1:], self._stream)
+
     def __call__(self, verifier, drafter):
         """Verify these logits (same shape, dtype, pitch and device as at construction) on the current stream;
         returns the plan's output dict (overwritten by each call)."""
@@ -322,6 +331,45 @@ class VerifyPlan:
         self._desc.drafter = drafter.data_ptr()
         _check(self._lib.dv_verify_rows(*self._args, _stream_handle(verifier.device)), "dv_verify_rows")
         return self.out
+
+
+class Prepared:
+    """One library call with its arguments marshalled once (ctypes objects built from device pointers that
+    stay valid), for loops that repeat the same call on the same buffers: each call only enters the library
+    and checks the status."""
+
+    def __init__(self, name: str, *args):
+        self._fn = getattr(load_library(), name)
+        self._name = name
+        self._args = args
+
+    def __call__(self):
+        _check(self._fn(*self._args), self._name)
+
+
+def prepare_seed_score(u, d_in, d_out, eligible, score) -> Prepared:
+    """dv_seed_score on fixed buffers (float32 [rows] each, eligible uint8 [rows] or None)."""
+    return Prepared("dv_seed_score", u.numel(), _ptr(u), _ptr(d_in), _ptr(d_out), _ptr(eligible), _ptr(score),
+                    _stream_handle(u.device))
+
+
+def prepare_select_topk(score, k, idx, val, cnt, *, eligible=None, mask=None, largest=True) -> Prepared:
+    """dv_select_topk of score [nseq, L] into fixed buffers (no threshold)."""
+    nseq, L = score.shape
+    return Prepared("dv_select_topk", nseq, L, _ptr(score), _ptr(eligible), int(k), int(bool(largest)), 0, 0.0,
+                    _ptr(idx), _ptr(val), _ptr(cnt), _ptr(mask), _stream_handle(score.device))
+
+
+def prepare_decide(rule, stats, decision, out_tok, *, rows, tau_kl=0.0, conf_thr=0.0, mask_token=-1, subject=None,
+                   group_len=0, prefix=None, best=None) -> Prepared:
+    """dv_decide on fixed buffers; ``stats`` maps dv_row_stats members to device tensors."""
+    rule = RULES[rule] if isinstance(rule, str) else int(rule)
+    args = dv_decide_args(rule=rule, tau_kl=float(tau_kl), conf_thr=float(conf_thr), mask_token=int(mask_token),
+                          rows=int(rows), group_len=int(group_len), seed=0, pos=None, pos_period=0)
+    st = dv_row_stats(**{f: (stats[f].data_ptr() if stats.get(f) is not None else None) for f in STAT_FIELDS})
+    dev = decision.device
+    return Prepared("dv_decide", ctypes.byref(args), ctypes.byref(st), _ptr(subject), None, _ptr(decision),
+                    _ptr(out_tok), _ptr(prefix), _ptr(best), _stream_handle(dev))
 
 
 def dv_decide(rule, stats, *, rows=None, tau_kl=0.0, conf_thr=0.0, mask_token=-1, subject=None, cur_tok=None,

@@ -12,8 +12,11 @@
  *
  * Conventions shared by every call:
  *   - Every array pointer is a caller-owned DEVICE pointer (hipMalloc'd or a
- *     torch tensor's data_ptr()). The library allocates nothing and keeps no
- *     state between calls; scratch memory, where a call needs it, is passed in.
+ *     torch tensor's data_ptr()). The library allocates nothing; scratch
+ *     memory, where a call needs it, is passed in. The one exception is
+ *     dv_verify_rows_noalloc, whose scratch is a fixed array in device memory
+ *     (one per GPU, held until the process ends) that every call of it on
+ *     that GPU shares; no other call keeps state between calls.
  *   - Calls validate their arguments on the host first. An invalid argument
  *     returns a status != DV_OK synchronously, before any HIP call, with no
  *     side effect. Valid calls enqueue kernels on `stream` and return without

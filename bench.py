@@ -27,7 +27,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0
 STAT_BYTES_PER_ROW = 36      # 5 float32 + 4 int32 outputs
 EXT_STAT_BYTES_PER_ROW = 44  # + kl_rev and p_tok_d (float32)
-VERIFY_SOURCE = os.path.join(ROOT, "token_verification_row_amd", "csrc", "verify.hip")
+# the streaming kernel and the host code that picks its launch geometry
+VERIFY_SOURCES = [os.path.join(ROOT, "token_verification_row_amd", "csrc", f) for f in ("verify.hip", "api.cpp")]
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "verify_rows_traffic.json")
 
 
@@ -35,20 +36,24 @@ def measured_traffic(workload: int):
     """HBM bytes per verify pass from the committed profiler counters, or None.
 
     The record holds FETCH_SIZE and WRITE_SIZE per pass (already scaled by the
-    plain-copy calibration) and the SHA-256 of the kernel source they were
-    taken on; a changed kernel gives None until the counters are taken again.
+    plain-copy calibration) and the SHA-256 of the kernel source and launch
+    code they were taken on (verify.hip, then api.cpp, concatenated); a change
+    to either gives None until the counters are taken again.
     """
     import hashlib
 
     try:
         with open(TRAFFIC_RECORD) as f:
             rec = json.load(f)
-        with open(VERIFY_SOURCE, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        h = hashlib.sha256()
+        for path in VERIFY_SOURCES:
+            with open(path, "rb") as f:
+                h.update(f.read())
+        sha = h.hexdigest()
     except (OSError, ValueError):
         return None
     entry = rec.get("workloads", {}).get(str(workload))
-    if rec.get("verify_hip_sha256") != sha or not entry:
+    if rec.get("sources_sha256") != sha or not entry:
         return None
     return entry["fetch_bytes"] + entry["write_bytes"]
 

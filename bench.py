@@ -335,6 +335,9 @@ def main() -> int:
             return 2
         att = synthetic_attention(args.influence, w.L, dev)
         att_ws = torch.empty(dv.dv_influence_drift_workspace_bytes(att[0]) + 256, dtype=torch.uint8, device=dev)
+        att_di = torch.empty((w.B, w.L), dtype=torch.float32, device=dev)
+        att_do = torch.empty((w.B, w.L), dtype=torch.float32, device=dev)
+        att_call = dv.prepare_influence_drift(*att, att_di, att_do, att_ws)
         att_ev = []
     dv_in = None
     if args.dual_view:
@@ -411,8 +414,8 @@ def main() -> int:
             timed(dv_ev if ev is not None else None, lambda: dv.dv_dual_view_attention(*dv_in, out=dv_out))
         got = timed(ev, lambda: plan(a, b))
         if att is not None:
-            di, do = timed(att_ev if ev is not None else None,
-                           lambda: dv.dv_influence_drift(*att, workspace=att_ws))
+            timed(att_ev if ev is not None else None, att_call)
+            di, do = att_di, att_do
             score = dv.dv_seed_score(got["entropy"], di.view(-1), do.view(-1), committed)
         else:
             score = dv.dv_seed_score(got["entropy"], d_in, d_out, committed)

@@ -272,14 +272,15 @@ def test_influence_validation_and_workspace(lib):
     out = ctypes.c_size_t(0)
     a = _att(nseq=1, heads=784, length=512)
     assert lib.dv_influence_drift_workspace_bytes(ctypes.byref(a), ctypes.byref(out)) == B.DV_OK
-    # 784 maps: one row tile each -> column partials 784*512 floats, row partials 784*512 floats
-    assert out.value == 784 * 512 * 4 + 784 * 512 * 4
+    # one 64-byte partial (8 column sums, 8 row sums) per (map, row tile, group of 8 positions)
+    # 784 maps: one row tile each, 64 groups
+    assert out.value == 784 * 1 * 64 * 64
     a = _att(nseq=1, heads=32, length=512)                      # 32 maps: 8 tiles of 64 rows
     assert lib.dv_influence_drift_workspace_bytes(ctypes.byref(a), ctypes.byref(out)) == B.DV_OK
-    assert out.value == 32 * 8 * 512 * 4 + 32 * 512 * 4
+    assert out.value == 32 * 8 * 64 * 64
     a = _att(nseq=1, heads=1, length=100, ld=104)
     assert lib.dv_influence_drift_workspace_bytes(ctypes.byref(a), ctypes.byref(out)) == B.DV_OK
-    assert out.value == ((2 * 100 * 4 + 255) // 256) * 256 + 100 * 4      # 2 tiles of 56 rows
+    assert out.value == 1 * 2 * 13 * 64                                    # 2 tiles of 56 rows, 13 groups
     def call(att, qm=FAKE, nc=FAKE, ws=FAKE, ws_bytes=1 << 30):
         return lib.dv_influence_drift(ctypes.byref(att) if att is not None else None, qm, nc, None, None, ws, ws_bytes,
                                       None)

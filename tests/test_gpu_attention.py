@@ -135,6 +135,15 @@ def test_bench_shape_784_maps():
     qm = (torch.rand((1, L), generator=g, device=dev) < 0.4).to(torch.uint8)
     nc = (torch.rand((1, L), generator=g, device=dev) < 0.2).to(torch.uint8)
     d_in, d_out = dv.dv_influence_drift(probs, qm, nc)
+    # the prepared call bench.py times gives the same bits, call after call
+    ws = torch.empty(dv.dv_influence_drift_workspace_bytes(probs) + 256, dtype=torch.uint8, device=dev)
+    p_in, p_out = torch.empty_like(d_in), torch.empty_like(d_out)
+    call = dv.prepare_influence_drift(probs, qm, nc, p_in, p_out, ws)
+    for _ in range(3):
+        p_in.fill_(-1.0)
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(p_in, d_in) and torch.equal(p_out, d_out)
     torch.cuda.synchronize()
     host = probs.view(torch.int16).cpu().numpy().view(np.uint16)
     r_in, r_out = OA.influence_drift(_widen(host, "bf16"), qm.cpu().numpy(), nc.cpu().numpy())

@@ -156,9 +156,7 @@ dv_status influence_geometry(const dv_attention *a, bool need_ptrs, dv::Influenc
   p.len = a->len;
   p.ld = a->ld;
   p.probs = a->probs;
-  const size_t col_bytes = static_cast<size_t>(maps) * tiles * a->len * sizeof(float);
-  const size_t col_aligned = (col_bytes + 255) / 256 * 256;
-  ws = col_aligned + static_cast<size_t>(maps) * a->len * sizeof(float);
+  ws = static_cast<size_t>(maps) * tiles * ((a->len + 7) / 8) * 16 * sizeof(float);
   return DV_OK;
 }
 
@@ -375,13 +373,11 @@ dv_status dv_influence_drift(const dv_attention *att, const uint8_t *query_maske
   if (!workspace) return fail(DV_ERR_WORKSPACE, "workspace of %zu bytes required", ws);
   if (workspace_bytes < ws) return fail(DV_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", ws, workspace_bytes);
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(DV_ERR_ALIGN, "workspace must be 256-byte aligned");
-  const size_t col_bytes = static_cast<size_t>(p.nseq * p.heads) * p.tiles * p.len * sizeof(float);
   p.query_masked = query_masked;
   p.new_cols = new_cols;
   p.d_in = d_in;
   p.d_out = d_out;
-  p.col_part = static_cast<float *>(workspace);
-  p.row_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + (col_bytes + 255) / 256 * 256);
+  p.part = static_cast<float *>(workspace);
   return hip_status(dv::launch_influence(p, stream), "dv_influence_drift launch");
 }
 

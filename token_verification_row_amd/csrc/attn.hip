@@ -8,14 +8,15 @@
 //   d_out[b][i] = (1/H) sum_h sum_{k new}    A[b][h][i][k]
 //
 // Pass 1 reads every attention row once (HBM-bound): one workgroup per
-// (sequence, head, tile of rows), lanes over 16-byte chunks of a row, up to four
-// rows in flight per wave. Each row's mass on new columns is a wave sum, kept by the
-// lane of that row and stored with those of 63 other rows as a per-(sequence,
-// head) row partial; the rows of masked queries are summed into per-lane
-// column accumulators, combined across the four waves in LDS in a fixed order
-// and written as a per-tile column partial. Pass 2 sums the partials of each
-// position over heads and tiles in double precision, in a fixed order, so
-// results do not depend on scheduling.
+// (sequence, head, tile of rows), lanes over 16-byte chunks of a row, a few rows
+// in flight per wave. Each row's mass on new columns is a wave sum, kept by the
+// lane of that row and collected in LDS; the rows of masked queries are summed
+// into per-lane column accumulators, combined across the waves in LDS in a fixed
+// order. The workgroup writes, for every group of 8 positions, its 8 column sums
+// and its 8 row sums as one 64-byte partial, laid out so that the partials of a
+// group from all heads and tiles are contiguous. Pass 2 sums each group's
+// partials in double precision, in a fixed order, so results do not depend on
+// scheduling.
 #include "dv_internal.h"
 
 namespace dv {
@@ -60,12 +61,15 @@ __device__ __forceinline__ void widen(const u32x4 &w, float (&x)[BF16 ? 8 : 4]) 
   }
 }
 
-// M: 16-byte chunks of a row per lane (lane l holds chunks l, l + 64, ...).
-template <bool BF16, int M>
-__global__ __launch_bounds__(256) void influence_rows_kernel(InfluenceLaunch p) {
+// M: 16-byte chunks of a row per lane (lane l holds chunks l, l + 64, ...); NW waves per
+// workgroup; LOADS: 16-byte loads per lane in flight per wave (whole rows).
+template <bool BF16, int M, int NW, int LOADS>
+__global__ __launch_bounds__(64 * NW) void influence_rows_kernel(InfluenceLaunch p) {
   constexpr int N = BF16 ? 8 : 4;
-  constexpr int U = M >= 4 ? 1 : 4 / M;  // rows in flight per wave: about four 16-byte loads per lane
-  __shared__ float col[kMaxInfluenceLen];
+  constexpr int U = M >= LOADS ? 1 : LOADS / M;  // rows in flight per wave
+  constexpr int CAP = 64 * M * N;                 // positions of a row this instantiation covers
+  __shared__ float col[CAP];
+  __shared__ float rsum[CAP];  // the tile's row sums, by row - r0 (a tile has at most len rows)
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t b = blockIdx.z, h = blockIdx.y;
@@ -85,7 +89,7 @@ __global__ __launch_bounds__(256) void influence_rows_kernel(InfluenceLaunch p) 
   // 32-bit word, the bits that belong to the row (the partly filled last
   // chunk of a row carries padding, which is cleared before use)
   constexpr bool kNewInLds = M >= 8;
-  __shared__ float s_new[kNewInLds ? kMaxInfluenceLen : 1];
+  __shared__ float s_new[kNewInLds ? CAP : 1];
   float newf[kNewInLds ? 1 : M][N];
   u32x4 keep[M];
 #pragma unroll
@@ -102,7 +106,7 @@ __global__ __launch_bounds__(256) void influence_rows_kernel(InfluenceLaunch p) 
     keep[m] = u32x4{kw[0], kw[1], kw[2], kw[3]};
   }
   if constexpr (kNewInLds) {
-    for (int32_t j = threadIdx.x; j < nch * N; j += 256) s_new[j] = (j < L && newc[j]) ? 1.0f : 0.0f;
+    for (int32_t j = threadIdx.x; j < nch * N; j += 64 * NW) s_new[j] = (j < L && newc[j]) ? 1.0f : 0.0f;
     __syncthreads();
   }
   float acc[M][N];
@@ -145,19 +149,19 @@ __global__ __launch_bounds__(256) void influence_rows_kernel(InfluenceLaunch p) 
     return wave_sum(rs);
   };
 
-  // this wave's rows: r0 + wave + 4 k, k < K; taken 64 at a time so that lane
+  // this wave's rows: r0 + wave + NW k, k < K; taken 64 at a time so that lane
   // k holds the query mask and, at the end, the row sum of row k of the group
-  const int32_t K = r1 > r0 + wave ? (r1 - r0 - wave + 3) / 4 : 0;
+  const int32_t K = r1 > r0 + wave ? (r1 - r0 - wave + NW - 1) / NW : 0;
   for (int32_t g = 0; g < K; g += 64) {
     const int32_t kn = min(64, K - g);
-    const int32_t my_row = r0 + wave + 4 * (g + lane);
+    const int32_t my_row = r0 + wave + NW * (g + lane);
     const unsigned long long qbits = __ballot(lane < kn && qmask[my_row] != 0);
     float my_sum = 0.0f;
     int32_t k = 0;
     for (; k + U <= kn; k += U) {  // U rows of this wave in flight
       u32x4 w[U][M];
 #pragma unroll
-      for (int u = 0; u < U; ++u) load_row(r0 + wave + 4 * (g + k + u), w[u]);
+      for (int u = 0; u < U; ++u) load_row(r0 + wave + NW * (g + k + u), w[u]);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const float su = fold_row((qbits >> (k + u)) & 1ull, w[u]);
@@ -166,15 +170,15 @@ __global__ __launch_bounds__(256) void influence_rows_kernel(InfluenceLaunch p) 
     }
     for (; k < kn; ++k) {
       u32x4 w0[M];
-      load_row(r0 + wave + 4 * (g + k), w0);
+      load_row(r0 + wave + NW * (g + k), w0);
       const float s0 = fold_row((qbits >> k) & 1ull, w0);
       my_sum = lane == k ? s0 : my_sum;
     }
-    if (lane < kn) p.row_part[bh * L + my_row] = my_sum;
+    if (lane < kn) rsum[my_row - r0] = my_sum;
   }
 
-  // column sums of the tile: wave 0 writes, waves 1..3 add, in that order
-  for (int w = 0; w < 4; ++w) {
+  // column sums of the tile: wave 0 writes, the others add, in wave order
+  for (int w = 0; w < NW; ++w) {
     if (wave == w) {
 #pragma unroll
       for (int m = 0; m < M; ++m) {
@@ -188,49 +192,76 @@ __global__ __launch_bounds__(256) void influence_rows_kernel(InfluenceLaunch p) 
     }
     __syncthreads();
   }
-  float *out = p.col_part + (bh * p.tiles + tile) * L;
-  for (int32_t j = threadIdx.x; j < L; j += 256) out[j] = col[j];
+  // the partials: 64 bytes per group of 8 positions, four 16-byte stores (columns 0-3,
+  // 4-7, rows 0-3, 4-7 of the group)
+  const int32_t G = (L + 7) / 8;
+  const int64_t mtot = p.heads * p.tiles, mine = h * p.tiles + tile;
+  float4 *out = reinterpret_cast<float4 *>(p.part);
+  for (int32_t x = threadIdx.x; x < 4 * G; x += 64 * NW) {
+    const int32_t grp = x >> 2, q = x & 3;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int32_t i = 8 * grp + 4 * (q & 1) + e;
+      if (q < 2) v[e] = i < L ? col[i] : 0.0f;
+      else v[e] = (i >= r0 && i < r1) ? rsum[i - r0] : 0.0f;
+    }
+    out[((b * G + grp) * mtot + mine) * 4 + q] = make_float4(v[0], v[1], v[2], v[3]);
+  }
 }
 
-// d_in and d_out of every (sequence, position): the partials summed over heads
-// (and tiles) in double precision. A block takes 8 positions; thread (s, c)
-// sums partials s, s + 128, ... of position c in order, then a fixed binary
-// tree over s adds the 128 sums, so the result does not depend on scheduling.
-constexpr int kRedCols = 8, kRedSplit = 128;
-
-__global__ __launch_bounds__(kRedCols * kRedSplit) void influence_reduce_kernel(InfluenceLaunch p) {
-  __shared__ double red_in[kRedSplit][kRedCols], red_out[kRedSplit][kRedCols];
-  const int c = threadIdx.x % kRedCols, sp = threadIdx.x / kRedCols;
-  const int64_t b = blockIdx.y, j = static_cast<int64_t>(blockIdx.x) * kRedCols + c;
-  double si = 0.0, so = 0.0;
-  if (j < p.len) {
-    const int64_t mc = p.heads * p.tiles;  // column partials of a sequence, in (head, tile) order
-    const float *cp = p.col_part + b * mc * p.len + j;
-    for (int64_t m = sp; m < mc; m += kRedSplit) si += cp[m * p.len];
-    const float *rp = p.row_part + b * p.heads * p.len + j;
-    for (int64_t h = sp; h < p.heads; h += kRedSplit) so += rp[h * p.len];
+// d_in and d_out of every (sequence, group of 8 positions): the group's partials
+// from all heads and tiles, contiguous, summed in double precision. Thread (s, q)
+// sums float4 q of partials s, s + 256, ... in order, then a fixed binary tree over
+// s adds the 256 sums, so the result does not depend on scheduling.
+constexpr int kRedSplit = 256;
+__global__ __launch_bounds__(4 * kRedSplit) void influence_reduce_kernel(InfluenceLaunch p) {
+  __shared__ double red[kRedSplit][17];  // 16 sums per split, padded against bank conflicts
+  const int q = threadIdx.x & 3, sp = threadIdx.x >> 2;
+  const int64_t b = blockIdx.y, grp = blockIdx.x;
+  const int64_t G = (p.len + 7) / 8, mtot = p.heads * p.tiles;
+  const float4 *src = reinterpret_cast<const float4 *>(p.part) + (b * G + grp) * mtot * 4 + q;
+  double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+#pragma unroll 4
+  for (int64_t m = sp; m < mtot; m += kRedSplit) {
+    const float4 v = src[m * 4];
+    s0 += v.x;
+    s1 += v.y;
+    s2 += v.z;
+    s3 += v.w;
   }
-  red_in[sp][c] = si;
-  red_out[sp][c] = so;
+  red[sp][4 * q] = s0;
+  red[sp][4 * q + 1] = s1;
+  red[sp][4 * q + 2] = s2;
+  red[sp][4 * q + 3] = s3;
   __syncthreads();
   for (int stride = kRedSplit / 2; stride > 0; stride >>= 1) {
     if (sp < stride) {
-      red_in[sp][c] += red_in[sp + stride][c];
-      red_out[sp][c] += red_out[sp + stride][c];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[sp][4 * q + e] += red[sp + stride][4 * q + e];
     }
     __syncthreads();
   }
-  if (sp == 0 && j < p.len) {
+  if (sp == 0) {
     const double inv = 1.0 / static_cast<double>(p.heads);
-    if (p.d_in) p.d_in[b * p.len + j] = static_cast<float>(red_in[0][c] * inv);
-    if (p.d_out) p.d_out[b * p.len + j] = static_cast<float>(red_out[0][c] * inv);
+    float *dst = q < 2 ? p.d_in : p.d_out;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t i = 8 * grp + 4 * (q & 1) + e;
+      if (dst && i < p.len) dst[b * p.len + i] = static_cast<float>(red[0][4 * q + e] * inv);
+    }
   }
 }
 
+// Rows of one 16-byte chunk per lane (up to 512 bf16 positions) stream best from two waves with
+// eight rows each in flight; longer rows from four waves with four 16-byte loads per lane.
 template <bool BF16, int M>
 hipError_t launch_rows(const InfluenceLaunch &p, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(p.tiles), static_cast<unsigned>(p.heads), static_cast<unsigned>(p.nseq));
-  hipLaunchKernelGGL((influence_rows_kernel<BF16, M>), grid, dim3(256), 0, stream, p);
+  if constexpr (M == 1)
+    hipLaunchKernelGGL((influence_rows_kernel<BF16, M, 2, 8>), grid, dim3(128), 0, stream, p);
+  else
+    hipLaunchKernelGGL((influence_rows_kernel<BF16, M, 4, 4>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -254,8 +285,8 @@ hipError_t launch_influence(const InfluenceLaunch &p, hipStream_t stream) {
   if (p.nseq == 0 || p.heads == 0) return hipSuccess;
   hipError_t e = p.bf16 ? launch_typed<true>(p, stream) : launch_typed<false>(p, stream);
   if (e != hipSuccess) return e;
-  const dim3 grid(static_cast<unsigned>((p.len + kRedCols - 1) / kRedCols), static_cast<unsigned>(p.nseq));
-  hipLaunchKernelGGL(influence_reduce_kernel, grid, dim3(kRedCols * kRedSplit), 0, stream, p);
+  const dim3 grid(static_cast<unsigned>((p.len + 7) / 8), static_cast<unsigned>(p.nseq));
+  hipLaunchKernelGGL(influence_reduce_kernel, grid, dim3(4 * kRedSplit), 0, stream, p);
   return hipGetLastError();
 }
 

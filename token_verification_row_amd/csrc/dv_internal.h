@@ -152,8 +152,10 @@ struct InfluenceLaunch {
   int64_t nseq, heads, len, ld;
   const uint8_t *query_masked, *new_cols;  // [nseq][len]
   float *d_in, *d_out;                     // [nseq][len]
-  float *col_part;                         // workspace [nseq][heads][tiles][len]
-  float *row_part;                         // workspace [nseq][heads][len]
+  // workspace [nseq][ceil(len / 8)][heads * tiles][16]: for each group of 8 positions and each
+  // (head, tile), the tile's 8 column sums (d_in) then its 8 row sums (d_out; 0 for rows
+  // outside the tile), so that the reduction reads each group's partials contiguously
+  float *part;
 };
 hipError_t launch_influence(const InfluenceLaunch &p, hipStream_t stream);
 

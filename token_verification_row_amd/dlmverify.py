@@ -537,6 +537,27 @@ def dv_influence_drift(probs, query_masked, new_cols, *, workspace=None):
     return d_in, d_out
 
 
+def prepare_influence_drift(probs, query_masked, new_cols, d_in, d_out, workspace) -> Prepared:
+    """dv_influence_drift on fixed buffers (d_in, d_out float32 [nseq, len]; workspace uint8 of at least
+    dv_influence_drift_workspace_bytes(probs) + 256 bytes), marshalled once."""
+    att = _attention_desc(probs)
+    B, H, L, _ = probs.shape
+    for name, t, dt in (("query_masked", query_masked, torch.uint8), ("new_cols", new_cols, torch.uint8),
+                        ("d_in", d_in, torch.float32), ("d_out", d_out, torch.float32)):
+        _need_cuda(t, name)
+        if t.dtype != dt or tuple(t.shape) != (B, L) or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous {dt} [nseq, len] tensor")
+    base = workspace.data_ptr()
+    ws_ptr = (base + 255) // 256 * 256
+    avail = workspace.numel() - (ws_ptr - base)
+    if avail < dv_influence_drift_workspace_bytes(probs):
+        raise ValueError("workspace too small")
+    call = Prepared("dv_influence_drift", ctypes.byref(att), _ptr(query_masked), _ptr(new_cols), _ptr(d_in),
+                    _ptr(d_out), ctypes.c_void_p(ws_ptr), avail, _stream_handle(probs.device))
+    call._keep = att  # the descriptor lives as long as the call
+    return call
+
+
 def dv_dual_view_attention(q, k_cur, v_cur, k_prev, v_prev, seed, *, scale=None, out=None):
     """COVER's dual-view attention. q: bf16 [nseq, heads, len, head_dim]; k_cur, v_cur, k_prev,
     v_prev: bf16 [nseq, kv_heads, len, head_dim]; seed: uint8 [nseq, len]. Returns float32

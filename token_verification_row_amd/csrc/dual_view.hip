@@ -225,14 +225,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
     }
     float red[8];  // pairwise trees keep the dependency chains short
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sc[i] *= cs;
-#pragma unroll
     for (int i = 0; i < 8; ++i) red[i] = fmaxf(sc[i], sc[i + 8]);
 #pragma unroll
     for (int w = 4; w >= 1; w /= 2)
 #pragma unroll
       for (int i = 0; i < w; ++i) red[i] = fmaxf(red[i], red[i + w]);
-    const float tmax = max_halves(red[0]);
+    const float tmax = max_halves(red[0]) * cs;  // cs > 0: the maximum of the scaled scores
     const bool raise = tmax > m + kLazy;  // true on the first block (m = -inf)
     if (__ballot(raise) != 0) {
       const float mn = raise ? tmax : m;
@@ -245,7 +243,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
         for (int i = 0; i < 16; ++i) o[c][i] *= corr;
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sc[i] = __builtin_amdgcn_exp2f(sc[i] - m);
+    for (int i = 0; i < 16; ++i) sc[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], cs, -m));
 #pragma unroll
     for (int i = 0; i < 8; ++i) red[i] = sc[i] + sc[i + 8];
 #pragma unroll
@@ -328,7 +326,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
   if (q_seed) {
     // the diagonal's value: the tiles held V_prev there, a seed query reads V_cur; its
     // weight against the final reference m is the tile's weight times every later rescale
-    const float pd = __builtin_amdgcn_exp2f(own * cs - m);
+    const float pd = __builtin_amdgcn_exp2f(__builtin_fmaf(own, cs, -m));
     const uint16_t *vc = Vc + static_cast<int64_t>(qi) * D;
     const uint16_t *vp = Vp + static_cast<int64_t>(qi) * D;
 #pragma unroll

@@ -131,7 +131,7 @@ def test_seed_score():
         np.testing.assert_allclose(g[fin], ref[fin], rtol=1e-6, atol=0)
 
 
-@pytest.mark.parametrize("L", [1, 2, 3, 17, 64, 1000, 1024, 2048, 5000, 16384])
+@pytest.mark.parametrize("L", [1, 2, 3, 17, 64, 1000, 1024, 2048, 2049, 5000, 16384])
 def test_select_topk_exact(L):
     print(f"case: select L={L}", flush=True)
     dev = _dev()

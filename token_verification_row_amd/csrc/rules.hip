@@ -209,7 +209,80 @@ __device__ __forceinline__ unsigned long long select_key(float s, uint32_t i, in
   return (static_cast<unsigned long long>(ord) << 32) | static_cast<unsigned long long>(0xFFFFFFFFu - i);
 }
 
-// One workgroup per sequence: bitonic sort of pow2 keys in LDS.
+// Sequences of up to kRankMaxLen positions: the sorted position of each kept entry is its
+// rank, the number of keys above its own (keys are distinct: the index is part of them).
+// One 4-wave workgroup per (sequence, 64 positions): the workgroup builds all the
+// sequence's keys in LDS (every load issued before the first is used) and counts the
+// entries the threshold keeps; each wave then ranks the 64 positions against a quarter of
+// the keys, and the quarters' counts are added in LDS. The workgroups of a sequence write
+// disjoint outputs, so none waits for another. Scores are not NaN, so the kept entries (key
+// above the threshold's key) are a prefix of the order and their number is
+// min(k, number of kept entries). Same keys, same order as the sort.
+constexpr int32_t kRankMaxLen = 2048;
+constexpr int kRankThreads = 256;
+__global__ __launch_bounds__(kRankThreads) void select_rank_kernel(SelectLaunch p) {
+  constexpr int kPer = kRankMaxLen / kRankThreads;  // keys built per thread, at most
+  __shared__ unsigned long long keys[kRankMaxLen];
+  __shared__ int32_t part[4][64];
+  __shared__ int32_t wave_kept[4];
+  const int64_t seq = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t L = static_cast<int32_t>(p.seq_len);
+  const float *sc = p.score + seq * p.seq_len;
+  const uint8_t *el = p.eligible ? p.eligible + seq * p.seq_len : nullptr;
+  // the threshold's key without its index word: a score is kept iff its key's upper word is above it
+  const uint32_t thr_ord = static_cast<uint32_t>(select_key(p.thr, 0u, p.largest) >> 32);
+  // loads at clamped (always valid) positions, all issued before the first is used
+  float v[kPer];
+  uint32_t e[kPer];
+#pragma unroll
+  for (int t = 0; t < kPer; ++t) v[t] = sc[min(t * kRankThreads + tid, L - 1)];
+  if (el) {
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) e[t] = el[min(t * kRankThreads + tid, L - 1)];
+  } else {
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) e[t] = 1u;
+  }
+  int32_t kept = 0;
+#pragma unroll
+  for (int t = 0; t < kPer; ++t) {
+    const int32_t j = t * kRankThreads + tid;
+    const bool ok = j < L && e[t] != 0;
+    const unsigned long long k = ok ? select_key(v[t], static_cast<uint32_t>(j), p.largest) : 0ull;
+    if (j < L) keys[j] = k;
+    const bool keep = k != 0 && (!p.use_thr || static_cast<uint32_t>(k >> 32) > thr_ord);
+    kept += __popcll(__ballot(keep));
+  }
+  if (lane == 0) wave_kept[wave] = kept;
+  __syncthreads();
+  const int32_t count = min(p.k, wave_kept[0] + wave_kept[1] + wave_kept[2] + wave_kept[3]);
+  const int32_t i = static_cast<int32_t>(blockIdx.y) * 64 + lane;
+  const unsigned long long ki = i < L ? keys[i] : 0ull;
+  const int32_t q = (L + 3) / 4, j0 = wave * q, j1 = min(L, j0 + q);
+  int32_t r = 0;
+#pragma unroll 16
+  for (int32_t j = j0; j < j1; ++j) r += keys[j] > ki ? 1 : 0;
+  part[wave][lane] = r;
+  __syncthreads();
+  if (wave != 0) return;
+  const int32_t rank = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
+  const bool sel = ki != 0 && rank < count;
+  if (sel) {
+    if (p.out_idx) p.out_idx[seq * p.k + rank] = i;
+    if (p.out_val) p.out_val[seq * p.k + rank] = sc[i];
+  }
+  if (p.out_mask && i < L) p.out_mask[seq * p.seq_len + i] = sel ? 1 : 0;
+  if (blockIdx.y == 0) {
+    for (int32_t j = count + lane; j < p.k; j += 64) {
+      if (p.out_idx) p.out_idx[seq * p.k + j] = -1;
+      if (p.out_val) p.out_val[seq * p.k + j] = __builtin_nanf("");
+    }
+    if (lane == 0 && p.out_count) p.out_count[seq] = count;
+  }
+}
+
+// Longer sequences: one workgroup per sequence, bitonic sort of pow2 keys in LDS.
 __global__ __launch_bounds__(1024) void select_topk_kernel(SelectLaunch p, int32_t pow2) {
   extern __shared__ unsigned long long keys[];
   uint8_t *flags = reinterpret_cast<uint8_t *>(keys + pow2);
@@ -302,6 +375,11 @@ hipError_t launch_seed_score(int64_t rows, const float *u, const float *d_in, co
 
 hipError_t launch_select_topk(const SelectLaunch &p, hipStream_t stream) {
   if (p.nseq == 0) return hipSuccess;
+  if (p.seq_len <= kRankMaxLen) {
+    const dim3 grid(static_cast<unsigned>(p.nseq), static_cast<unsigned>((p.seq_len + 63) / 64));
+    hipLaunchKernelGGL(select_rank_kernel, grid, dim3(kRankThreads), 0, stream, p);
+    return hipGetLastError();
+  }
   int32_t pow2 = 2;
   while (pow2 < p.seq_len) pow2 <<= 1;
   const size_t lds = static_cast<size_t>(pow2) * sizeof(unsigned long long) + static_cast<size_t>(p.seq_len);

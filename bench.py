@@ -1,8 +1,9 @@
 """Throughput of the verification hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic logits:
-dv_verify_rows (the fused verify pass), dv_decide, dv_seed_score and
-dv_select_topk. The default workload is the SPOT-style tree of 64 candidate
+dv_verify_rows (the fused verify pass), dv_decide, and the seed score with its
+per-sequence selection (dv_seed_select; at workload 5, which ranks by KL,
+dv_seed_score and dv_select_topk). The default workload is the SPOT-style tree of 64 candidate
 block states x 32 positions over a 151 936-token vocabulary, bf16, T = 1,
 noise shared per position (coupled-noise acceptance per candidate).
 
@@ -381,26 +382,33 @@ def main() -> int:
                       prefix=z(max(1, R // (w.group_len or R))), best=z(1), idx=z(nseq, k),
                       val=z(nseq, k, dt=torch.float32), cnt=z(nseq), mask=z(nseq, seq_len, dt=torch.uint8))
             bufs.append(bf)
-            calls = [dv.prepare_seed_score(got["entropy"], d_in, d_out, committed, bf["score"])]
+            # the seed score and its selection are one call, except at workload 5, which ranks by KL
+            u2 = got["entropy"].view(nseq, seq_len)
             if w.n_committed:
-                calls.append(dv.prepare_select_topk(bf["score"].view(nseq, seq_len), k, bf["idx"], bf["val"], bf["cnt"],
-                                                    eligible=committed.view(nseq, seq_len), mask=bf["mask"]))
-                calls.append(dv.prepare_decide("COVER", got, bf["decision"], bf["out_tok"], rows=R,
-                                               conf_thr=w.conf_thr, subject=bf["mask"].view(-1)))
+                calls = [dv.prepare_seed_select(u2, d_in, d_out, committed, bf["score"], k, bf["idx"], bf["val"],
+                                                bf["cnt"], select_eligible=committed, mask=bf["mask"]),
+                         dv.prepare_decide("COVER", got, bf["decision"], bf["out_tok"], rows=R,
+                                           conf_thr=w.conf_thr, subject=bf["mask"].view(-1))]
             else:
+                if w.number == 5:
+                    calls = [dv.prepare_seed_score(got["entropy"], d_in, d_out, committed, bf["score"])]
+                else:
+                    calls = [dv.prepare_seed_select(u2, d_in, d_out, committed, bf["score"], k, bf["idx"], bf["val"],
+                                                    bf["cnt"])]
                 if w.group_len:
                     calls.append(dv.prepare_decide("COUPLED_ACCEPT", got, bf["decision"], bf["out_tok"], rows=R,
                                                    group_len=w.group_len, prefix=bf["prefix"], best=bf["best"]))
                 else:
                     calls.append(dv.prepare_decide("KL_OR_CONF", got, bf["decision"], bf["out_tok"], rows=R,
                                                    tau_kl=w.tau_kl or 0.05, conf_thr=w.conf_thr or 0.9))
-                sel = got["kl"] if w.number == 5 else bf["score"]
-                calls.append(dv.prepare_select_topk(sel.view(nseq, seq_len), k, bf["idx"], bf["val"], bf["cnt"]))
+                if w.number == 5:
+                    calls.append(dv.prepare_select_topk(got["kl"].view(nseq, seq_len), k, bf["idx"], bf["val"],
+                                                        bf["cnt"]))
             for ci in range(copies):
                 prepared[(ci, oi)] = (plans[oi].prepared(*inputs[ci]), calls)
 
     def step(i, ev=None):
-        """verify -> decide -> seed score -> select, with the workload's own rule and selection score."""
+        """verify -> decide, seed score + select, with the workload's own rule and selection score."""
         if prepared is not None:
             verify, rest = prepared[(i % copies, i % 2)]
             if ev is not None:
@@ -417,16 +425,15 @@ def main() -> int:
         if dv_in is not None:
             timed(dv_ev if ev is not None else None, lambda: dv.dv_dual_view_attention(*dv_in, out=dv_out))
         got = timed(ev, lambda: plan(a, b))
+        di, do = d_in, d_out
         if att is not None:
             timed(att_ev if ev is not None else None, att_call)
-            di, do = att_di, att_do
-            score = dv.dv_seed_score(got["entropy"], di.view(-1), do.view(-1), committed)
-        else:
-            score = dv.dv_seed_score(got["entropy"], d_in, d_out, committed)
+            di, do = att_di.view(-1), att_do.view(-1)
+        u2 = got["entropy"].view(nseq, seq_len)
         if w.n_committed:
             # COVER: the top seeds among committed positions are re-verified (KEEP / REPLACE / REMASK)
-            _, _, _, mask = dv.dv_select_topk(score.view(nseq, seq_len), k, eligible=committed.view(nseq, seq_len),
-                                              want_mask=True)
+            _, _, _, _, mask = dv.dv_seed_select(u2, di, do, k, seed_eligible=committed, select_eligible=committed,
+                                                 want_mask=True)
             dv.dv_decide("COVER", got, conf_thr=w.conf_thr, mask_token=-1, subject=mask.view(-1))
             return
         if tree is not None:
@@ -437,7 +444,11 @@ def main() -> int:
         else:
             dv.dv_decide("KL_OR_CONF", got, tau_kl=w.tau_kl or 0.05, conf_thr=w.conf_thr or 0.9, mask_token=-1)
         # workload 5 ranks positions by KL; the others by the seed score
-        dv.dv_select_topk((got["kl"] if w.number == 5 else score).view(nseq, seq_len), k)
+        if w.number == 5:
+            dv.dv_seed_score(got["entropy"], di, do, committed)
+            dv.dv_select_topk(got["kl"].view(nseq, seq_len), k)
+        else:
+            dv.dv_seed_select(u2, di, do, k, seed_eligible=committed)
 
     n_warm = warm(step)
     every = max(1, args.sample_every) if args.steps >= 5 * max(1, args.sample_every) else 1
@@ -489,7 +500,8 @@ def main() -> int:
                                + (f", noise shared per position (period {period}), coupled acceptance per "
                                   f"{w.group_len}-row candidate" if period else ""),
                    "rows": R, "vocab": V, "input_copies": copies,
-                   "step": "dv_verify_rows + dv_seed_score + dv_select_topk + "
+                   "step": "dv_verify_rows + "
+                           + ("dv_seed_score + dv_select_topk + " if w.number == 5 else "dv_seed_select + ")
                            + ("dv_tree_accept" if tree is not None else "dv_decide")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": None if args.extended else measured_traffic(w.number),
@@ -520,7 +532,7 @@ def main() -> int:
         line["influence"] = {"maps": args.influence, "len": w.L, **att_us, "avg_us": att_us["mean_us"],
                              "bytes_per_launch": att_bytes,
                              "achieved_GBps": att_bytes / (att_us["median_us"] * 1e-6) / 1e9}
-        line["config"]["step"] = "dv_verify_rows + dv_influence_drift + dv_seed_score + dv_select_topk + dv_decide"
+        line["config"]["step"] = "dv_verify_rows + dv_influence_drift + dv_seed_select + dv_decide"
     print(json.dumps(line), flush=True)
     return 0
 

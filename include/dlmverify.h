@@ -271,6 +271,23 @@ dv_status dv_select_topk(int64_t nseq, int64_t seq_len, const float *score, cons
                          int32_t k, int32_t largest, int32_t use_thr, float thr, int32_t *out_idx,
                          float *out_val, int32_t *out_count, uint8_t *out_mask, hipStream_t stream);
 
+/* The seed score and the per-sequence selection of it in one call ([COVER] §2:
+ * every position's seed score, then the top-scoring positions become the
+ * seeds). Output for output the same as dv_seed_score(nseq * seq_len, u, d_in,
+ * d_out, seed_eligible, score) followed by dv_select_topk(nseq, seq_len,
+ * score, select_eligible, k, largest, use_thr, thr, ...): u, d_in, d_out are
+ * device float32 [nseq][seq_len]; seed_eligible and select_eligible uint8
+ * [nseq][seq_len] or NULL; score (required) receives the seed scores; the
+ * selection outputs are dv_select_topk's. Up to 2048 positions per sequence
+ * it is one launch (the selection computes the scores it ranks); longer
+ * sequences take the two launches. Errors: DV_ERR_NULL (u, d_in, d_out or
+ * score NULL), DV_ERR_SHAPE (nseq < 0, seq_len < 1), DV_ERR_ARG (k < 1 or
+ * k > seq_len, thr not finite), DV_ERR_UNSUPPORTED (seq_len > 16384). */
+dv_status dv_seed_select(int64_t nseq, int64_t seq_len, const float *u, const float *d_in, const float *d_out,
+                         const uint8_t *seed_eligible, float *score, const uint8_t *select_eligible,
+                         int32_t k, int32_t largest, int32_t use_thr, float thr, int32_t *out_idx,
+                         float *out_val, int32_t *out_count, uint8_t *out_mask, hipStream_t stream);
+
 /* Shape of dv_tree_accept's input: ntrees independent trees of `nodes` nodes
  * each over blocks of `block_len` positions. */
 typedef struct dv_tree_args {

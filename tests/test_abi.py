@@ -30,7 +30,7 @@ def _declared_functions():
 def test_exports_every_declared_function(lib):
     names = _declared_functions()
     assert names == sorted(["dv_verify_workspace_bytes", "dv_verify_rows", "dv_verify_rows_noalloc", "dv_decide", "dv_seed_score",
-                           "dv_select_topk", "dv_tree_accept", "dv_influence_drift_workspace_bytes",
+                           "dv_select_topk", "dv_seed_select", "dv_tree_accept", "dv_influence_drift_workspace_bytes",
                            "dv_influence_drift", "dv_dual_view_attention", "dv_debug_hash", "dv_debug_noise", "dv_debug_read_probe", "dv_status_str",
                            "dv_last_error", "dv_version"])
     for n in names:
@@ -170,6 +170,16 @@ def test_seed_score_select_hash_validation(lib):
     assert sel(1, 16385, FAKE, None, 3, 1, 0, 0.0, None, None, None, None, None) == B.DV_ERR_UNSUPPORTED
     assert sel(1, 10, None, None, 3, 1, 0, 0.0, None, None, None, None, None) == B.DV_ERR_NULL
     assert sel(0, 10, None, None, 3, 1, 0, 0.0, None, None, None, None, None) == B.DV_OK
+    ss = lib.dv_seed_select
+    assert ss(-1, 10, FAKE, FAKE, FAKE, None, FAKE, None, 1, 1, 0, 0.0, None, None, None, None, None) == B.DV_ERR_SHAPE
+    assert ss(1, 0, FAKE, FAKE, FAKE, None, FAKE, None, 1, 1, 0, 0.0, None, None, None, None, None) == B.DV_ERR_SHAPE
+    assert ss(1, 16385, FAKE, FAKE, FAKE, None, FAKE, None, 1, 1, 0, 0.0, None, None, None, None, None) == B.DV_ERR_UNSUPPORTED
+    assert ss(1, 10, FAKE, FAKE, FAKE, None, FAKE, None, 11, 1, 0, 0.0, None, None, None, None, None) == B.DV_ERR_ARG
+    assert ss(1, 10, FAKE, FAKE, FAKE, None, FAKE, None, 3, 1, 1, float("nan"), None, None, None, None, None) == B.DV_ERR_ARG
+    assert ss(1, 10, FAKE, None, FAKE, None, FAKE, None, 3, 1, 0, 0.0, None, None, None, None, None) == B.DV_ERR_NULL
+    assert ss(1, 10, FAKE, FAKE, FAKE, None, None, None, 3, 1, 0, 0.0, None, None, None, None, None) == B.DV_ERR_NULL
+    assert ss(1 << 30, 16, FAKE, FAKE, FAKE, None, FAKE, None, 3, 1, 0, 0.0, None, None, None, None, None) == B.DV_ERR_SHAPE
+    assert ss(0, 10, None, None, None, None, None, None, 3, 1, 0, 0.0, None, None, None, None, None) == B.DV_OK
     assert lib.dv_debug_hash(0, None, 0, -1, 4, FAKE, None) == B.DV_ERR_SHAPE
     assert lib.dv_debug_hash(0, None, -1, 1, 4, FAKE, None) == B.DV_ERR_SHAPE
     assert lib.dv_debug_hash(0, None, 0, 2, 4, None, None) == B.DV_ERR_NULL

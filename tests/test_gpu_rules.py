@@ -1,4 +1,4 @@
-"""GPU parity of dv_decide, dv_seed_score and dv_select_topk, alone (fed the
+"""GPU parity of dv_decide, dv_seed_score, dv_select_topk and dv_seed_select, alone (fed the
 same fp32 inputs as the oracle: exact) and chained after dv_verify_rows on the
 workloads (against the oracle's own statistics: exact outside the near-tie
 bands)."""
@@ -162,6 +162,55 @@ def test_select_topk_exact(L):
                     for s in range(nseq):
                         m[s, ri[s, :rc[s]]] = 1
                     np.testing.assert_array_equal(mask.cpu().numpy(), m, err_msg=ctx)
+
+
+@pytest.mark.parametrize("L", [1, 5, 32, 64, 100, 1024, 2048, 2049, 4096])
+def test_seed_select_matches_two_calls(L):
+    """dv_seed_select gives, output for output and bit for bit, dv_seed_score followed by dv_select_topk
+    (one launch up to 2048 positions, two beyond), and the oracle's selection of those scores."""
+    print(f"case: seed select L={L}", flush=True)
+    dev = _dev()
+    rng = np.random.default_rng(1000 + L)
+    nseq = 4
+    u = rng.uniform(0, 4, (nseq, L)).round(1).astype(np.float32)       # many equal scores
+    d_in = rng.uniform(0, 1, (nseq, L)).round(1).astype(np.float32)
+    d_out = rng.uniform(0, 1, (nseq, L)).round(1).astype(np.float32)
+    u[0, : min(L, 3)] = 0.0
+    seed_el = (rng.random((nseq, L)) < 0.8).astype(np.uint8)
+    sel_el = (rng.random((nseq, L)) < 0.7).astype(np.uint8)
+    sel_el[1] = 0
+    gu, gi, go = _t(u, dev), _t(d_in, dev), _t(d_out, dev)
+    bits = lambda x: x.contiguous().view(torch.int32).cpu().numpy()
+    for k in sorted({1, min(L, 4), min(L, 64), L}):
+        for largest in (True, False):
+            for use_thr, thr in ((False, 0.0), (True, 1.0)):
+                for se in (None, seed_el):
+                    for xe in (None, sel_el):
+                        ctx = f"L={L} k={k} largest={largest} thr={use_thr} seed_el={se is not None} sel_el={xe is not None}"
+                        gse = None if se is None else _t(se, dev)
+                        gxe = None if xe is None else _t(xe, dev)
+                        score, idx, val, cnt, mask = dv.dv_seed_select(gu, gi, go, k, seed_eligible=gse,
+                                                                       select_eligible=gxe, largest=largest,
+                                                                       use_thr=use_thr, thr=thr, want_mask=True)
+                        rs = dv.dv_seed_score(gu.view(-1), gi.view(-1), go.view(-1), None if gse is None else gse.view(-1))
+                        ri, rv, rc, rm = dv.dv_select_topk(rs.view(nseq, L), k, eligible=gxe, largest=largest,
+                                                           use_thr=use_thr, thr=thr, want_mask=True)
+                        np.testing.assert_array_equal(bits(score.view(-1)), bits(rs), err_msg=ctx)
+                        np.testing.assert_array_equal(idx.cpu().numpy(), ri.cpu().numpy(), err_msg=ctx)
+                        np.testing.assert_array_equal(bits(val), bits(rv), err_msg=ctx)
+                        np.testing.assert_array_equal(cnt.cpu().numpy(), rc.cpu().numpy(), err_msg=ctx)
+                        np.testing.assert_array_equal(mask.cpu().numpy(), rm.cpu().numpy(), err_msg=ctx)
+                        if k == min(L, 4) and se is not None:
+                            # the selection of those scores, by the oracle
+                            oi, _, oc = oselect.select_topk(score.cpu().numpy(), k, eligible=xe, largest=largest,
+                                                            use_thr=use_thr, thr=np.float32(thr))
+                            np.testing.assert_array_equal(cnt.cpu().numpy(), oc, err_msg=ctx)
+                            np.testing.assert_array_equal(idx.cpu().numpy(), oi, err_msg=ctx)
+    ref = oselect.seed_score(u.ravel(), d_in.ravel(), d_out.ravel(), seed_el.ravel())
+    got = dv.dv_seed_select(gu, gi, go, 1, seed_eligible=_t(seed_el, dev))[0].cpu().numpy().ravel().astype(np.float64)
+    fin = np.isfinite(ref)
+    np.testing.assert_array_equal(np.isfinite(got), fin)
+    np.testing.assert_allclose(got[fin], ref[fin], rtol=1e-6, atol=0)
 
 
 # ---------------------------------------------------------------- chains ----

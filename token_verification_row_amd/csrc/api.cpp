@@ -352,6 +352,38 @@ dv_status dv_select_topk(int64_t nseq, int64_t seq_len, const float *score, cons
   return hip_status(dv::launch_select_topk(p, stream), "dv_select_topk launch");
 }
 
+dv_status dv_seed_select(int64_t nseq, int64_t seq_len, const float *u, const float *d_in, const float *d_out,
+                         const uint8_t *seed_eligible, float *score, const uint8_t *select_eligible, int32_t k,
+                         int32_t largest, int32_t use_thr, float thr, int32_t *out_idx, float *out_val,
+                         int32_t *out_count, uint8_t *out_mask, hipStream_t stream) {
+  if (nseq < 0 || nseq > kMaxIndex) return fail(DV_ERR_SHAPE, "nseq out of range");
+  if (seq_len < 1) return fail(DV_ERR_SHAPE, "seq_len must be >= 1");
+  if (seq_len > dv::kMaxSelectLen)
+    return fail(DV_ERR_UNSUPPORTED, "seq_len %lld exceeds %lld", (long long)seq_len, (long long)dv::kMaxSelectLen);
+  if (nseq > kMaxIndex / seq_len) return fail(DV_ERR_SHAPE, "nseq * seq_len out of range");
+  if (k < 1 || k > seq_len) return fail(DV_ERR_ARG, "k must be in [1, seq_len]");
+  if (use_thr && !finite(thr)) return fail(DV_ERR_ARG, "thr must be finite");
+  if (nseq > 0 && (!u || !d_in || !d_out || !score)) return fail(DV_ERR_NULL, "u, d_in, d_out and score are required");
+  dv::SelectLaunch p{};
+  p.nseq = nseq;
+  p.seq_len = seq_len;
+  p.eligible = select_eligible;
+  p.k = k;
+  p.largest = largest != 0;
+  p.use_thr = use_thr != 0;
+  p.thr = thr;
+  p.out_idx = out_idx;
+  p.out_val = out_val;
+  p.out_count = out_count;
+  p.out_mask = out_mask;
+  p.u = u;
+  p.d_in = d_in;
+  p.d_out = d_out;
+  p.seed_eligible = seed_eligible;
+  p.score_out = score;
+  return hip_status(dv::launch_seed_select(p, stream), "dv_seed_select launch");
+}
+
 dv_status dv_influence_drift_workspace_bytes(const dv_attention *att, size_t *bytes) {
   if (!bytes) return fail(DV_ERR_NULL, "bytes is NULL");
   dv::InfluenceLaunch p{};

@@ -126,9 +126,15 @@ struct SelectLaunch {
   float *out_val;
   int32_t *out_count;
   uint8_t *out_mask;
+  // seed scores computed in the selection (u set): u (1 + d_in) / (1 + d_out) where
+  // seed_eligible (or everywhere), -inf elsewhere, written to score_out; score is then unused
+  const float *u, *d_in, *d_out;
+  const uint8_t *seed_eligible;
+  float *score_out;
 };
 constexpr int64_t kMaxSelectLen = 16384;
 hipError_t launch_select_topk(const SelectLaunch &p, hipStream_t stream);
+hipError_t launch_seed_select(const SelectLaunch &p, hipStream_t stream);
 
 constexpr int kMaxTreeNodes = 1024;
 constexpr int kMaxTreeBlockLen = 1024;

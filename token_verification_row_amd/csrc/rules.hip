@@ -217,12 +217,15 @@ __device__ __forceinline__ unsigned long long select_key(float s, uint32_t i, in
 // the keys, and the quarters' counts are added in LDS. The workgroups of a sequence write
 // disjoint outputs, so none waits for another. Scores are not NaN, so the kept entries (key
 // above the threshold's key) are a prefix of the order and their number is
-// min(k, number of kept entries). Same keys, same order as the sort.
+// min(k, number of kept entries). Same keys, same order as the sort. Given the seed score's
+// inputs (p.u set) instead of scores, it computes the scores with seed_score_kernel's
+// arithmetic, and each workgroup writes those of its own 64 positions.
 constexpr int32_t kRankMaxLen = 2048;
 constexpr int kRankThreads = 256;
 __global__ __launch_bounds__(kRankThreads) void select_rank_kernel(SelectLaunch p) {
   constexpr int kPer = kRankMaxLen / kRankThreads;  // keys built per thread, at most
   __shared__ unsigned long long keys[kRankMaxLen];
+  __shared__ float vals[kRankMaxLen];
   __shared__ int32_t part[4][64];
   __shared__ int32_t wave_kept[4];
   const int64_t seq = blockIdx.x;
@@ -235,8 +238,31 @@ __global__ __launch_bounds__(kRankThreads) void select_rank_kernel(SelectLaunch 
   // loads at clamped (always valid) positions, all issued before the first is used
   float v[kPer];
   uint32_t e[kPer];
+  if (p.u) {
+    // the seed scores, with seed_score_kernel's arithmetic
+    const int64_t base = seq * p.seq_len;
+    float uu[kPer], di[kPer], dd[kPer];
+    uint32_t se[kPer];
 #pragma unroll
-  for (int t = 0; t < kPer; ++t) v[t] = sc[min(t * kRankThreads + tid, L - 1)];
+    for (int t = 0; t < kPer; ++t) {
+      const int64_t j = base + min(t * kRankThreads + tid, L - 1);
+      uu[t] = p.u[j];
+      di[t] = p.d_in[j];
+      dd[t] = p.d_out[j];
+      se[t] = p.seed_eligible ? p.seed_eligible[j] : 1u;
+    }
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) {
+      float s = -INFINITY;
+      if (se[t] != 0) s = uu[t] * (1.0f + di[t]) / (1.0f + dd[t]);
+      v[t] = s;
+      const int32_t j = t * kRankThreads + tid;
+      if (p.score_out && j < L && (j >> 6) == static_cast<int32_t>(blockIdx.y)) p.score_out[base + j] = s;
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) v[t] = sc[min(t * kRankThreads + tid, L - 1)];
+  }
   if (el) {
 #pragma unroll
     for (int t = 0; t < kPer; ++t) e[t] = el[min(t * kRankThreads + tid, L - 1)];
@@ -250,7 +276,10 @@ __global__ __launch_bounds__(kRankThreads) void select_rank_kernel(SelectLaunch 
     const int32_t j = t * kRankThreads + tid;
     const bool ok = j < L && e[t] != 0;
     const unsigned long long k = ok ? select_key(v[t], static_cast<uint32_t>(j), p.largest) : 0ull;
-    if (j < L) keys[j] = k;
+    if (j < L) {
+      keys[j] = k;
+      vals[j] = v[t];
+    }
     const bool keep = k != 0 && (!p.use_thr || static_cast<uint32_t>(k >> 32) > thr_ord);
     kept += __popcll(__ballot(keep));
   }
@@ -270,7 +299,7 @@ __global__ __launch_bounds__(kRankThreads) void select_rank_kernel(SelectLaunch 
   const bool sel = ki != 0 && rank < count;
   if (sel) {
     if (p.out_idx) p.out_idx[seq * p.k + rank] = i;
-    if (p.out_val) p.out_val[seq * p.k + rank] = sc[i];
+    if (p.out_val) p.out_val[seq * p.k + rank] = vals[i];
   }
   if (p.out_mask && i < L) p.out_mask[seq * p.seq_len + i] = sel ? 1 : 0;
   if (blockIdx.y == 0) {
@@ -371,6 +400,24 @@ hipError_t launch_seed_score(int64_t rows, const float *u, const float *d_in, co
   const unsigned blocks = static_cast<unsigned>((rows + 255) / 256);
   hipLaunchKernelGGL(seed_score_kernel, dim3(blocks), dim3(256), 0, stream, rows, u, d_in, d_out, eligible, score);
   return hipGetLastError();
+}
+
+hipError_t launch_seed_select(const SelectLaunch &p, hipStream_t stream) {
+  if (p.nseq == 0) return hipSuccess;
+  if (p.seq_len <= kRankMaxLen) {
+    const dim3 grid(static_cast<unsigned>(p.nseq), static_cast<unsigned>((p.seq_len + 63) / 64));
+    hipLaunchKernelGGL(select_rank_kernel, grid, dim3(kRankThreads), 0, stream, p);
+    return hipGetLastError();
+  }
+  // longer sequences: the scores, then the sort
+  hipError_t e = launch_seed_score(p.nseq * p.seq_len, p.u, p.d_in, p.d_out, p.seed_eligible, p.score_out, stream);
+  if (e != hipSuccess) return e;
+  SelectLaunch q = p;
+  q.score = p.score_out;
+  q.u = q.d_in = q.d_out = nullptr;
+  q.seed_eligible = nullptr;
+  q.score_out = nullptr;
+  return launch_select_topk(q, stream);
 }
 
 hipError_t launch_select_topk(const SelectLaunch &p, hipStream_t stream) {

@@ -94,6 +94,8 @@ _SIGNATURES = {
     "dv_seed_score": (ctypes.c_int, [ctypes.c_int64, _P, _P, _P, _P, _P, _P]),
     "dv_select_topk": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_int32, ctypes.c_float, _P, _P, _P, _P, _P]),
+    "dv_seed_select": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
+                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P, _P, _P, _P, _P]),
     "dv_tree_accept": (ctypes.c_int, [ctypes.POINTER(dv_tree_args)] + [_P] * 15),
     "dv_dual_view_attention": (ctypes.c_int, [ctypes.POINTER(dv_dual_view_args)] + [_P] * 8),
     "dv_influence_drift_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(dv_attention), ctypes.POINTER(ctypes.c_size_t)]),
@@ -360,6 +362,15 @@ def prepare_select_topk(score, k, idx, val, cnt, *, eligible=None, mask=None, la
                     _ptr(idx), _ptr(val), _ptr(cnt), _ptr(mask), _stream_handle(score.device))
 
 
+def prepare_seed_select(u, d_in, d_out, seed_eligible, score, k, idx, val, cnt, *, select_eligible=None, mask=None,
+                        largest=True) -> Prepared:
+    """dv_seed_select on fixed buffers: u, d_in, d_out, score [nseq, L] (no threshold)."""
+    nseq, L = u.shape
+    return Prepared("dv_seed_select", nseq, L, _ptr(u), _ptr(d_in), _ptr(d_out), _ptr(seed_eligible), _ptr(score),
+                    _ptr(select_eligible), int(k), int(bool(largest)), 0, 0.0, _ptr(idx), _ptr(val), _ptr(cnt),
+                    _ptr(mask), _stream_handle(u.device))
+
+
 def prepare_decide(rule, stats, decision, out_tok, *, rows, tau_kl=0.0, conf_thr=0.0, mask_token=-1, subject=None,
                    group_len=0, prefix=None, best=None) -> Prepared:
     """dv_decide on fixed buffers; ``stats`` maps dv_row_stats members to device tensors."""
@@ -446,6 +457,38 @@ def dv_select_topk(score, k, *, eligible=None, largest=True, use_thr=False, thr=
                                          int(bool(use_thr)), float(thr), _ptr(idx), _ptr(val), _ptr(cnt),
                                          _ptr(mask), _stream_handle(dev)), "dv_select_topk")
     return idx, val, cnt[:nseq], mask
+
+
+def dv_seed_select(u, d_in, d_out, k, *, seed_eligible=None, select_eligible=None, largest=True, use_thr=False, thr=0.0,
+                   want_mask=False):
+    """COVER seed scores of u, d_in, d_out [nseq, L] and their per-sequence top-k in one call: the same outputs
+    as dv_seed_score followed by dv_select_topk. Returns (score [nseq, L], idx, val, count, mask or None)."""
+    for name, v in (("u", u), ("d_in", d_in), ("d_out", d_out)):
+        _need_cuda(v, name)
+        if v.dtype != torch.float32 or not v.is_contiguous():
+            raise TypeError(f"{name} must be contiguous float32")
+    if u.dim() != 2:
+        raise ValueError("u must be [nseq, L]")
+    nseq, L = u.shape
+    if d_in.numel() != u.numel() or d_out.numel() != u.numel():
+        raise ValueError("u, d_in and d_out must have the same number of elements")
+    for name, e in (("seed_eligible", seed_eligible), ("select_eligible", select_eligible)):
+        if e is not None:
+            _need_cuda(e, name)
+            if e.dtype != torch.uint8 or e.numel() != u.numel() or not e.is_contiguous():
+                raise TypeError(f"{name} must be contiguous uint8 with one entry per position")
+    dev = u.device
+    kk = max(int(k), 1)
+    score = torch.empty((nseq, L), dtype=torch.float32, device=dev)
+    idx = torch.empty((nseq, kk), dtype=torch.int32, device=dev)
+    val = torch.empty((nseq, kk), dtype=torch.float32, device=dev)
+    cnt = torch.empty(max(nseq, 1), dtype=torch.int32, device=dev)
+    mask = torch.empty((nseq, L), dtype=torch.uint8, device=dev) if want_mask else None
+    _check(load_library().dv_seed_select(nseq, L, _ptr(u), _ptr(d_in), _ptr(d_out), _ptr(seed_eligible), _ptr(score),
+                                         _ptr(select_eligible), int(k), int(bool(largest)), int(bool(use_thr)),
+                                         float(thr), _ptr(idx), _ptr(val), _ptr(cnt), _ptr(mask), _stream_handle(dev)),
+           "dv_seed_select")
+    return score, idx, val, cnt[:nseq], mask
 
 
 def dv_tree_accept(parent, node_pos, node_tok, root_masked, conf, tok_v, *, block_tokens=None, update_mask=False):

@@ -31,6 +31,17 @@ namespace {
 constexpr int kTreeThreads = 1024;
 constexpr int kTreeWaves = kTreeThreads / 64;
 constexpr int kPosPerLane = kMaxTreeBlockLen / 64;
+constexpr int kPre = 4;  // (node, position) entries per thread read ahead in small trees
+
+// A small tree's confidences, tokens and root mask flags, read by each thread at the start for the
+// entries tid + kTreeThreads k it handles later, so that every global read of the kernel is in
+// flight at once (one round trip to memory instead of one per phase).
+struct Prefetch {
+  bool on;
+  float conf[kPre];
+  int32_t tok[kPre];
+  uint32_t masked[kPre];
+};
 
 struct TreeLds {
   int32_t parent[kMaxTreeNodes];
@@ -66,7 +77,7 @@ __device__ __forceinline__ uint32_t float_order(float x) {
 // atomic max on (confidence, lowest position), and the winner records its
 // token. Every load of confidence and token is independent of the others.
 __device__ void transitions_small(TreeLds &s, const TreeLaunch &p, int64_t nb, const uint8_t *root_masked,
-                                  int32_t n, int32_t L) {
+                                  int32_t n, int32_t L, const Prefetch &pf) {
   const int tid = threadIdx.x;
   for (int32_t i = tid; i < n; i += kTreeThreads) {
     unsigned long long m = 0;
@@ -87,20 +98,46 @@ __device__ void transitions_small(TreeLds &s, const TreeLaunch &p, int64_t nb, c
   }
   __syncthreads();
   const int64_t total = static_cast<int64_t>(n) * L;
-  for (int64_t e = tid; e < total; e += kTreeThreads) {
+  auto offer = [&](int64_t e, bool masked, float c) {
     const int32_t i = static_cast<int32_t>(e / L), q = static_cast<int32_t>(e - static_cast<int64_t>(i) * L);
-    if (!root_masked[q] || ((s.pmask[i] >> q) & 1ull)) continue;
-    const float c = p.conf[nb * L + e];
+    if (!masked || ((s.pmask[i] >> q) & 1ull)) return;
     const unsigned long long key = (static_cast<unsigned long long>(float_order(c)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(q));
     atomicMax(&s.tkey[i], key);
-  }
-  __syncthreads();
-  for (int64_t e = tid; e < total; e += kTreeThreads) {
+  };
+  auto claim = [&](int64_t e, int32_t tok) {
     const int32_t i = static_cast<int32_t>(e / L), q = static_cast<int32_t>(e - static_cast<int64_t>(i) * L);
     const unsigned long long k = s.tkey[i];
     if (k != 0 && static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(k & 0xFFFFFFFFull)) == q) {
       s.tpos[i] = static_cast<int16_t>(q);
-      s.ttok[i] = p.tok_v[nb * L + e];
+      s.ttok[i] = tok;
+    }
+  };
+  if (pf.on) {
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) {
+      const int64_t e = tid + static_cast<int64_t>(k) * kTreeThreads;
+      if (e < total) offer(e, pf.masked[k] != 0, pf.conf[k]);
+    }
+  } else {
+    for (int64_t e = tid; e < total; e += kTreeThreads) {
+      const int32_t q = static_cast<int32_t>(e % L);
+      if (root_masked[q]) offer(e, true, p.conf[nb * L + e]);
+    }
+  }
+  __syncthreads();
+  if (pf.on) {
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) {
+      const int64_t e = tid + static_cast<int64_t>(k) * kTreeThreads;
+      if (e < total) claim(e, pf.tok[k]);
+    }
+  } else {
+    for (int64_t e = tid; e < total; e += kTreeThreads) {
+      const int32_t i = static_cast<int32_t>(e / L);
+      const unsigned long long k = s.tkey[i];
+      // only the winner reads its token
+      if (k != 0 && static_cast<int64_t>(0xFFFFFFFFu - static_cast<uint32_t>(k & 0xFFFFFFFFull)) == e - static_cast<int64_t>(i) * L)
+        claim(e, p.tok_v[nb * L + e]);
     }
   }
 }
@@ -171,6 +208,21 @@ __global__ __launch_bounds__(kTreeThreads) void tree_accept_kernel(TreeLaunch p)
   const int32_t n = static_cast<int32_t>(p.nodes), L = static_cast<int32_t>(p.block_len);
   const int64_t nb = t * p.nodes;  // node base of this tree
   const uint8_t *root_masked = p.root_masked + t * p.block_len;
+  const int64_t total = static_cast<int64_t>(n) * L;
+  Prefetch pf;
+  pf.on = L <= 64 && total <= static_cast<int64_t>(kPre) * kTreeThreads;
+  if (pf.on) {
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) {
+      // entries past the tree read its last entry (always inside the arrays) and are not used
+      const int64_t e = min(tid + static_cast<int64_t>(k) * kTreeThreads, total - 1);
+      pf.conf[k] = p.conf[nb * L + e];
+      pf.tok[k] = p.tok_v[nb * L + e];
+      pf.masked[k] = root_masked[e % L];
+    }
+  }
+  // the root mask flag of position tid, for the updated mask at the end (block_len <= kTreeThreads)
+  const uint32_t own_masked = tid < L ? root_masked[tid] : 0u;
   for (int32_t i = tid; i < n; i += kTreeThreads) {
     s.parent[i] = i == 0 ? -1 : p.parent[nb + i];
     s.pos[i] = p.node_pos[nb + i];
@@ -182,7 +234,7 @@ __global__ __launch_bounds__(kTreeThreads) void tree_accept_kernel(TreeLaunch p)
 
   // 2. the target's transition from every node's state that could be accepted
   if (L <= 64) {
-    transitions_small(s, p, nb, root_masked, n, L);
+    transitions_small(s, p, nb, root_masked, n, L, pf);
   } else {
     transitions_wide(s, p, nb, root_masked, n, L);
   }
@@ -253,18 +305,16 @@ __global__ __launch_bounds__(kTreeThreads) void tree_accept_kernel(TreeLaunch p)
     if (p.commit_tok) p.commit_tok[t * p.block_len + m] = m < nc ? s.commit_tok[m] : -1;
   }
   // apply the commits (committed positions are distinct); out_masked may alias
-  // root_masked: every read of it happened before the barriers above, or is
-  // the read of the same element by the thread that writes it
+  // root_masked: every read of it happened before the barriers above
   for (int32_t m = tid; m < nc; m += kTreeThreads) {
     const int32_t q = s.commit_pos[m];
     if (p.block_tokens) p.block_tokens[t * p.block_len + q] = s.commit_tok[m];
   }
-  if (p.out_masked) {
-    for (int32_t q = tid; q < L; q += kTreeThreads) {
-      bool m = root_masked[q] != 0;
-      for (int32_t c = 0; c < nc && m; ++c) m = s.commit_pos[c] != q;
-      p.out_masked[t * p.block_len + q] = m ? 1 : 0;
-    }
+  if (p.out_masked && tid < L) {
+    const int32_t q = tid;
+    bool m = own_masked != 0;
+    for (int32_t c = 0; c < nc && m; ++c) m = s.commit_pos[c] != q;
+    p.out_masked[t * p.block_len + q] = m ? 1 : 0;
   }
 }
 

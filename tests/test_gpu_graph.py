@@ -1,5 +1,5 @@
 """The whole path under HIP graph capture: dv_verify_rows (with its noise table),
-dv_decide, dv_seed_score and dv_select_topk allocate nothing and clear nothing
+dv_decide, dv_seed_score, dv_select_topk and dv_seed_select allocate nothing and clear nothing
 with memset, so a captured step replays to the eager results, replay after
 replay, with other work and synchronisations in between."""
 
@@ -20,7 +20,10 @@ def _step(a, b, w, out, ws, d_in, d_out, bufs):
                                    want_best=True)
     score = dv.dv_seed_score(got["entropy"], d_in, d_out)
     idx, val, cnt, _ = dv.dv_select_topk(score.view(-1, w.group_len), 8)
-    for k, v in (("d", d), ("o", o), ("pre", pre), ("best", best), ("idx", idx), ("val", val), ("cnt", cnt)):
+    # the same seed score and selection in one launch
+    score2, idx2, val2, cnt2, _ = dv.dv_seed_select(got["entropy"].view(-1, w.group_len), d_in, d_out, 8)
+    for k, v in (("d", d), ("o", o), ("pre", pre), ("best", best), ("idx", idx), ("val", val), ("cnt", cnt),
+                 ("score2", score2), ("idx2", idx2), ("val2", val2), ("cnt2", cnt2)):
         bufs[k] = v
     return bufs
 

@@ -104,7 +104,8 @@ def test_hand_example():
 
 
 @pytest.mark.parametrize("n,L,vocab,p_follow", [(1, 1, 1, 0.0), (1, 7, 3, 0.0), (5, 3, 2, 0.9), (64, 32, 4, 0.8),
-                                                (200, 16, 2, 0.6), (300, 100, 3, 0.95), (1024, 64, 2, 0.9), (1024, 65, 2, 0.9)])
+                                                (200, 16, 2, 0.6), (300, 100, 3, 0.95), (1024, 64, 2, 0.9), (1024, 65, 2, 0.9),
+                                                (64, 64, 2, 0.9), (65, 64, 2, 0.9), (1024, 4, 2, 0.9), (205, 20, 2, 0.9)])
 def test_random_trees(n, L, vocab, p_follow):
     print(f"case: random trees n={n} L={L}", flush=True)
     rng = np.random.default_rng(n * 131 + L)

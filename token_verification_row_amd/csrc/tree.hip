@@ -7,17 +7,18 @@
 // One workgroup per tree:
 //   1. the node arrays go to LDS;
 //   2. the target's transition from each node's state: the masked positions
-//      are the root's minus those committed on the path (a walk over LDS), the
+//      are the root's minus those committed on the path (pointer jumping in LDS), the
 //      transition is the masked position with the highest confidence, lowest
 //      position on ties, with the verifier's token (one thread per (node,
 //      position) for blocks of up to 64 positions, else one wave per node);
 //   3. one thread per node accepts it when every node on its path matches its
-//      parent's transition, and counts its depth;
+//      parent's transition, and counts its depth (pointer jumping);
 //   4. the deepest accepted node (lowest index on ties), its path and the
 //      target's transition there form the commit list, which can be applied
 //      to the block's tokens and mask.
 // An accepted path commits distinct masked positions, so a node deeper than
-// block_len cannot be accepted: every walk stops after block_len + 1 steps.
+// block_len cannot be accepted: a path of more than block_len edges gets no
+// transition and its node is not accepted.
 // Device data that breaks the layout (a parent not below its node, a position
 // outside the block) makes that node unacceptable, never an access outside
 // the arrays.
@@ -30,6 +31,7 @@ namespace {
 
 constexpr int kTreeThreads = 1024;
 constexpr int kTreeWaves = kTreeThreads / 64;
+static_assert(kMaxTreeNodes <= kTreeThreads, "one node per thread in the pointer jumping");
 constexpr int kPosPerLane = kMaxTreeBlockLen / 64;
 constexpr int kPre = 4;  // (node, position) entries per thread read ahead in small trees
 
@@ -49,7 +51,8 @@ struct TreeLds {
   int32_t tok[kMaxTreeNodes];
   int32_t ttok[kMaxTreeNodes];         // transition token of each node's state
   int16_t tpos[kMaxTreeNodes];         // transition position (-1: none, or not needed)
-  int16_t depth[kMaxTreeNodes];        // accepted depth, -1 when not accepted
+  int16_t depth[kMaxTreeNodes];        // accepted depth, -1 when not accepted (edges so far while jumping)
+  int16_t anc[kMaxTreeNodes];          // pointer jumping: the ancestor a node's summary reaches (-1: the root)
   unsigned long long pmask[kMaxTreeNodes];  // blocks of <= 64 positions: positions committed on the path
   unsigned long long tkey[kMaxTreeNodes];   // blocks of <= 64 positions: best (confidence, position) key
   int32_t commit_pos[kMaxTreeBlockLen + 1];
@@ -64,37 +67,76 @@ __device__ __forceinline__ int32_t parent_of(const TreeLds &s, int32_t i) {
   return (q >= 0 && q < i) ? q : -1;
 }
 
+// Pointer jumping to the root, one node per thread: a node's summary is (anc, bits, steps): the
+// ancestor it reaches, the OR of the positions committed on the way (path masks only) and the number
+// of edges, -1 once a link on the way is broken. Each round adds the ancestor's summary to the node's
+// and jumps to the ancestor's ancestor, so after ceil(log2 n) rounds every summary reaches the root:
+// log2 n dependent LDS reads instead of one per level. The caller has published every node's first
+// summary (s.depth, s.anc, and s.pmask with bits) and synchronised.
+template <bool BITS>
+__device__ __forceinline__ void jump_to_root(TreeLds &s, int32_t n, int32_t &anc, int32_t &steps,
+                                             unsigned long long &bits) {
+  const int tid = threadIdx.x;
+  for (int32_t span = 1; span < n; span <<= 1) {
+    const bool act = tid < n && anc >= 0;
+    unsigned long long b2 = 0;
+    int32_t s2 = 0, a2 = -1;
+    if (act) {
+      if (BITS) b2 = s.pmask[anc];
+      s2 = s.depth[anc];
+      a2 = s.anc[anc];
+    }
+    __syncthreads();
+    if (act) {
+      bits |= b2;
+      steps = (steps < 0 || s2 < 0) ? -1 : steps + s2;
+      anc = steps < 0 ? -1 : a2;
+      if (BITS) s.pmask[tid] = bits;
+      s.depth[tid] = static_cast<int16_t>(steps);
+      s.anc[tid] = static_cast<int16_t>(anc);
+    }
+    __syncthreads();
+  }
+}
+
 // Order-preserving unsigned image of a float (larger float, larger image).
 __device__ __forceinline__ uint32_t float_order(float x) {
   const uint32_t b = __float_as_uint(x);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Blocks of up to 64 positions. Each thread walks one node's path (at most
-// block_len steps: a longer path cannot be accepted and gets no transition)
-// into a 64-bit mask of committed positions; then one thread per (node,
-// position) offers its masked position to the node's transition with an LDS
-// atomic max on (confidence, lowest position), and the winner records its
-// token. Every load of confidence and token is independent of the others.
+// Blocks of up to 64 positions. Each node's path (at most block_len edges: a
+// longer path cannot be accepted and gets no transition) gives a 64-bit mask of
+// committed positions, by pointer jumping; then one thread per (node, position)
+// offers its masked position to the node's transition with an LDS atomic max on
+// (confidence, lowest position), and the winner records its token. Every load of
+// confidence and token is independent of the others.
 __device__ void transitions_small(TreeLds &s, const TreeLaunch &p, int64_t nb, const uint8_t *root_masked,
                                   int32_t n, int32_t L, const Prefetch &pf) {
-  const int tid = threadIdx.x;
-  for (int32_t i = tid; i < n; i += kTreeThreads) {
-    unsigned long long m = 0;
-    int32_t j = i, steps = 0;
-    bool ok = true;
-    while (j > 0) {
-      const int32_t q = s.pos[j];
-      const int32_t up = parent_of(s, j);
-      if (++steps > L || up < 0) {
-        ok = false;
-        break;
+  const int tid = threadIdx.x;  // node tid (n <= kTreeThreads)
+  int32_t anc = -1, steps = 0;
+  unsigned long long bits = 0;
+  if (tid < n) {
+    if (tid > 0) {
+      const int32_t up = parent_of(s, tid);
+      if (up < 0) {
+        steps = -1;
+      } else {
+        anc = up;
+        steps = 1;
+        const int32_t q = s.pos[tid];
+        if (q >= 0 && q < L) bits = 1ull << q;
       }
-      if (q >= 0 && q < L) m |= 1ull << q;
-      j = up;
     }
-    s.pmask[i] = ok ? m : ~0ull;  // all positions taken: no transition
-    s.tkey[i] = 0;
+    s.pmask[tid] = bits;
+    s.depth[tid] = static_cast<int16_t>(steps);
+    s.anc[tid] = static_cast<int16_t>(anc);
+  }
+  __syncthreads();
+  jump_to_root<true>(s, n, anc, steps, bits);
+  if (tid < n) {
+    s.pmask[tid] = (steps >= 0 && steps <= L) ? bits : ~0ull;  // all positions taken: no transition
+    s.tkey[tid] = 0;
   }
   __syncthreads();
   const int64_t total = static_cast<int64_t>(n) * L;
@@ -240,21 +282,24 @@ __global__ __launch_bounds__(kTreeThreads) void tree_accept_kernel(TreeLaunch p)
   }
   __syncthreads();
 
-  // 3. acceptance and depth, one thread per node: walk to the root while every
-  // node on the way matches its parent's transition
-  for (int32_t i = tid; i < n; i += kTreeThreads) {
-    int32_t j = i, d = 0;
-    bool ok = true;
-    while (j > 0) {
-      const int32_t up = parent_of(s, j);
-      if (up < 0 || d >= L || s.tpos[up] < 0 || s.pos[j] != s.tpos[up] || s.tok[j] != s.ttok[up]) {
-        ok = false;
-        break;
+  // 3. acceptance and depth, one thread per node: a node is accepted when every node on its path
+  // matches its parent's transition and the path has at most block_len edges (pointer jumping)
+  {
+    int32_t anc = -1, steps = 0;
+    unsigned long long none = 0;
+    if (tid < n) {
+      if (tid > 0) {
+        const int32_t up = parent_of(s, tid);
+        const bool ok = up >= 0 && s.tpos[up] >= 0 && s.pos[tid] == s.tpos[up] && s.tok[tid] == s.ttok[up];
+        anc = ok ? up : -1;
+        steps = ok ? 1 : -1;
       }
-      ++d;
-      j = up;
+      s.depth[tid] = static_cast<int16_t>(steps);
+      s.anc[tid] = static_cast<int16_t>(anc);
     }
-    s.depth[i] = static_cast<int16_t>(ok ? d : -1);
+    __syncthreads();
+    jump_to_root<false>(s, n, anc, steps, none);
+    if (tid < n) s.depth[tid] = static_cast<int16_t>(steps >= 0 && steps <= L ? steps : -1);
   }
   __syncthreads();
 

@@ -1,9 +1,12 @@
 """Throughput of the verification hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic logits:
-dv_verify_rows (the fused verify pass), dv_decide, and the seed score with its
-per-sequence selection (dv_seed_select; at workload 5, which ranks by KL,
-dv_seed_score and dv_select_topk). The default workload is the SPOT-style tree of 64 candidate
+dv_verify_rows (the fused verify pass), the decisions, and the seed score with
+its per-sequence selection. The decisions and the seed selection are independent
+and go in one call, dv_decide_seed_select (one launch); at workload 3 the
+decisions re-verify the selected seeds, so dv_seed_select runs first and
+dv_decide after it; workload 5 ranks by KL (dv_decide, dv_seed_score,
+dv_select_topk). The default workload is the SPOT-style tree of 64 candidate
 block states x 32 positions over a 151 936-token vocabulary, bf16, T = 1,
 noise shared per position (coupled-noise acceptance per candidate).
 
@@ -391,20 +394,21 @@ def main() -> int:
                          dv.prepare_decide("COVER", got, bf["decision"], bf["out_tok"], rows=R,
                                            conf_thr=w.conf_thr, subject=bf["mask"].view(-1))]
             else:
-                if w.number == 5:
-                    calls = [dv.prepare_seed_score(got["entropy"], d_in, d_out, committed, bf["score"])]
-                else:
-                    calls = [dv.prepare_seed_select(u2, d_in, d_out, committed, bf["score"], k, bf["idx"], bf["val"],
-                                                    bf["cnt"])]
                 if w.group_len:
-                    calls.append(dv.prepare_decide("COUPLED_ACCEPT", got, bf["decision"], bf["out_tok"], rows=R,
-                                                   group_len=w.group_len, prefix=bf["prefix"], best=bf["best"]))
+                    dec = dv.prepare_decide("COUPLED_ACCEPT", got, bf["decision"], bf["out_tok"], rows=R,
+                                            group_len=w.group_len, prefix=bf["prefix"], best=bf["best"])
                 else:
-                    calls.append(dv.prepare_decide("KL_OR_CONF", got, bf["decision"], bf["out_tok"], rows=R,
-                                                   tau_kl=w.tau_kl or 0.05, conf_thr=w.conf_thr or 0.9))
+                    dec = dv.prepare_decide("KL_OR_CONF", got, bf["decision"], bf["out_tok"], rows=R,
+                                            tau_kl=w.tau_kl or 0.05, conf_thr=w.conf_thr or 0.9)
                 if w.number == 5:
-                    calls.append(dv.prepare_select_topk(got["kl"].view(nseq, seq_len), k, bf["idx"], bf["val"],
-                                                        bf["cnt"]))
+                    calls = [dv.prepare_seed_score(got["entropy"], d_in, d_out, committed, bf["score"]), dec,
+                             dv.prepare_select_topk(got["kl"].view(nseq, seq_len), k, bf["idx"], bf["val"],
+                                                    bf["cnt"])]
+                else:
+                    # the decisions and the seed selection are independent: one call, one launch
+                    calls = [dv.prepare_decide_seed_select(
+                        dec, dv.prepare_seed_select(u2, d_in, d_out, committed, bf["score"], k, bf["idx"], bf["val"],
+                                                    bf["cnt"]))]
             for ci in range(copies):
                 prepared[(ci, oi)] = (plans[oi].prepared(*inputs[ci]), calls)
 
@@ -439,17 +443,22 @@ def main() -> int:
             return
         if tree is not None:
             dv.dv_tree_accept(*tree, got["conf"], got["tok_v"])
+            dec = None
         elif w.group_len:
-            dv.dv_decide("COUPLED_ACCEPT", got, mask_token=-1, group_len=w.group_len, want_prefix=True,
-                         want_best=True)
+            dec = dict(rule="COUPLED_ACCEPT", stats=got, mask_token=-1, group_len=w.group_len, want_prefix=True,
+                       want_best=True)
         else:
-            dv.dv_decide("KL_OR_CONF", got, tau_kl=w.tau_kl or 0.05, conf_thr=w.conf_thr or 0.9, mask_token=-1)
-        # workload 5 ranks positions by KL; the others by the seed score
+            dec = dict(rule="KL_OR_CONF", stats=got, tau_kl=w.tau_kl or 0.05, conf_thr=w.conf_thr or 0.9,
+                       mask_token=-1)
+        # workload 5 ranks positions by KL; the others by the seed score, in one call with the decisions
         if w.number == 5:
+            dv.dv_decide(**dec)
             dv.dv_seed_score(got["entropy"], di, do, committed)
             dv.dv_select_topk(got["kl"].view(nseq, seq_len), k)
-        else:
+        elif dec is None:
             dv.dv_seed_select(u2, di, do, k, seed_eligible=committed)
+        else:
+            dv.dv_decide_seed_select(dec, dict(u=u2, d_in=di, d_out=do, k=k, seed_eligible=committed))
 
     n_warm = warm(step)
     every = max(1, args.sample_every) if args.steps >= 5 * max(1, args.sample_every) else 1
@@ -482,6 +491,9 @@ def main() -> int:
         torch.cuda.empty_cache()
         cpu = cpu_baselines(w, a_rows, b_rows, pos, dev, workers, host_cores)
 
+    step_calls = ("dv_decide + dv_seed_score + dv_select_topk" if w.number == 5 else
+                  "dv_seed_select + dv_decide" if w.n_committed else
+                  "dv_tree_accept + dv_seed_select" if tree is not None else "dv_decide_seed_select")
     line = {
         "metric": "verified rows/s and achieved HBM GB/s (% of peak), fused verify kernel",
         "value": R / (ms_per_step * 1e-3),
@@ -501,9 +513,7 @@ def main() -> int:
                                + (f", noise shared per position (period {period}), coupled acceptance per "
                                   f"{w.group_len}-row candidate" if period else ""),
                    "rows": R, "vocab": V, "input_copies": copies,
-                   "step": "dv_verify_rows + "
-                           + ("dv_seed_score + dv_select_topk + " if w.number == 5 else "dv_seed_select + ")
-                           + ("dv_tree_accept" if tree is not None else "dv_decide")},
+                   "step": "dv_verify_rows + " + step_calls},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": None if args.extended else measured_traffic(w.number),
                      "kernel": "dv_verify_rows (noise table when rows share positions + streaming verify kernel)",
@@ -533,7 +543,7 @@ def main() -> int:
         line["influence"] = {"maps": args.influence, "len": w.L, **att_us, "avg_us": att_us["mean_us"],
                              "bytes_per_launch": att_bytes,
                              "achieved_GBps": att_bytes / (att_us["median_us"] * 1e-6) / 1e9}
-        line["config"]["step"] = "dv_verify_rows + dv_influence_drift + dv_seed_select + dv_decide"
+        line["config"]["step"] = "dv_verify_rows + dv_influence_drift + " + step_calls
     print(json.dumps(line), flush=True)
     return 0
 

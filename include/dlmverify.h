@@ -288,6 +288,29 @@ dv_status dv_seed_select(int64_t nseq, int64_t seq_len, const float *u, const fl
                          int32_t k, int32_t largest, int32_t use_thr, float thr, int32_t *out_idx,
                          float *out_val, int32_t *out_count, uint8_t *out_mask, hipStream_t stream);
 
+/* dv_decide and dv_seed_select of one decoding step in one launch ([COVER] §2
+ * and §3: the seeds are chosen by the Score equation while the positions are
+ * decided; [SPOT] §3: the coupled check and the threshold selection of one
+ * step). Arguments: dv_decide's (a .. best_group), then dv_seed_select's
+ * (nseq .. out_mask), then the stream; each means what it means there, and the
+ * outputs are those of dv_decide followed by dv_seed_select. The two calls run
+ * together, so they may share no memory that either writes: a decision output
+ * overlapping a seed-selection input or output, or a seed-selection output
+ * overlapping a decision input, is DV_ERR_ARG (so a selection's out_mask cannot
+ * be the subject of the decisions in the same call). One launch when the
+ * selection takes at most 2048 positions per sequence (nseq >= 1) and the
+ * decision is the one-workgroup path (group_len > 0, rows <= 16384, at most 1024
+ * groups) or needs no best_group; otherwise the calls' own launches, in order.
+ * Errors: those of dv_decide, then those of dv_seed_select, then DV_ERR_ARG
+ * for shared memory; nothing is launched when any check fails. */
+dv_status dv_decide_seed_select(const dv_decide_args *a, const dv_row_stats *stats, const uint8_t *subject,
+                                const int32_t *cur_tok, uint8_t *decision, int32_t *out_tok, int32_t *prefix_len,
+                                int32_t *best_group, int64_t nseq, int64_t seq_len, const float *u, const float *d_in,
+                                const float *d_out, const uint8_t *seed_eligible, float *score,
+                                const uint8_t *select_eligible, int32_t k, int32_t largest, int32_t use_thr, float thr,
+                                int32_t *out_idx, float *out_val, int32_t *out_count, uint8_t *out_mask,
+                                hipStream_t stream);
+
 /* Shape of dv_tree_accept's input: ntrees independent trees of `nodes` nodes
  * each over blocks of `block_len` positions. */
 typedef struct dv_tree_args {

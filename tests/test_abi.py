@@ -30,7 +30,7 @@ def _declared_functions():
 def test_exports_every_declared_function(lib):
     names = _declared_functions()
     assert names == sorted(["dv_verify_workspace_bytes", "dv_verify_rows", "dv_verify_rows_noalloc", "dv_decide", "dv_seed_score",
-                           "dv_select_topk", "dv_seed_select", "dv_tree_accept", "dv_influence_drift_workspace_bytes",
+                           "dv_select_topk", "dv_seed_select", "dv_decide_seed_select", "dv_tree_accept", "dv_influence_drift_workspace_bytes",
                            "dv_influence_drift", "dv_dual_view_attention", "dv_debug_hash", "dv_debug_noise", "dv_debug_read_probe", "dv_status_str",
                            "dv_last_error", "dv_version"])
     for n in names:
@@ -184,6 +184,39 @@ def test_seed_score_select_hash_validation(lib):
     assert lib.dv_debug_hash(0, None, -1, 1, 4, FAKE, None) == B.DV_ERR_SHAPE
     assert lib.dv_debug_hash(0, None, 0, 2, 4, None, None) == B.DV_ERR_NULL
     assert lib.dv_debug_hash(0, None, 0, 0, 4, None, None) == B.DV_OK
+
+
+def test_decide_seed_select_validation(lib):
+    """dv_decide_seed_select checks both calls' arguments, then that the two share no memory that either
+    writes, before anything is launched (distinct fake device addresses, never dereferenced)."""
+    f = lib.dv_decide_seed_select
+    buf = lambda i: (1 << 32) + i * (1 << 24)  # disjoint 16 MiB ranges
+    st = B.dv_row_stats(kl=buf(0), conf=buf(1), tok_v=buf(2), tok_d=buf(3))
+
+    def call(rule=B.DV_RULE_KL, rows=64, group_len=0, subject=None, decision=buf(4), out_tok=buf(5), prefix=None,
+             best=None, nseq=1, L=64, u=buf(6), d_in=buf(7), d_out=buf(8), score=buf(9), k=4, thr=0.0, use_thr=0,
+             idx=buf(10), val=buf(11), cnt=buf(12), mask=buf(13)):
+        a = B.dv_decide_args(rule=rule, tau_kl=0.1, conf_thr=0.9, mask_token=-1, rows=rows, group_len=group_len)
+        return f(ctypes.byref(a), ctypes.byref(st), subject, None, decision, out_tok, prefix, best, nseq, L, u, d_in,
+                 d_out, None, score, None, k, 1, use_thr, thr, idx, val, cnt, mask, None)
+
+    # each call's own checks, the decision's first
+    assert call(rule=99) == B.DV_ERR_ARG
+    assert call(rows=64, group_len=7, best=buf(14), prefix=buf(15)) == B.DV_ERR_SHAPE
+    assert call(k=0) == B.DV_ERR_ARG
+    assert call(L=16385) == B.DV_ERR_UNSUPPORTED
+    assert call(score=None) == B.DV_ERR_NULL
+    assert call(use_thr=1, thr=float("inf")) == B.DV_ERR_ARG
+    # shared memory: the selection's mask as the decisions' subject, outputs on each other, a decision
+    # output on a selection input, a selection output on a decision input
+    assert call(subject=buf(13)) == B.DV_ERR_ARG
+    assert call(decision=buf(13) + 8) == B.DV_ERR_ARG
+    assert call(out_tok=buf(6) + 4) == B.DV_ERR_ARG
+    assert call(score=buf(0) + 64) == B.DV_ERR_ARG
+    assert call(idx=buf(2)) == B.DV_ERR_ARG
+    # nothing to do in either: nothing launched (empty ranges overlap nothing)
+    assert call(rows=0, nseq=0) == B.DV_OK
+    assert call(rows=0, nseq=0, subject=buf(13)) == B.DV_OK
 
 
 def test_debug_noise_validation(lib):

@@ -1,5 +1,5 @@
 """The whole path under HIP graph capture: dv_verify_rows (with its noise table),
-dv_decide, dv_seed_score, dv_select_topk and dv_seed_select allocate nothing and clear nothing
+dv_decide, dv_seed_score, dv_select_topk, dv_seed_select and dv_decide_seed_select allocate nothing and clear nothing
 with memset, so a captured step replays to the eager results, replay after
 replay, with other work and synchronisations in between."""
 
@@ -22,8 +22,14 @@ def _step(a, b, w, out, ws, d_in, d_out, bufs):
     idx, val, cnt, _ = dv.dv_select_topk(score.view(-1, w.group_len), 8)
     # the same seed score and selection in one launch
     score2, idx2, val2, cnt2, _ = dv.dv_seed_select(got["entropy"].view(-1, w.group_len), d_in, d_out, 8)
+    # the decisions and the seed selection in one launch
+    (d3, o3, pre3, best3), (score3, idx3, _, cnt3, _) = dv.dv_decide_seed_select(
+        dict(rule="COUPLED_ACCEPT", stats=got, mask_token=-1, group_len=w.group_len, want_prefix=True, want_best=True),
+        dict(u=got["entropy"].view(-1, w.group_len), d_in=d_in.view(-1, w.group_len),
+             d_out=d_out.view(-1, w.group_len), k=8))
     for k, v in (("d", d), ("o", o), ("pre", pre), ("best", best), ("idx", idx), ("val", val), ("cnt", cnt),
-                 ("score2", score2), ("idx2", idx2), ("val2", val2), ("cnt2", cnt2)):
+                 ("score2", score2), ("idx2", idx2), ("val2", val2), ("cnt2", cnt2), ("d3", d3), ("o3", o3),
+                 ("pre3", pre3), ("best3", best3), ("score3", score3), ("idx3", idx3), ("cnt3", cnt3)):
         bufs[k] = v
     return bufs
 
@@ -46,6 +52,9 @@ def test_path_replays_in_a_graph():
     out = {k: torch.empty(rows, dtype=torch.float32 if k in ("lse_v", "lse_d", "kl", "entropy", "conf") else torch.int32,
                           device=dev) for k in dv.CORE_FIELDS}
     eager = {k: v.clone() for k, v in _step(a, b, w, out, ws, d_in, d_out, {}).items()}
+    for x, y in (("d", "d3"), ("o", "o3"), ("pre", "pre3"), ("best", "best3"), ("score2", "score3"), ("idx2", "idx3"),
+                 ("cnt2", "cnt3")):
+        assert torch.equal(eager[x].view(-1), eager[y].view(-1)), (x, y)
     eager_stats = {k: v.clone() for k, v in out.items()}
     torch.cuda.synchronize()
 

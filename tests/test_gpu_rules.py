@@ -1,4 +1,4 @@
-"""GPU parity of dv_decide, dv_seed_score, dv_select_topk and dv_seed_select, alone (fed the
+"""GPU parity of dv_decide, dv_seed_score, dv_select_topk, dv_seed_select and dv_decide_seed_select, alone (fed the
 same fp32 inputs as the oracle: exact) and chained after dv_verify_rows on the
 workloads (against the oracle's own statistics: exact outside the near-tie
 bands)."""
@@ -217,6 +217,84 @@ def test_seed_select_matches_two_calls(L):
 
 def _upload_bf16(x, dev):
     return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("rule,rows,group_len,prefix,best,nseq,L", [
+    ("COUPLED_ACCEPT", 2048, 32, True, True, 64, 32),     # one launch: one-workgroup decisions
+    ("KL_OR_CONF", 512, 0, False, False, 1, 512),          # one launch: one wave per 64 rows
+    ("COVER", 960, 96, True, True, 3, 320),
+    ("KL", 64, 1, True, False, 2, 2048),
+    ("COUPLED_ACCEPT", 16384, 16, True, True, 8, 2048),    # the largest one-workgroup batch
+    ("CONF", 16400, 16, True, False, 4, 64),               # one launch: one wave per group
+    ("COUPLED_ACCEPT", 20000, 8, True, True, 4, 64),       # the decisions' own two launches, then the selection
+    ("KL", 1000, 0, False, False, 2, 4096),                 # the selection's own two launches
+    ("KL_OR_CONF", 300, 0, False, False, 0, 16),            # no selection
+])
+def test_decide_seed_select_matches_two_calls(rule, rows, group_len, prefix, best, nseq, L):
+    """dv_decide_seed_select gives, output for output and bit for bit, dv_decide followed by
+    dv_seed_select, whichever launch it takes."""
+    print(f"case: decide+seed select {rule} rows={rows} group_len={group_len} nseq={nseq} L={L}", flush=True)
+    dev = _dev()
+    rng = np.random.default_rng(rows + 7 * L + group_len)
+    st = dict(kl=rng.uniform(0, 0.2, rows).astype(np.float32), conf=rng.uniform(0, 1, rows).astype(np.float32),
+              tok_v=rng.integers(0, 3, rows).astype(np.int32), tok_d=rng.integers(0, 3, rows).astype(np.int32))
+    gst = {k: _t(v, dev) for k, v in st.items()}
+    subject = _t((rng.random(rows) < 0.8).astype(np.uint8), dev) if rule == "COVER" else None
+    cur = _t(rng.integers(0, 3, rows).astype(np.int32), dev) if rule == "COVER" else None
+    u = _t(rng.uniform(0, 4, (nseq, L)).round(1).astype(np.float32), dev)
+    d_in = _t(rng.uniform(0, 1, (nseq, L)).astype(np.float32), dev)
+    d_out = _t(rng.uniform(0, 1, (nseq, L)).astype(np.float32), dev)
+    seed_el = _t((rng.random((nseq, L)) < 0.8).astype(np.uint8), dev)
+    k = min(L, 8)
+    dkw = dict(rule=rule, stats=gst, tau_kl=0.1, conf_thr=0.9, mask_token=-9, subject=subject, cur_tok=cur,
+               group_len=group_len, want_prefix=prefix, want_best=best)
+    skw = dict(u=u, d_in=d_in, d_out=d_out, k=k, seed_eligible=seed_el, select_eligible=seed_el, want_mask=True)
+    bits = lambda x: None if x is None else (x.contiguous().view(torch.int32) if x.dtype == torch.float32 else x).cpu().numpy()
+    for rep in range(2):
+        (d, o, pre, bg), (score, idx, val, cnt, mask) = dv.dv_decide_seed_select(dkw, skw)
+        rd, ro, rpre, rbg = dv.dv_decide(dkw["rule"], gst, **{x: v for x, v in dkw.items() if x not in ("rule", "stats")})
+        rscore, ridx, rval, rcnt, rmask = dv.dv_seed_select(u, d_in, d_out, k, seed_eligible=seed_el,
+                                                            select_eligible=seed_el, want_mask=True)
+        for name, x, y in (("decision", d, rd), ("out_tok", o, ro), ("prefix", pre, rpre), ("best", bg, rbg),
+                           ("score", score, rscore), ("idx", idx, ridx), ("val", val, rval), ("cnt", cnt, rcnt),
+                           ("mask", mask, rmask)):
+            if y is None:
+                assert x is None, name
+                continue
+            np.testing.assert_array_equal(bits(x), bits(y), err_msg=f"{name} rep={rep}")
+    # the prepared form: one call on fixed buffers, the same outputs
+    if nseq > 0:
+        bd = dict(decision=torch.empty(rows, dtype=torch.uint8, device=dev),
+                  out_tok=torch.empty(rows, dtype=torch.int32, device=dev),
+                  prefix=torch.empty(max(1, rows // (group_len or rows)), dtype=torch.int32, device=dev),
+                  best=torch.empty(1, dtype=torch.int32, device=dev))
+        bs = dict(score=torch.empty((nseq, L), dtype=torch.float32, device=dev),
+                  idx=torch.empty((nseq, k), dtype=torch.int32, device=dev),
+                  val=torch.empty((nseq, k), dtype=torch.float32, device=dev),
+                  cnt=torch.empty(nseq, dtype=torch.int32, device=dev),
+                  mask=torch.empty((nseq, L), dtype=torch.uint8, device=dev))
+        pd = dv.prepare_decide(rule, gst, bd["decision"], bd["out_tok"], rows=rows, tau_kl=0.1, conf_thr=0.9,
+                               mask_token=-9, subject=subject, group_len=group_len,
+                               prefix=bd["prefix"] if prefix else None, best=bd["best"] if best else None)
+        ps = dv.prepare_seed_select(u, d_in, d_out, seed_el, bs["score"], k, bs["idx"], bs["val"], bs["cnt"],
+                                    select_eligible=seed_el, mask=bs["mask"])
+        if cur is None:
+            dv.prepare_decide_seed_select(pd, ps)()
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(bits(bd["decision"]), bits(rd))
+            np.testing.assert_array_equal(bits(bd["out_tok"]), bits(ro))
+            if best:
+                np.testing.assert_array_equal(bits(bd["best"]), bits(rbg))
+            np.testing.assert_array_equal(bits(bs["idx"]), bits(ridx))
+            np.testing.assert_array_equal(bits(bs["mask"]), bits(rmask))
+        # a selection's mask may not be the decisions' subject in the same call
+        pd2 = dv.prepare_decide(rule, gst, bd["decision"], bd["out_tok"], rows=rows, tau_kl=0.1, conf_thr=0.9,
+                                mask_token=-9, subject=bs["mask"].view(-1)[:rows] if nseq * L >= rows else None,
+                                group_len=group_len, prefix=bd["prefix"] if prefix else None,
+                                best=bd["best"] if best else None)
+        if nseq * L >= rows:
+            with pytest.raises(dv.DVError):
+                dv.prepare_decide_seed_select(pd2, ps)()
 
 
 def test_workload_tiny_rules_chain():

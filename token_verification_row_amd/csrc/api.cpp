@@ -243,8 +243,12 @@ dv_status dv_verify_rows_noalloc(const dv_logits *logits, const dv_noise *noise,
   return launch_verify_rows(logits, noise, g, out, table, stream);
 }
 
-dv_status dv_decide(const dv_decide_args *a, const dv_row_stats *stats, const uint8_t *subject, const int32_t *cur_tok,
-                    uint8_t *decision, int32_t *out_tok, int32_t *prefix_len, int32_t *best_group, hipStream_t stream) {
+// dv_decide's checks and launch parameters; `launch` is false when the call has nothing to do.
+static dv_status decide_launch_of(const dv_decide_args *a, const dv_row_stats *stats, const uint8_t *subject,
+                                  const int32_t *cur_tok, uint8_t *decision, int32_t *out_tok, int32_t *prefix_len,
+                                  int32_t *best_group, dv::DecideLaunch &p, bool &launch) {
+  launch = false;
+  p = dv::DecideLaunch{};
   if (!a || !stats) return fail(DV_ERR_NULL, "args or stats is NULL");
   if (a->rows < 0 || a->rows > kMaxIndex) return fail(DV_ERR_SHAPE, "rows out of range");
   if (a->group_len < 0 || a->group_len > kMaxIndex) return fail(DV_ERR_SHAPE, "group_len out of range");
@@ -287,15 +291,13 @@ dv_status dv_decide(const dv_decide_args *a, const dv_row_stats *stats, const ui
   if (a->rows == 0) {
     if (best_group) {
       // no groups: the answer is -1, written by the reduction kernel
-      dv::DecideLaunch p{};
       p.rows = 0;
       p.best_group = best_group;
       p.prefix_len = prefix_len;
-      return hip_status(dv::launch_decide(p, stream), "dv_decide launch");
+      launch = true;
     }
     return ok();
   }
-  dv::DecideLaunch p{};
   p.rule = a->rule;
   p.tau_kl = a->tau_kl;
   p.conf_thr = a->conf_thr;
@@ -316,6 +318,16 @@ dv_status dv_decide(const dv_decide_args *a, const dv_row_stats *stats, const ui
   p.seed_b = dv::seed_word(a->seed);
   p.pos = a->pos;
   p.pos_period = a->pos_period;
+  launch = true;
+  return ok();
+}
+
+dv_status dv_decide(const dv_decide_args *a, const dv_row_stats *stats, const uint8_t *subject, const int32_t *cur_tok,
+                    uint8_t *decision, int32_t *out_tok, int32_t *prefix_len, int32_t *best_group, hipStream_t stream) {
+  dv::DecideLaunch p;
+  bool launch;
+  const dv_status s = decide_launch_of(a, stats, subject, cur_tok, decision, out_tok, prefix_len, best_group, p, launch);
+  if (s != DV_OK || !launch) return s;
   return hip_status(dv::launch_decide(p, stream), "dv_decide launch");
 }
 
@@ -352,10 +364,13 @@ dv_status dv_select_topk(int64_t nseq, int64_t seq_len, const float *score, cons
   return hip_status(dv::launch_select_topk(p, stream), "dv_select_topk launch");
 }
 
-dv_status dv_seed_select(int64_t nseq, int64_t seq_len, const float *u, const float *d_in, const float *d_out,
-                         const uint8_t *seed_eligible, float *score, const uint8_t *select_eligible, int32_t k,
-                         int32_t largest, int32_t use_thr, float thr, int32_t *out_idx, float *out_val,
-                         int32_t *out_count, uint8_t *out_mask, hipStream_t stream) {
+// dv_seed_select's checks and launch parameters.
+static dv_status seed_select_launch_of(int64_t nseq, int64_t seq_len, const float *u, const float *d_in,
+                                       const float *d_out, const uint8_t *seed_eligible, float *score,
+                                       const uint8_t *select_eligible, int32_t k, int32_t largest, int32_t use_thr,
+                                       float thr, int32_t *out_idx, float *out_val, int32_t *out_count,
+                                       uint8_t *out_mask, dv::SelectLaunch &p) {
+  p = dv::SelectLaunch{};
   if (nseq < 0 || nseq > kMaxIndex) return fail(DV_ERR_SHAPE, "nseq out of range");
   if (seq_len < 1) return fail(DV_ERR_SHAPE, "seq_len must be >= 1");
   if (seq_len > dv::kMaxSelectLen)
@@ -364,7 +379,6 @@ dv_status dv_seed_select(int64_t nseq, int64_t seq_len, const float *u, const fl
   if (k < 1 || k > seq_len) return fail(DV_ERR_ARG, "k must be in [1, seq_len]");
   if (use_thr && !finite(thr)) return fail(DV_ERR_ARG, "thr must be finite");
   if (nseq > 0 && (!u || !d_in || !d_out || !score)) return fail(DV_ERR_NULL, "u, d_in, d_out and score are required");
-  dv::SelectLaunch p{};
   p.nseq = nseq;
   p.seq_len = seq_len;
   p.eligible = select_eligible;
@@ -381,7 +395,71 @@ dv_status dv_seed_select(int64_t nseq, int64_t seq_len, const float *u, const fl
   p.d_out = d_out;
   p.seed_eligible = seed_eligible;
   p.score_out = score;
+  return ok();
+}
+
+dv_status dv_seed_select(int64_t nseq, int64_t seq_len, const float *u, const float *d_in, const float *d_out,
+                         const uint8_t *seed_eligible, float *score, const uint8_t *select_eligible, int32_t k,
+                         int32_t largest, int32_t use_thr, float thr, int32_t *out_idx, float *out_val,
+                         int32_t *out_count, uint8_t *out_mask, hipStream_t stream) {
+  dv::SelectLaunch p;
+  const dv_status s = seed_select_launch_of(nseq, seq_len, u, d_in, d_out, seed_eligible, score, select_eligible, k,
+                                            largest, use_thr, thr, out_idx, out_val, out_count, out_mask, p);
+  if (s != DV_OK) return s;
   return hip_status(dv::launch_seed_select(p, stream), "dv_seed_select launch");
+}
+
+namespace {
+// A device byte range [lo, lo + bytes); null or empty ranges overlap nothing.
+struct Span {
+  uintptr_t lo;
+  size_t bytes;
+};
+Span span_of(const void *p, int64_t n, size_t elem) {
+  return Span{reinterpret_cast<uintptr_t>(p), p && n > 0 ? static_cast<size_t>(n) * elem : 0u};
+}
+bool overlap(const Span &x, const Span &y) {
+  return x.bytes && y.bytes && x.lo < y.lo + y.bytes && y.lo < x.lo + x.bytes;
+}
+}  // namespace
+
+dv_status dv_decide_seed_select(const dv_decide_args *a, const dv_row_stats *stats, const uint8_t *subject,
+                                const int32_t *cur_tok, uint8_t *decision, int32_t *out_tok, int32_t *prefix_len,
+                                int32_t *best_group, int64_t nseq, int64_t seq_len, const float *u, const float *d_in,
+                                const float *d_out, const uint8_t *seed_eligible, float *score,
+                                const uint8_t *select_eligible, int32_t k, int32_t largest, int32_t use_thr, float thr,
+                                int32_t *out_idx, float *out_val, int32_t *out_count, uint8_t *out_mask,
+                                hipStream_t stream) {
+  dv::DecideLaunch pd;
+  bool decide;
+  dv_status s = decide_launch_of(a, stats, subject, cur_tok, decision, out_tok, prefix_len, best_group, pd, decide);
+  if (s != DV_OK) return s;
+  dv::SelectLaunch ps;
+  s = seed_select_launch_of(nseq, seq_len, u, d_in, d_out, seed_eligible, score, select_eligible, k, largest, use_thr,
+                            thr, out_idx, out_val, out_count, out_mask, ps);
+  if (s != DV_OK) return s;
+  // The two run together: no buffer one of them writes may be one the other reads or writes.
+  const int64_t R = a->rows, n = nseq * seq_len, ng = a->group_len > 0 ? R / a->group_len : 0;
+  const int32_t *tok_d_read = cur_tok ? nullptr : stats->tok_d;
+  const Span d_in_spans[] = {span_of(pd.kl, R, 4), span_of(pd.conf, R, 4), span_of(pd.p_tok, R, 4),
+                             span_of(pd.tok_v, R, 4), span_of(tok_d_read, R, 4), span_of(subject, R, 1),
+                             span_of(cur_tok, R, 4), span_of(pd.pos, R, 4)};
+  const Span d_out_spans[] = {span_of(decision, R, 1), span_of(out_tok, R, 4), span_of(prefix_len, ng, 4),
+                              span_of(best_group, 1, 4)};
+  const Span s_in_spans[] = {span_of(u, n, 4), span_of(d_in, n, 4), span_of(d_out, n, 4),
+                             span_of(seed_eligible, n, 1), span_of(select_eligible, n, 1)};
+  const Span s_out_spans[] = {span_of(score, n, 4), span_of(out_idx, nseq * k, 4), span_of(out_val, nseq * k, 4),
+                              span_of(out_count, nseq, 4), span_of(out_mask, n, 1)};
+  for (const Span &x : d_out_spans) {
+    for (const Span &y : s_in_spans)
+      if (overlap(x, y)) return fail(DV_ERR_ARG, "a decision output overlaps a seed-selection input");
+    for (const Span &y : s_out_spans)
+      if (overlap(x, y)) return fail(DV_ERR_ARG, "a decision output overlaps a seed-selection output");
+  }
+  for (const Span &x : s_out_spans)
+    for (const Span &y : d_in_spans)
+      if (overlap(x, y)) return fail(DV_ERR_ARG, "a seed-selection output overlaps a decision input");
+  return hip_status(dv::launch_decide_seed_select(pd, decide, ps, stream), "dv_decide_seed_select launch");
 }
 
 dv_status dv_influence_drift_workspace_bytes(const dv_attention *att, size_t *bytes) {

@@ -135,6 +135,8 @@ struct SelectLaunch {
 constexpr int64_t kMaxSelectLen = 16384;
 hipError_t launch_select_topk(const SelectLaunch &p, hipStream_t stream);
 hipError_t launch_seed_select(const SelectLaunch &p, hipStream_t stream);
+// dv_decide (when decide is set) and dv_seed_select, fused into one launch where both fit it
+hipError_t launch_decide_seed_select(const DecideLaunch &d, bool decide, const SelectLaunch &s, hipStream_t stream);
 
 constexpr int kMaxTreeNodes = 1024;
 constexpr int kMaxTreeBlockLen = 1024;

@@ -44,6 +44,23 @@ __device__ __forceinline__ uint8_t rule_of_row(const DecideLaunch &p, int64_t r,
   }
 }
 
+// rule_of_row with the rule fixed at compile time (a loop over rows then holds one rule's code only).
+template <int RULE>
+__device__ __forceinline__ uint8_t rule_of_row_t(const DecideLaunch &p, int64_t r, int32_t cur) {
+  if constexpr (RULE == DV_RULE_TRUST) return DV_KEEP;
+  if constexpr (RULE == DV_RULE_KL) return p.kl[r] > p.tau_kl ? DV_REMASK : DV_KEEP;
+  if constexpr (RULE == DV_RULE_CONF) return p.conf[r] < p.conf_thr ? DV_REMASK : DV_KEEP;
+  if constexpr (RULE == DV_RULE_KL_OR_CONF) return (p.kl[r] > p.tau_kl || p.conf[r] < p.conf_thr) ? DV_REMASK : DV_KEEP;
+  if constexpr (RULE == DV_RULE_COVER) {
+    if (p.tok_v[r] == cur) return DV_KEEP;
+    return p.conf[r] >= p.conf_thr ? DV_REPLACE : DV_REMASK;
+  }
+  if constexpr (RULE == DV_RULE_CONF_DRAFT) return p.p_tok[r] < p.conf_thr ? DV_REMASK : DV_KEEP;
+  if constexpr (RULE == DV_RULE_KL_STOCHASTIC)
+    return __fmul_rn(remask_uniform(p, r), p.tau_kl) < p.kl[r] ? DV_REMASK : DV_KEEP;
+  return DV_NONE;
+}
+
 __device__ __forceinline__ int32_t current_token(const DecideLaunch &p, int64_t r) {
   return p.cur_tok ? p.cur_tok[r] : p.tok_d[r];
 }
@@ -66,9 +83,7 @@ __device__ __forceinline__ void emit(const DecideLaunch &p, int64_t r, uint8_t d
 // the first decided row that breaks the group (coupled acceptance: tokens
 // disagree; other rules: decision is not KEEP); pass 2 writes the decisions.
 // With group_len == 0 the rows are cut into 64-row tiles and no prefix exists.
-__global__ __launch_bounds__(256) void decide_kernel(DecideLaunch p) {
-  const int lane = threadIdx.x & 63;
-  const int64_t g = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+__device__ __forceinline__ void decide_group(const DecideLaunch &p, int64_t g, int lane) {
   const int64_t G = p.group_len > 0 ? p.group_len : 64;
   const int64_t ngroups = (p.rows + G - 1) / G;
   if (g >= ngroups) return;
@@ -107,6 +122,10 @@ __global__ __launch_bounds__(256) void decide_kernel(DecideLaunch p) {
   if (p.prefix_len && lane == 0) p.prefix_len[g] = static_cast<int32_t>(first);
 }
 
+__global__ __launch_bounds__(256) void decide_kernel(DecideLaunch p) {
+  decide_group(p, static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6), threadIdx.x & 63);
+}
+
 // Longest accepted prefix over all groups, lowest group index on ties.
 __global__ __launch_bounds__(1024) void best_group_kernel(const int32_t *prefix, int64_t ngroups, int32_t *best) {
   __shared__ long long s_key[1024];
@@ -136,55 +155,169 @@ __global__ __launch_bounds__(1024) void best_group_kernel(const int32_t *prefix,
 constexpr int64_t kSmallDecideRows = 16384;
 constexpr int64_t kSmallDecideGroups = 1024;
 
-__global__ __launch_bounds__(1024) void decide_small_kernel(DecideLaunch p) {
-  __shared__ int32_t s_first[kSmallDecideGroups];
-  __shared__ long long s_key[1024];
-  const int tid = threadIdx.x;
-  const int64_t G = p.group_len;  // > 0 and dividing rows
-  const int64_t ngroups = p.rows / G;
-  const bool coupled = p.rule == DV_RULE_COUPLED_ACCEPT;
-  for (int64_t g = tid; g < ngroups; g += 1024) s_first[g] = static_cast<int32_t>(G);
-  __syncthreads();
-  for (int64_t r = tid; r < p.rows; r += 1024) {
-    if (!is_subject(p, r)) continue;
-    const int32_t cur = current_token(p, r);
-    const bool brk = coupled ? (p.tok_v[r] != cur) : (rule_of_row(p, r, cur) != DV_KEEP);
-    if (brk) atomicMin(&s_first[r / G], static_cast<int32_t>(r % G));
+// Largest key of a workgroup of kThreads threads: xor shuffles inside each wave,
+// then one LDS round over the waves' results. Every thread gets the answer.
+template <int kThreads>
+__device__ __forceinline__ long long block_max_key(long long key, long long *s_wave) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const long long other = __shfl_xor(key, o);
+    key = other > key ? other : key;
   }
+  if ((threadIdx.x & 63) == 0) s_wave[threadIdx.x >> 6] = key;
   __syncthreads();
-  for (int64_t r = tid; r < p.rows; r += 1024) {
-    const int32_t cur = current_token(p, r);
-    uint8_t d = DV_NONE;
-    if (is_subject(p, r)) {
-      if (coupled) {
-        const int64_t j = r % G, first = s_first[r / G];
-        d = j < first ? DV_KEEP : (j == first ? DV_REPLACE : DV_REMASK);
-      } else {
-        d = rule_of_row(p, r, cur);
+  long long m = s_wave[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) m = s_wave[w] > m ? s_wave[w] : m;
+  return m;
+}
+
+// q = r / G and m = r - q G for 0 <= r < 2^24 and G >= 1: the quotient through the
+// float reciprocal is off by at most one, which the remainder's range corrects
+// (integer division is a long instruction sequence on this GPU).
+__device__ __forceinline__ void divmod_small(int32_t r, int32_t G, float rcp_G, int32_t &q, int32_t &m) {
+  q = static_cast<int32_t>(static_cast<float>(r) * rcp_G);
+  m = r - q * G;
+  if (m < 0) {
+    --q;
+    m += G;
+  }
+  if (m >= G) {
+    ++q;
+    m -= G;
+  }
+}
+
+// The single-workgroup decision over all rows, for a workgroup of kThreads
+// threads (group_len > 0 dividing rows, rows <= kSmallDecideRows, at most
+// kSmallDecideGroups groups), with the rule fixed at compile time.
+template <int kThreads, int RULE>
+__device__ __forceinline__ void decide_small_rule(const DecideLaunch &p, int32_t *s_first, long long *s_wave) {
+  constexpr bool coupled = RULE == DV_RULE_COUPLED_ACCEPT;
+  const int32_t tid = static_cast<int32_t>(threadIdx.x);
+  const int32_t rows = static_cast<int32_t>(p.rows), G = static_cast<int32_t>(p.group_len);
+  const int32_t ngroups = rows / G;
+  const float rcp_G = 1.0f / static_cast<float>(G);
+  for (int32_t g = tid; g < ngroups; g += kThreads) s_first[g] = G;
+  __syncthreads();
+  // Rows go in batches of kBatch per thread, every load of a batch issued before the first
+  // is used (at clamped, always valid rows, the optional arrays chosen outside the batch):
+  // one memory round trip per batch, not one per row.
+  constexpr int kBatch = 8;
+  const int32_t *ctok = p.cur_tok ? p.cur_tok : p.tok_d;
+  const auto load_batch = [&](int32_t base, bool (&subj)[kBatch], int32_t (&cur)[kBatch], int32_t (&tv)[kBatch]) {
+    int32_t rc[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) rc[i] = min(base + i * kThreads, rows - 1);
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) cur[i] = ctok[rc[i]];
+    if constexpr (coupled) {
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) tv[i] = p.tok_v[rc[i]];
+    }
+    uint8_t sb[kBatch];
+    if (p.subject) {
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) sb[i] = p.subject[rc[i]];
+    } else {
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) sb[i] = 1;
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) subj[i] = base + i * kThreads < rows && sb[i] != 0;
+  };
+  for (int32_t base = tid; base < rows; base += kThreads * kBatch) {
+    bool subj[kBatch], brk[kBatch];
+    int32_t cur[kBatch], tv[kBatch];
+    load_batch(base, subj, cur, tv);
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if constexpr (coupled)
+        brk[i] = subj[i] && tv[i] != cur[i];
+      else
+        brk[i] = subj[i] && rule_of_row_t<RULE>(p, min(base + i * kThreads, rows - 1), cur[i]) != DV_KEEP;
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (brk[i]) {
+        int32_t g, j;
+        divmod_small(base + i * kThreads, G, rcp_G, g, j);
+        atomicMin(&s_first[g], j);
       }
     }
-    emit(p, r, d, cur);
+  }
+  __syncthreads();
+  for (int32_t base = tid; base < rows; base += kThreads * kBatch) {
+    bool subj[kBatch];
+    int32_t cur[kBatch], tv[kBatch];
+    uint8_t d[kBatch];
+    load_batch(base, subj, cur, tv);
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int32_t r = base + i * kThreads;
+      d[i] = DV_NONE;
+      if (subj[i]) {
+        if constexpr (coupled) {
+          int32_t g, j;
+          divmod_small(r, G, rcp_G, g, j);
+          const int32_t first = s_first[g];
+          d[i] = j < first ? DV_KEEP : (j == first ? DV_REPLACE : DV_REMASK);
+        } else {
+          d[i] = rule_of_row_t<RULE>(p, r, cur[i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int32_t r = base + i * kThreads;
+      if (r < rows) {
+        if (p.decision) p.decision[r] = d[i];
+        if (p.out_tok) {
+          int32_t t = cur[i];
+          if (d[i] == DV_REPLACE) {
+            if constexpr (coupled)
+              t = tv[i];
+            else
+              t = p.tok_v[r];
+          }
+          if (d[i] == DV_REMASK) t = p.mask_token;
+          p.out_tok[r] = t;
+        }
+      }
+    }
   }
   long long key = LLONG_MIN;
-  for (int64_t g = tid; g < ngroups; g += 1024) {
+  for (int32_t g = tid; g < ngroups; g += kThreads) {
     const int32_t f = s_first[g];
     if (p.prefix_len) p.prefix_len[g] = f;
+    // larger prefix first; among equal prefixes the smaller index gives the larger key
     const long long k = (static_cast<long long>(f) << 32) | static_cast<long long>(0xFFFFFFFFu - static_cast<uint32_t>(g));
     key = k > key ? k : key;
   }
   if (p.best_group == nullptr) return;  // uniform: no barrier follows for anyone
-  s_key[tid] = key;
-  __syncthreads();
-  for (int o = 512; o > 0; o >>= 1) {
-    if (tid < o) {
-      const long long other = s_key[tid + o];
-      if (other > s_key[tid]) s_key[tid] = other;
-    }
-    __syncthreads();
-  }
+  const long long best = block_max_key<kThreads>(key, s_wave);
   if (tid == 0)
-    p.best_group[0] = ngroups > 0 ? static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(s_key[0] & 0xFFFFFFFFll)) : -1;
+    p.best_group[0] = ngroups > 0 ? static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(best & 0xFFFFFFFFll)) : -1;
 }
+
+template <int kThreads>
+__device__ __forceinline__ void decide_small_block(const DecideLaunch &p) {
+  __shared__ int32_t s_first[kSmallDecideGroups];
+  __shared__ long long s_wave[kThreads / 64];
+  switch (p.rule) {
+    case DV_RULE_COUPLED_ACCEPT: decide_small_rule<kThreads, DV_RULE_COUPLED_ACCEPT>(p, s_first, s_wave); break;
+    case DV_RULE_TRUST: decide_small_rule<kThreads, DV_RULE_TRUST>(p, s_first, s_wave); break;
+    case DV_RULE_KL: decide_small_rule<kThreads, DV_RULE_KL>(p, s_first, s_wave); break;
+    case DV_RULE_CONF: decide_small_rule<kThreads, DV_RULE_CONF>(p, s_first, s_wave); break;
+    case DV_RULE_KL_OR_CONF: decide_small_rule<kThreads, DV_RULE_KL_OR_CONF>(p, s_first, s_wave); break;
+    case DV_RULE_COVER: decide_small_rule<kThreads, DV_RULE_COVER>(p, s_first, s_wave); break;
+    case DV_RULE_CONF_DRAFT: decide_small_rule<kThreads, DV_RULE_CONF_DRAFT>(p, s_first, s_wave); break;
+    case DV_RULE_KL_STOCHASTIC: decide_small_rule<kThreads, DV_RULE_KL_STOCHASTIC>(p, s_first, s_wave); break;
+    default: break;
+  }
+}
+
+__global__ __launch_bounds__(1024) void decide_small_kernel(DecideLaunch p) { decide_small_block<1024>(p); }
 
 // ------------------------------------------------------------ seed score ----
 // [COVER] §2, the Score equation: u (1 + d_in) / (1 + d_out).
@@ -222,13 +355,13 @@ __device__ __forceinline__ unsigned long long select_key(float s, uint32_t i, in
 // arithmetic, and each workgroup writes those of its own 64 positions.
 constexpr int32_t kRankMaxLen = 2048;
 constexpr int kRankThreads = 256;
-__global__ __launch_bounds__(kRankThreads) void select_rank_kernel(SelectLaunch p) {
+// The workgroup of sequence seq and positions [64 by, 64 by + 64) (kRankThreads threads).
+__device__ __forceinline__ void select_rank_block(const SelectLaunch &p, int64_t seq, int32_t by) {
   constexpr int kPer = kRankMaxLen / kRankThreads;  // keys built per thread, at most
   __shared__ unsigned long long keys[kRankMaxLen];
   __shared__ float vals[kRankMaxLen];
   __shared__ int32_t part[4][64];
   __shared__ int32_t wave_kept[4];
-  const int64_t seq = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t L = static_cast<int32_t>(p.seq_len);
   const float *sc = p.score + seq * p.seq_len;
@@ -238,6 +371,13 @@ __global__ __launch_bounds__(kRankThreads) void select_rank_kernel(SelectLaunch 
   // loads at clamped (always valid) positions, all issued before the first is used
   float v[kPer];
   uint32_t e[kPer];
+  if (el) {
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) e[t] = el[min(t * kRankThreads + tid, L - 1)];
+  } else {
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) e[t] = 1u;
+  }
   if (p.u) {
     // the seed scores, with seed_score_kernel's arithmetic
     const int64_t base = seq * p.seq_len;
@@ -249,7 +389,14 @@ __global__ __launch_bounds__(kRankThreads) void select_rank_kernel(SelectLaunch 
       uu[t] = p.u[j];
       di[t] = p.d_in[j];
       dd[t] = p.d_out[j];
-      se[t] = p.seed_eligible ? p.seed_eligible[j] : 1u;
+    }
+    // the optional array chosen once, outside the loads (a choice per load would wait for each)
+    if (p.seed_eligible) {
+#pragma unroll
+      for (int t = 0; t < kPer; ++t) se[t] = p.seed_eligible[base + min(t * kRankThreads + tid, L - 1)];
+    } else {
+#pragma unroll
+      for (int t = 0; t < kPer; ++t) se[t] = 1u;
     }
 #pragma unroll
     for (int t = 0; t < kPer; ++t) {
@@ -257,18 +404,11 @@ __global__ __launch_bounds__(kRankThreads) void select_rank_kernel(SelectLaunch 
       if (se[t] != 0) s = uu[t] * (1.0f + di[t]) / (1.0f + dd[t]);
       v[t] = s;
       const int32_t j = t * kRankThreads + tid;
-      if (p.score_out && j < L && (j >> 6) == static_cast<int32_t>(blockIdx.y)) p.score_out[base + j] = s;
+      if (p.score_out && j < L && (j >> 6) == by) p.score_out[base + j] = s;
     }
   } else {
 #pragma unroll
     for (int t = 0; t < kPer; ++t) v[t] = sc[min(t * kRankThreads + tid, L - 1)];
-  }
-  if (el) {
-#pragma unroll
-    for (int t = 0; t < kPer; ++t) e[t] = el[min(t * kRankThreads + tid, L - 1)];
-  } else {
-#pragma unroll
-    for (int t = 0; t < kPer; ++t) e[t] = 1u;
   }
   int32_t kept = 0;
 #pragma unroll
@@ -286,7 +426,7 @@ __global__ __launch_bounds__(kRankThreads) void select_rank_kernel(SelectLaunch 
   if (lane == 0) wave_kept[wave] = kept;
   __syncthreads();
   const int32_t count = min(p.k, wave_kept[0] + wave_kept[1] + wave_kept[2] + wave_kept[3]);
-  const int32_t i = static_cast<int32_t>(blockIdx.y) * 64 + lane;
+  const int32_t i = by * 64 + lane;
   const unsigned long long ki = i < L ? keys[i] : 0ull;
   const int32_t q = (L + 3) / 4, j0 = wave * q, j1 = min(L, j0 + q);
   int32_t r = 0;
@@ -302,13 +442,17 @@ __global__ __launch_bounds__(kRankThreads) void select_rank_kernel(SelectLaunch 
     if (p.out_val) p.out_val[seq * p.k + rank] = vals[i];
   }
   if (p.out_mask && i < L) p.out_mask[seq * p.seq_len + i] = sel ? 1 : 0;
-  if (blockIdx.y == 0) {
+  if (by == 0) {
     for (int32_t j = count + lane; j < p.k; j += 64) {
       if (p.out_idx) p.out_idx[seq * p.k + j] = -1;
       if (p.out_val) p.out_val[seq * p.k + j] = __builtin_nanf("");
     }
     if (lane == 0 && p.out_count) p.out_count[seq] = count;
   }
+}
+
+__global__ __launch_bounds__(kRankThreads) void select_rank_kernel(SelectLaunch p) {
+  select_rank_block(p, blockIdx.x, static_cast<int32_t>(blockIdx.y));
 }
 
 // Longer sequences: one workgroup per sequence, bitonic sort of pow2 keys in LDS.
@@ -373,6 +517,26 @@ __global__ __launch_bounds__(1024) void select_topk_kernel(SelectLaunch p, int32
   }
 }
 
+// ------------------------------------------------- decide + seed select ----
+// dv_decide and dv_seed_select in one launch of kRankThreads-thread workgroups:
+// the first nd workgroups decide (one workgroup for the whole batch on the
+// small-batch path, else one group per wave as decide_kernel), the others
+// select as select_rank_kernel, workgroup nd + seq * ny + y taking positions
+// [64 y, 64 y + 64) of sequence seq. The two calls share no memory, so the
+// order in which their workgroups run does not matter.
+__global__ __launch_bounds__(kRankThreads) void decide_select_kernel(DecideLaunch d, SelectLaunch s, uint32_t nd,
+                                                                    int32_t small, uint32_t ny) {
+  const uint32_t b = blockIdx.x;
+  if (b < nd) {
+    if (small)
+      decide_small_block<kRankThreads>(d);
+    else
+      decide_group(d, static_cast<int64_t>(b) * (kRankThreads / 64) + (threadIdx.x >> 6), threadIdx.x & 63);
+    return;
+  }
+  select_rank_block(s, (b - nd) / ny, static_cast<int32_t>((b - nd) % ny));
+}
+
 // ------------------------------------------------------------- noise dump ----
 }  // namespace
 
@@ -418,6 +582,29 @@ hipError_t launch_seed_select(const SelectLaunch &p, hipStream_t stream) {
   q.seed_eligible = nullptr;
   q.score_out = nullptr;
   return launch_select_topk(q, stream);
+}
+
+hipError_t launch_decide_seed_select(const DecideLaunch &d, bool decide, const SelectLaunch &s, hipStream_t stream) {
+  const int64_t G = d.group_len > 0 ? d.group_len : 64;
+  const int64_t ngroups = (d.rows + G - 1) / G;
+  const bool small = d.group_len > 0 && d.rows <= kSmallDecideRows && ngroups <= kSmallDecideGroups;
+  // one launch when the decision is one workgroup or one wave per group with no best-group pass,
+  // and the selection is the rank path
+  const bool fusable = decide && d.rows > 0 && (small || d.best_group == nullptr) && s.nseq > 0 &&
+                       s.seq_len <= kRankMaxLen;
+  const int64_t ny = (s.seq_len + 63) / 64;
+  const int64_t nd = small ? 1 : (ngroups + kRankThreads / 64 - 1) / (kRankThreads / 64);
+  if (fusable && nd + s.nseq * ny <= 0x7FFFFFFFll) {
+    hipLaunchKernelGGL(decide_select_kernel, dim3(static_cast<unsigned>(nd + s.nseq * ny)), dim3(kRankThreads), 0,
+                       stream, d, s, static_cast<uint32_t>(nd), small ? 1 : 0, static_cast<uint32_t>(ny));
+    return hipGetLastError();
+  }
+  // otherwise each call's own launches, in call order
+  if (decide) {
+    const hipError_t e = launch_decide(d, stream);
+    if (e != hipSuccess) return e;
+  }
+  return launch_seed_select(s, stream);
 }
 
 hipError_t launch_select_topk(const SelectLaunch &p, hipStream_t stream) {

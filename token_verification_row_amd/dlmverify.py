@@ -96,6 +96,9 @@ _SIGNATURES = {
                                       ctypes.c_int32, ctypes.c_float, _P, _P, _P, _P, _P]),
     "dv_seed_select": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P, _P, _P, _P, _P]),
+    "dv_decide_seed_select": (ctypes.c_int, [ctypes.POINTER(dv_decide_args), ctypes.POINTER(dv_row_stats)] + [_P] * 6 +
+                              [ctypes.c_int64, ctypes.c_int64] + [_P] * 6 +
+                              [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float] + [_P] * 5),
     "dv_tree_accept": (ctypes.c_int, [ctypes.POINTER(dv_tree_args)] + [_P] * 15),
     "dv_dual_view_attention": (ctypes.c_int, [ctypes.POINTER(dv_dual_view_args)] + [_P] * 8),
     "dv_influence_drift_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(dv_attention), ctypes.POINTER(ctypes.c_size_t)]),
@@ -371,6 +374,15 @@ def prepare_seed_select(u, d_in, d_out, seed_eligible, score, k, idx, val, cnt, 
                     _ptr(mask), _stream_handle(u.device))
 
 
+def prepare_decide_seed_select(decide: Prepared, seed_select: Prepared) -> Prepared:
+    """A prepared dv_decide and a prepared dv_seed_select (same stream) as one dv_decide_seed_select call."""
+    if decide._name != "dv_decide" or seed_select._name != "dv_seed_select":
+        raise TypeError("expects a prepared dv_decide and a prepared dv_seed_select")
+    if decide._args[-1] != seed_select._args[-1]:
+        raise ValueError("the two calls must use one stream")
+    return Prepared("dv_decide_seed_select", *decide._args[:-1], *seed_select._args[:-1], decide._args[-1])
+
+
 def prepare_decide(rule, stats, decision, out_tok, *, rows, tau_kl=0.0, conf_thr=0.0, mask_token=-1, subject=None,
                    group_len=0, prefix=None, best=None) -> Prepared:
     """dv_decide on fixed buffers; ``stats`` maps dv_row_stats members to device tensors."""
@@ -383,11 +395,9 @@ def prepare_decide(rule, stats, decision, out_tok, *, rows, tau_kl=0.0, conf_thr
                     _ptr(out_tok), _ptr(prefix), _ptr(best), _stream_handle(dev))
 
 
-def dv_decide(rule, stats, *, rows=None, tau_kl=0.0, conf_thr=0.0, mask_token=-1, subject=None, cur_tok=None,
-              group_len=0, want_prefix=False, want_best=False, seed=0, pos=None, pos_period=0):
-    """Per-position decisions. ``stats`` is a dict with kl / conf / tok_v / tok_d
-    tensors. Returns (decision uint8, out_tok int32, prefix int32 or None, best int32[1] or None).
-    seed, pos (int32 [rows]) and pos_period key the draws of KL_STOCHASTIC, as in dv_verify_rows."""
+def _decide_call(rule, stats, *, rows=None, tau_kl=0.0, conf_thr=0.0, mask_token=-1, subject=None, cur_tok=None,
+                 group_len=0, want_prefix=False, want_best=False, seed=0, pos=None, pos_period=0):
+    """dv_decide's C arguments (without the stream), the outputs they point to and the device."""
     rule = RULES[rule] if isinstance(rule, str) else int(rule)
     ref = next(v for k, v in stats.items() if k in STAT_FIELDS and v is not None)
     rows = ref.numel() if rows is None else int(rows)
@@ -410,12 +420,22 @@ def dv_decide(rule, stats, *, rows=None, tau_kl=0.0, conf_thr=0.0, mask_token=-1
                           rows=rows, group_len=int(group_len), seed=int(seed) & 0xFFFFFFFFFFFFFFFF,
                           pos=None if pos is None else pos.data_ptr(), pos_period=int(pos_period))
     st = dv_row_stats(**{f: (stats[f].data_ptr() if stats.get(f) is not None else None) for f in STAT_FIELDS})
-    _check(load_library().dv_decide(ctypes.byref(args), ctypes.byref(st), _ptr(subject), _ptr(cur_tok),
-                                    _ptr(decision), _ptr(out_tok), _ptr(prefix), _ptr(best), _stream_handle(dev)),
-           "dv_decide")
+    cargs = (ctypes.byref(args), ctypes.byref(st), _ptr(subject), _ptr(cur_tok), _ptr(decision), _ptr(out_tok),
+             _ptr(prefix), _ptr(best))
     if prefix is not None:
         prefix = prefix[:ngroups]
-    return decision, out_tok, prefix, best
+    return cargs, (decision, out_tok, prefix, best), dev
+
+
+def dv_decide(rule, stats, **kw):
+    """Per-position decisions. ``stats`` is a dict with kl / conf / tok_v / tok_d
+    tensors. Keywords: rows, tau_kl, conf_thr, mask_token, subject, cur_tok, group_len, want_prefix,
+    want_best, seed, pos, pos_period. Returns (decision uint8, out_tok int32, prefix int32 or None,
+    best int32[1] or None). seed, pos (int32 [rows]) and pos_period key the draws of KL_STOCHASTIC, as
+    in dv_verify_rows."""
+    cargs, outs, dev = _decide_call(rule, stats, **kw)
+    _check(load_library().dv_decide(*cargs, _stream_handle(dev)), "dv_decide")
+    return outs
 
 
 def dv_seed_score(u, d_in, d_out, eligible=None, *, out=None):
@@ -459,10 +479,9 @@ def dv_select_topk(score, k, *, eligible=None, largest=True, use_thr=False, thr=
     return idx, val, cnt[:nseq], mask
 
 
-def dv_seed_select(u, d_in, d_out, k, *, seed_eligible=None, select_eligible=None, largest=True, use_thr=False, thr=0.0,
-                   want_mask=False):
-    """COVER seed scores of u, d_in, d_out [nseq, L] and their per-sequence top-k in one call: the same outputs
-    as dv_seed_score followed by dv_select_topk. Returns (score [nseq, L], idx, val, count, mask or None)."""
+def _seed_select_call(u, d_in, d_out, k, *, seed_eligible=None, select_eligible=None, largest=True, use_thr=False,
+                      thr=0.0, want_mask=False):
+    """dv_seed_select's C arguments (without the stream), the outputs they point to and the device."""
     for name, v in (("u", u), ("d_in", d_in), ("d_out", d_out)):
         _need_cuda(v, name)
         if v.dtype != torch.float32 or not v.is_contiguous():
@@ -484,11 +503,30 @@ def dv_seed_select(u, d_in, d_out, k, *, seed_eligible=None, select_eligible=Non
     val = torch.empty((nseq, kk), dtype=torch.float32, device=dev)
     cnt = torch.empty(max(nseq, 1), dtype=torch.int32, device=dev)
     mask = torch.empty((nseq, L), dtype=torch.uint8, device=dev) if want_mask else None
-    _check(load_library().dv_seed_select(nseq, L, _ptr(u), _ptr(d_in), _ptr(d_out), _ptr(seed_eligible), _ptr(score),
-                                         _ptr(select_eligible), int(k), int(bool(largest)), int(bool(use_thr)),
-                                         float(thr), _ptr(idx), _ptr(val), _ptr(cnt), _ptr(mask), _stream_handle(dev)),
-           "dv_seed_select")
-    return score, idx, val, cnt[:nseq], mask
+    cargs = (nseq, L, _ptr(u), _ptr(d_in), _ptr(d_out), _ptr(seed_eligible), _ptr(score), _ptr(select_eligible),
+             int(k), int(bool(largest)), int(bool(use_thr)), float(thr), _ptr(idx), _ptr(val), _ptr(cnt), _ptr(mask))
+    return cargs, (score, idx, val, cnt[:nseq], mask), dev
+
+
+def dv_seed_select(u, d_in, d_out, k, **kw):
+    """COVER seed scores of u, d_in, d_out [nseq, L] and their per-sequence top-k in one call: the same outputs
+    as dv_seed_score followed by dv_select_topk. Keywords: seed_eligible, select_eligible, largest, use_thr,
+    thr, want_mask. Returns (score [nseq, L], idx, val, count, mask or None)."""
+    cargs, outs, dev = _seed_select_call(u, d_in, d_out, k, **kw)
+    _check(load_library().dv_seed_select(*cargs, _stream_handle(dev)), "dv_seed_select")
+    return outs
+
+
+def dv_decide_seed_select(decide: dict, seed_select: dict):
+    """dv_decide and dv_seed_select in one call (one launch where both fit it). ``decide`` holds dv_decide's
+    arguments by name (rule, stats and its keywords), ``seed_select`` dv_seed_select's (u, d_in, d_out, k and
+    its keywords). Returns (dv_decide's outputs, dv_seed_select's outputs)."""
+    dargs, douts, dev = _decide_call(**decide)
+    sargs, souts, sdev = _seed_select_call(**seed_select)
+    if sdev != dev:
+        raise ValueError("the decision and the selection must be on one device")
+    _check(load_library().dv_decide_seed_select(*dargs, *sargs, _stream_handle(dev)), "dv_decide_seed_select")
+    return douts, souts
 
 
 def dv_tree_accept(parent, node_pos, node_tok, root_masked, conf, tok_v, *, block_tokens=None, update_mask=False):

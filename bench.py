@@ -254,6 +254,10 @@ def main() -> int:
     ap.add_argument("--read-probe", action="store_true",
                     help="instead of the path, time the read-only streaming probe (dv_debug_read_probe) over the "
                          "workload's logits in the verify pass's launch shape: the attainable read rate")
+    ap.add_argument("--gemm-reference", type=int, default=0, metavar="N",
+                    help="instead of the path, time a bf16 N x N x N matrix product through torch.matmul (the "
+                         "vendor GEMM library) --steps times: the dense bf16 rate a tuned library reaches on this "
+                         "GPU, the reference for the dual-view attention's matrix-core rate")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; the verification path has no multi-GPU mode (asked for --gpus {args.gpus})",
@@ -279,6 +283,31 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": args.steps}), flush=True)
+        return 0
+    if args.gemm_reference:
+        n = args.gemm_reference
+        g = torch.Generator(device=dev).manual_seed(0)
+        a = torch.randn((n, n), device=dev, generator=g).to(torch.bfloat16)
+        b = torch.randn((n, n), device=dev, generator=g).to(torch.bfloat16)
+        c = torch.empty((n, n), device=dev, dtype=torch.bfloat16)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < max(args.warmup_seconds, 1.0):
+            torch.matmul(a, b, out=c)
+            torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        stream = torch.cuda.current_stream(dev)
+        for e0, e1 in ev:
+            e0.record(stream)
+            torch.matmul(a, b, out=c)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        st = _summary(_durations_us(ev))
+        flop = 2.0 * n ** 3
+        print(json.dumps({"gemm_reference": {"n": n, "dtype": "bf16", "launches": args.steps, **st,
+                                             "flop_per_launch": flop,
+                                             "TFLOPs_median": flop / (st["median_us"] * 1e-6) / 1e12,
+                                             "frac_of_2500TFLOPs": flop / (st["median_us"] * 1e-6) / 1e12 / 2500.0}}),
+              flush=True)
         return 0
     w = W.workload(args.workload)
     if args.temperature is not None:

@@ -43,3 +43,17 @@ def test_json_line(args):
     assert 0 < rf["frac"] < 1 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-9
     # steps run back to back: a step takes at least the verify call it contains
     assert d["ms_per_step"] * 1000 >= 0.9 * rf["median_us"]
+
+
+@pytest.mark.gpu
+def test_gemm_reference_line():
+    """--gemm-reference prints one JSON line with the library GEMM's rate and its share of the bf16 peak."""
+    print("case: bench --gemm-reference 1024", flush=True)
+    r = _run("--gemm-reference", "1024", "--steps", "3", "--warmup-seconds", "0")
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+    assert len(lines) == 1, r.stdout[-2000:]
+    g = json.loads(lines[0])["gemm_reference"]
+    assert g["n"] == 1024 and g["launches"] == 3 and g["flop_per_launch"] == 2.0 * 1024 ** 3
+    assert g["TFLOPs_median"] > 0 and 0 < g["frac_of_2500TFLOPs"] < 1
+

@@ -4,8 +4,8 @@ One step = one pass of the whole path over one batch of synthetic logits:
 dv_verify_rows (the fused verify pass), the decisions, and the seed score with
 its per-sequence selection. The decisions and the seed selection are independent
 and go in one call, dv_decide_seed_select (one launch); at workload 3 the
-decisions re-verify the selected seeds, so dv_seed_select runs first and
-dv_decide after it; workload 5 ranks by KL (dv_decide, dv_seed_score,
+decisions re-verify the selected seeds, which dv_seed_select_decide does in the
+selection's own launch; workload 5 ranks by KL (dv_decide, dv_seed_score,
 dv_select_topk). The default workload is the SPOT-style tree of 64 candidate
 block states x 32 positions over a 151 936-token vocabulary, bf16, T = 1,
 noise shared per position (coupled-noise acceptance per candidate).
@@ -418,10 +418,11 @@ def main() -> int:
             # the seed score and its selection are one call, except at workload 5, which ranks by KL
             u2 = got["entropy"].view(nseq, seq_len)
             if w.n_committed:
-                calls = [dv.prepare_seed_select(u2, d_in, d_out, committed, bf["score"], k, bf["idx"], bf["val"],
-                                                bf["cnt"], select_eligible=committed, mask=bf["mask"]),
-                         dv.prepare_decide("COVER", got, bf["decision"], bf["out_tok"], rows=R,
-                                           conf_thr=w.conf_thr, subject=bf["mask"].view(-1))]
+                # COVER: the top seeds among committed positions are re-verified, in the selection's launch
+                calls = [dv.prepare_seed_select_decide(
+                    dv.prepare_seed_select(u2, d_in, d_out, committed, bf["score"], k, bf["idx"], bf["val"],
+                                           bf["cnt"], select_eligible=committed, mask=bf["mask"]),
+                    dv.prepare_decide("COVER", got, bf["decision"], bf["out_tok"], rows=R, conf_thr=w.conf_thr))]
             else:
                 if w.group_len:
                     dec = dv.prepare_decide("COUPLED_ACCEPT", got, bf["decision"], bf["out_tok"], rows=R,
@@ -466,9 +467,9 @@ def main() -> int:
         u2 = got["entropy"].view(nseq, seq_len)
         if w.n_committed:
             # COVER: the top seeds among committed positions are re-verified (KEEP / REPLACE / REMASK)
-            _, _, _, _, mask = dv.dv_seed_select(u2, di, do, k, seed_eligible=committed, select_eligible=committed,
-                                                 want_mask=True)
-            dv.dv_decide("COVER", got, conf_thr=w.conf_thr, mask_token=-1, subject=mask.view(-1))
+            dv.dv_seed_select_decide(dict(u=u2, d_in=di, d_out=do, k=k, seed_eligible=committed,
+                                          select_eligible=committed),
+                                     dict(rule="COVER", stats=got, conf_thr=w.conf_thr, mask_token=-1))
             return
         if tree is not None:
             dv.dv_tree_accept(*tree, got["conf"], got["tok_v"])
@@ -521,7 +522,7 @@ def main() -> int:
         cpu = cpu_baselines(w, a_rows, b_rows, pos, dev, workers, host_cores)
 
     step_calls = ("dv_decide + dv_seed_score + dv_select_topk" if w.number == 5 else
-                  "dv_seed_select + dv_decide" if w.n_committed else
+                  "dv_seed_select_decide" if w.n_committed else
                   "dv_tree_accept + dv_seed_select" if tree is not None else "dv_decide_seed_select")
     line = {
         "metric": "verified rows/s and achieved HBM GB/s (% of peak), fused verify kernel",

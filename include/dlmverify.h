@@ -311,6 +311,29 @@ dv_status dv_decide_seed_select(const dv_decide_args *a, const dv_row_stats *sta
                                 int32_t *out_idx, float *out_val, int32_t *out_count, uint8_t *out_mask,
                                 hipStream_t stream);
 
+/* COVER's seed step in one launch ([COVER] §2: the top-scoring positions by
+ * the Score equation become the seeds; §3: the seeds are re-verified, KEEP,
+ * REPLACE or REMASK): dv_seed_select, then dv_decide over the same rows with
+ * the selection as its subject. Arguments: dv_seed_select's (nseq .. out_mask;
+ * out_mask is required here), then dv_decide's without subject, prefix_len and
+ * best_group (a, stats, cur_tok, decision, out_tok), then the stream. The
+ * outputs are those of dv_seed_select(...) followed by dv_decide(a, stats,
+ * out_mask, cur_tok, decision, out_tok, NULL, NULL): rows not selected get
+ * DV_NONE and keep their current token. a->rows must be nseq * seq_len, and
+ * the rule one of single rows (not COUPLED_ACCEPT). No buffer that one part
+ * writes may overlap one the other reads or writes. One launch up to 2048
+ * positions per sequence (the selection's workgroups decide their own
+ * positions); longer sequences take the selection's launches and then the
+ * decisions'. Errors: those of dv_seed_select; DV_ERR_NULL (out_mask NULL);
+ * those of dv_decide; DV_ERR_SHAPE (a->rows != nseq * seq_len); DV_ERR_ARG
+ * (COUPLED_ACCEPT, or shared memory). Nothing is launched when a check fails. */
+dv_status dv_seed_select_decide(int64_t nseq, int64_t seq_len, const float *u, const float *d_in, const float *d_out,
+                                const uint8_t *seed_eligible, float *score, const uint8_t *select_eligible,
+                                int32_t k, int32_t largest, int32_t use_thr, float thr, int32_t *out_idx,
+                                float *out_val, int32_t *out_count, uint8_t *out_mask, const dv_decide_args *a,
+                                const dv_row_stats *stats, const int32_t *cur_tok, uint8_t *decision,
+                                int32_t *out_tok, hipStream_t stream);
+
 /* Shape of dv_tree_accept's input: ntrees independent trees of `nodes` nodes
  * each over blocks of `block_len` positions. */
 typedef struct dv_tree_args {

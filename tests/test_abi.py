@@ -30,7 +30,7 @@ def _declared_functions():
 def test_exports_every_declared_function(lib):
     names = _declared_functions()
     assert names == sorted(["dv_verify_workspace_bytes", "dv_verify_rows", "dv_verify_rows_noalloc", "dv_decide", "dv_seed_score",
-                           "dv_select_topk", "dv_seed_select", "dv_decide_seed_select", "dv_tree_accept", "dv_influence_drift_workspace_bytes",
+                           "dv_select_topk", "dv_seed_select", "dv_decide_seed_select", "dv_seed_select_decide", "dv_tree_accept", "dv_influence_drift_workspace_bytes",
                            "dv_influence_drift", "dv_dual_view_attention", "dv_debug_hash", "dv_debug_noise", "dv_debug_read_probe", "dv_status_str",
                            "dv_last_error", "dv_version"])
     for n in names:
@@ -217,6 +217,32 @@ def test_decide_seed_select_validation(lib):
     # nothing to do in either: nothing launched (empty ranges overlap nothing)
     assert call(rows=0, nseq=0) == B.DV_OK
     assert call(rows=0, nseq=0, subject=buf(13)) == B.DV_OK
+
+
+def test_seed_select_decide_validation(lib):
+    """dv_seed_select_decide checks the selection, its mask, the decisions, their shape and rule, and that
+    neither part writes what the other touches, before anything is launched."""
+    f = lib.dv_seed_select_decide
+    buf = lambda i: (1 << 32) + i * (1 << 24)
+    st = B.dv_row_stats(kl=buf(0), conf=buf(1), tok_v=buf(2), tok_d=buf(3))
+
+    def call(rule=B.DV_RULE_COVER, rows=128, nseq=2, L=64, k=4, score=buf(9), mask=buf(13), decision=buf(4),
+             out_tok=buf(5), cur=None, idx=buf(10), group_len=0):
+        a = B.dv_decide_args(rule=rule, tau_kl=0.1, conf_thr=0.9, mask_token=-1, rows=rows, group_len=group_len)
+        return f(nseq, L, buf(6), buf(7), buf(8), None, score, None, k, 1, 0, 0.0, idx, buf(11), buf(12), mask,
+                 ctypes.byref(a), ctypes.byref(st), cur, decision, out_tok, None)
+
+    assert call(k=0) == B.DV_ERR_ARG                              # the selection's checks first
+    assert call(mask=None) == B.DV_ERR_NULL                      # the mask is the decisions' subject
+    assert call(rule=99) == B.DV_ERR_ARG                         # then the decisions'
+    assert call(rows=100) == B.DV_ERR_SHAPE                      # rows = nseq * seq_len
+    assert call(rule=B.DV_RULE_COUPLED_ACCEPT) == B.DV_ERR_SHAPE  # (dv_decide's own check: no groups)
+    assert call(rule=B.DV_RULE_COUPLED_ACCEPT, group_len=64) == B.DV_ERR_ARG  # a rule of single rows
+    assert call(decision=buf(13) + 3) == B.DV_ERR_ARG            # a decision output on the mask
+    assert call(out_tok=buf(8)) == B.DV_ERR_ARG                  # ... on a selection input
+    assert call(score=buf(1) + 16) == B.DV_ERR_ARG               # a selection output on conf
+    assert call(idx=buf(3)) == B.DV_ERR_ARG                      # ... on the current tokens (tok_d)
+    assert call(nseq=0, rows=0) == B.DV_OK                       # nothing to do: nothing launched
 
 
 def test_debug_noise_validation(lib):

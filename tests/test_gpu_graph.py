@@ -1,5 +1,6 @@
 """The whole path under HIP graph capture: dv_verify_rows (with its noise table),
-dv_decide, dv_seed_score, dv_select_topk, dv_seed_select and dv_decide_seed_select allocate nothing and clear nothing
+dv_decide, dv_seed_score, dv_select_topk, dv_seed_select, dv_decide_seed_select and
+dv_seed_select_decide allocate nothing and clear nothing
 with memset, so a captured step replays to the eager results, replay after
 replay, with other work and synchronisations in between."""
 
@@ -27,9 +28,15 @@ def _step(a, b, w, out, ws, d_in, d_out, bufs):
         dict(rule="COUPLED_ACCEPT", stats=got, mask_token=-1, group_len=w.group_len, want_prefix=True, want_best=True),
         dict(u=got["entropy"].view(-1, w.group_len), d_in=d_in.view(-1, w.group_len),
              d_out=d_out.view(-1, w.group_len), k=8))
+    # COVER's seed step: the selection, then the decisions over its seeds, in one launch
+    (_, _, _, _, mask4), (d4, o4) = dv.dv_seed_select_decide(
+        dict(u=got["entropy"].view(-1, w.group_len), d_in=d_in.view(-1, w.group_len),
+             d_out=d_out.view(-1, w.group_len), k=8),
+        dict(rule="COVER", stats=got, conf_thr=0.9, mask_token=-1))
     for k, v in (("d", d), ("o", o), ("pre", pre), ("best", best), ("idx", idx), ("val", val), ("cnt", cnt),
                  ("score2", score2), ("idx2", idx2), ("val2", val2), ("cnt2", cnt2), ("d3", d3), ("o3", o3),
-                 ("pre3", pre3), ("best3", best3), ("score3", score3), ("idx3", idx3), ("cnt3", cnt3)):
+                 ("pre3", pre3), ("best3", best3), ("score3", score3), ("idx3", idx3), ("cnt3", cnt3),
+                 ("mask4", mask4), ("d4", d4), ("o4", o4)):
         bufs[k] = v
     return bufs
 

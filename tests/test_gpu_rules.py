@@ -297,6 +297,64 @@ def test_decide_seed_select_matches_two_calls(rule, rows, group_len, prefix, bes
                 dv.prepare_decide_seed_select(pd2, ps)()
 
 
+@pytest.mark.parametrize("rule,nseq,L", [("COVER", 1, 512), ("COVER", 3, 2048), ("KL_OR_CONF", 64, 32),
+                                          ("CONF_DRAFT", 2, 100), ("KL_STOCHASTIC", 2, 64), ("TRUST", 1, 1),
+                                          ("COVER", 2, 4096)])
+def test_seed_select_decide_matches_two_calls(rule, nseq, L):
+    """dv_seed_select_decide gives, output for output and bit for bit, dv_seed_select followed by dv_decide with
+    the selection's mask as the subject (one launch up to 2048 positions, the two calls' launches beyond)."""
+    print(f"case: seed select + decide {rule} nseq={nseq} L={L}", flush=True)
+    dev = _dev()
+    rows = nseq * L
+    rng = np.random.default_rng(31 * L + nseq)
+    st = dict(kl=rng.uniform(0, 0.2, rows).astype(np.float32), conf=rng.uniform(0, 1, rows).astype(np.float32),
+              tok_v=rng.integers(0, 3, rows).astype(np.int32), tok_d=rng.integers(0, 3, rows).astype(np.int32),
+              p_tok_d=rng.uniform(0, 1, rows).astype(np.float32))
+    st["conf"][::13] = np.float32(0.9)
+    gst = {k: _t(v, dev) for k, v in st.items()}
+    u = _t(rng.uniform(0, 4, (nseq, L)).round(1).astype(np.float32), dev)
+    d_in = _t(rng.uniform(0, 1, (nseq, L)).astype(np.float32), dev)
+    d_out = _t(rng.uniform(0, 1, (nseq, L)).astype(np.float32), dev)
+    committed = _t((rng.random((nseq, L)) < 0.7).astype(np.uint8), dev)
+    k = max(1, min(L, L // 10))
+    bits = lambda x: (x.contiguous().view(torch.int32) if x.dtype == torch.float32 else x).cpu().numpy()
+    for use_cur in (False, True):
+        cur = _t(rng.integers(0, 3, rows).astype(np.int32), dev) if use_cur else None
+        skw = dict(u=u, d_in=d_in, d_out=d_out, k=k, seed_eligible=committed, select_eligible=committed)
+        dkw = dict(rule=rule, stats=gst, tau_kl=0.1, conf_thr=0.9, mask_token=-9, cur_tok=cur, seed=11,
+                   pos_period=L)
+        (score, idx, val, cnt, mask), (d, o) = dv.dv_seed_select_decide(skw, dkw)
+        rscore, ridx, rval, rcnt, rmask = dv.dv_seed_select(u, d_in, d_out, k, seed_eligible=committed,
+                                                            select_eligible=committed, want_mask=True)
+        rd, ro, _, _ = dv.dv_decide(rule, gst, tau_kl=0.1, conf_thr=0.9, mask_token=-9, cur_tok=cur, seed=11,
+                                    pos_period=L, subject=rmask.view(-1))
+        for name, x, y in (("score", score, rscore), ("idx", idx, ridx), ("val", val, rval), ("cnt", cnt, rcnt),
+                           ("mask", mask, rmask), ("decision", d, rd), ("out_tok", o, ro)):
+            np.testing.assert_array_equal(bits(x), bits(y), err_msg=f"{name} cur={use_cur}")
+        # the rows not selected are left undecided with their current token
+        m = mask.view(-1).cpu().numpy().astype(bool)
+        assert (d.cpu().numpy()[~m] == dv.DV_NONE).all()
+    # the prepared form on fixed buffers
+    bs = dict(score=torch.empty((nseq, L), dtype=torch.float32, device=dev),
+              idx=torch.empty((nseq, k), dtype=torch.int32, device=dev),
+              val=torch.empty((nseq, k), dtype=torch.float32, device=dev),
+              cnt=torch.empty(nseq, dtype=torch.int32, device=dev),
+              mask=torch.empty((nseq, L), dtype=torch.uint8, device=dev),
+              decision=torch.empty(rows, dtype=torch.uint8, device=dev),
+              out_tok=torch.empty(rows, dtype=torch.int32, device=dev))
+    ps = dv.prepare_seed_select(u, d_in, d_out, committed, bs["score"], k, bs["idx"], bs["val"], bs["cnt"],
+                                select_eligible=committed, mask=bs["mask"])
+    pd = dv.prepare_decide(rule, gst, bs["decision"], bs["out_tok"], rows=rows, tau_kl=0.1, conf_thr=0.9,
+                           mask_token=-9)
+    dv.prepare_seed_select_decide(ps, pd)()
+    # the prepared decision has no current-token array and seed 0, positions r
+    pd_ref, po_ref, _, _ = dv.dv_decide(rule, gst, tau_kl=0.1, conf_thr=0.9, mask_token=-9, subject=rmask.view(-1))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(bs["mask"]), bits(rmask))
+    np.testing.assert_array_equal(bits(bs["decision"]), bits(pd_ref))
+    np.testing.assert_array_equal(bits(bs["out_tok"]), bits(po_ref))
+
+
 def test_workload_tiny_rules_chain():
     w = W.workload(1)
     print(f"case: workload 1 chain ({w.name})", flush=True)

@@ -421,6 +421,33 @@ Span span_of(const void *p, int64_t n, size_t elem) {
 bool overlap(const Span &x, const Span &y) {
   return x.bytes && y.bytes && x.lo < y.lo + y.bytes && y.lo < x.lo + x.bytes;
 }
+
+// A decision and a seed selection that run in one launch: no buffer one of them writes may be
+// one the other reads or writes (the decisions' inputs as the rule reads them).
+dv_status check_no_shared_writes(const dv::DecideLaunch &pd, const dv::SelectLaunch &ps) {
+  const int64_t R = pd.rows, n = ps.nseq * ps.seq_len, ng = pd.group_len > 0 ? R / pd.group_len : 0;
+  const int32_t *tok_d_read = pd.cur_tok ? nullptr : pd.tok_d;
+  const Span d_in_spans[] = {span_of(pd.kl, R, 4), span_of(pd.conf, R, 4), span_of(pd.p_tok, R, 4),
+                             span_of(pd.tok_v, R, 4), span_of(tok_d_read, R, 4), span_of(pd.subject, R, 1),
+                             span_of(pd.cur_tok, R, 4), span_of(pd.pos, R, 4)};
+  const Span d_out_spans[] = {span_of(pd.decision, R, 1), span_of(pd.out_tok, R, 4), span_of(pd.prefix_len, ng, 4),
+                              span_of(pd.best_group, 1, 4)};
+  const Span s_in_spans[] = {span_of(ps.u, n, 4), span_of(ps.d_in, n, 4), span_of(ps.d_out, n, 4),
+                             span_of(ps.seed_eligible, n, 1), span_of(ps.eligible, n, 1)};
+  const Span s_out_spans[] = {span_of(ps.score_out, n, 4), span_of(ps.out_idx, ps.nseq * ps.k, 4),
+                              span_of(ps.out_val, ps.nseq * ps.k, 4), span_of(ps.out_count, ps.nseq, 4),
+                              span_of(ps.out_mask, n, 1)};
+  for (const Span &x : d_out_spans) {
+    for (const Span &y : s_in_spans)
+      if (overlap(x, y)) return fail(DV_ERR_ARG, "a decision output overlaps a seed-selection input");
+    for (const Span &y : s_out_spans)
+      if (overlap(x, y)) return fail(DV_ERR_ARG, "a decision output overlaps a seed-selection output");
+  }
+  for (const Span &x : s_out_spans)
+    for (const Span &y : d_in_spans)
+      if (overlap(x, y)) return fail(DV_ERR_ARG, "a seed-selection output overlaps a decision input");
+  return ok();
+}
 }  // namespace
 
 dv_status dv_decide_seed_select(const dv_decide_args *a, const dv_row_stats *stats, const uint8_t *subject,
@@ -438,28 +465,32 @@ dv_status dv_decide_seed_select(const dv_decide_args *a, const dv_row_stats *sta
   s = seed_select_launch_of(nseq, seq_len, u, d_in, d_out, seed_eligible, score, select_eligible, k, largest, use_thr,
                             thr, out_idx, out_val, out_count, out_mask, ps);
   if (s != DV_OK) return s;
-  // The two run together: no buffer one of them writes may be one the other reads or writes.
-  const int64_t R = a->rows, n = nseq * seq_len, ng = a->group_len > 0 ? R / a->group_len : 0;
-  const int32_t *tok_d_read = cur_tok ? nullptr : stats->tok_d;
-  const Span d_in_spans[] = {span_of(pd.kl, R, 4), span_of(pd.conf, R, 4), span_of(pd.p_tok, R, 4),
-                             span_of(pd.tok_v, R, 4), span_of(tok_d_read, R, 4), span_of(subject, R, 1),
-                             span_of(cur_tok, R, 4), span_of(pd.pos, R, 4)};
-  const Span d_out_spans[] = {span_of(decision, R, 1), span_of(out_tok, R, 4), span_of(prefix_len, ng, 4),
-                              span_of(best_group, 1, 4)};
-  const Span s_in_spans[] = {span_of(u, n, 4), span_of(d_in, n, 4), span_of(d_out, n, 4),
-                             span_of(seed_eligible, n, 1), span_of(select_eligible, n, 1)};
-  const Span s_out_spans[] = {span_of(score, n, 4), span_of(out_idx, nseq * k, 4), span_of(out_val, nseq * k, 4),
-                              span_of(out_count, nseq, 4), span_of(out_mask, n, 1)};
-  for (const Span &x : d_out_spans) {
-    for (const Span &y : s_in_spans)
-      if (overlap(x, y)) return fail(DV_ERR_ARG, "a decision output overlaps a seed-selection input");
-    for (const Span &y : s_out_spans)
-      if (overlap(x, y)) return fail(DV_ERR_ARG, "a decision output overlaps a seed-selection output");
-  }
-  for (const Span &x : s_out_spans)
-    for (const Span &y : d_in_spans)
-      if (overlap(x, y)) return fail(DV_ERR_ARG, "a seed-selection output overlaps a decision input");
+  s = check_no_shared_writes(pd, ps);
+  if (s != DV_OK) return s;
   return hip_status(dv::launch_decide_seed_select(pd, decide, ps, stream), "dv_decide_seed_select launch");
+}
+
+dv_status dv_seed_select_decide(int64_t nseq, int64_t seq_len, const float *u, const float *d_in, const float *d_out,
+                                const uint8_t *seed_eligible, float *score, const uint8_t *select_eligible, int32_t k,
+                                int32_t largest, int32_t use_thr, float thr, int32_t *out_idx, float *out_val,
+                                int32_t *out_count, uint8_t *out_mask, const dv_decide_args *a,
+                                const dv_row_stats *stats, const int32_t *cur_tok, uint8_t *decision,
+                                int32_t *out_tok, hipStream_t stream) {
+  dv::SelectLaunch ps;
+  dv_status s = seed_select_launch_of(nseq, seq_len, u, d_in, d_out, seed_eligible, score, select_eligible, k, largest,
+                                      use_thr, thr, out_idx, out_val, out_count, out_mask, ps);
+  if (s != DV_OK) return s;
+  if (!out_mask) return fail(DV_ERR_NULL, "out_mask is required: the selection is the decisions' subject");
+  dv::DecideLaunch pd;
+  bool decide;
+  s = decide_launch_of(a, stats, nullptr, cur_tok, decision, out_tok, nullptr, nullptr, pd, decide);
+  if (s != DV_OK) return s;
+  if (a->rows != nseq * seq_len) return fail(DV_ERR_SHAPE, "the decisions' rows must be nseq * seq_len");
+  if (a->rule == DV_RULE_COUPLED_ACCEPT)
+    return fail(DV_ERR_ARG, "the decisions over the selected seeds take a rule of single rows");
+  s = check_no_shared_writes(pd, ps);
+  if (s != DV_OK) return s;
+  return hip_status(dv::launch_seed_select_decide(ps, pd, stream), "dv_seed_select_decide launch");
 }
 
 dv_status dv_influence_drift_workspace_bytes(const dv_attention *att, size_t *bytes) {

@@ -137,6 +137,8 @@ hipError_t launch_select_topk(const SelectLaunch &p, hipStream_t stream);
 hipError_t launch_seed_select(const SelectLaunch &p, hipStream_t stream);
 // dv_decide (when decide is set) and dv_seed_select, fused into one launch where both fit it
 hipError_t launch_decide_seed_select(const DecideLaunch &d, bool decide, const SelectLaunch &s, hipStream_t stream);
+// dv_seed_select, then dv_decide with the selection's mask (s.out_mask, required) as the subject
+hipError_t launch_seed_select_decide(const SelectLaunch &s, const DecideLaunch &d, hipStream_t stream);
 
 constexpr int kMaxTreeNodes = 1024;
 constexpr int kMaxTreeBlockLen = 1024;

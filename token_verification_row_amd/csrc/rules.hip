@@ -330,6 +330,49 @@ __global__ __launch_bounds__(256) void seed_score_kernel(int64_t rows, const flo
   score[r] = s;
 }
 
+// A row's inputs to the row rules, loaded together: every pointer the rule may read is
+// replaced, when the call left it NULL, by the current-token array (always given), so that
+// no load sits behind a branch and none waits for another. The rule then reads only the
+// fields the call checked it gives.
+struct RowVals {
+  float kl, conf, p_tok;
+  int32_t tok_v, cur;
+};
+__device__ __forceinline__ RowVals load_row_vals(const DecideLaunch &p, int64_t r) {
+  const int32_t *ctok = p.cur_tok ? p.cur_tok : p.tok_d;
+  const float *any = reinterpret_cast<const float *>(ctok);
+  RowVals v;
+  v.cur = ctok[r];
+  v.kl = (p.kl ? p.kl : any)[r];
+  v.conf = (p.conf ? p.conf : any)[r];
+  v.p_tok = (p.p_tok ? p.p_tok : any)[r];
+  v.tok_v = (p.tok_v ? p.tok_v : ctok)[r];
+  return v;
+}
+
+// rule_of_row on loaded values.
+__device__ __forceinline__ uint8_t rule_of_vals(const DecideLaunch &p, int64_t r, const RowVals &v) {
+  switch (p.rule) {
+    case DV_RULE_TRUST:
+      return DV_KEEP;
+    case DV_RULE_KL:
+      return v.kl > p.tau_kl ? DV_REMASK : DV_KEEP;
+    case DV_RULE_CONF:
+      return v.conf < p.conf_thr ? DV_REMASK : DV_KEEP;
+    case DV_RULE_KL_OR_CONF:
+      return (v.kl > p.tau_kl || v.conf < p.conf_thr) ? DV_REMASK : DV_KEEP;
+    case DV_RULE_COVER:
+      if (v.tok_v == v.cur) return DV_KEEP;
+      return v.conf >= p.conf_thr ? DV_REPLACE : DV_REMASK;
+    case DV_RULE_CONF_DRAFT:
+      return v.p_tok < p.conf_thr ? DV_REMASK : DV_KEEP;
+    case DV_RULE_KL_STOCHASTIC:
+      return __fmul_rn(remask_uniform(p, r), p.tau_kl) < v.kl ? DV_REMASK : DV_KEEP;
+    default:
+      return DV_NONE;
+  }
+}
+
 // --------------------------------------------------------------- top-k ----
 // Keys sort descending: the upper word orders the scores (largest or smallest
 // first), the lower word is ~index so that equal scores go to the lower index.
@@ -356,7 +399,12 @@ __device__ __forceinline__ unsigned long long select_key(float s, uint32_t i, in
 constexpr int32_t kRankMaxLen = 2048;
 constexpr int kRankThreads = 256;
 // The workgroup of sequence seq and positions [64 by, 64 by + 64) (kRankThreads threads).
-__device__ __forceinline__ void select_rank_block(const SelectLaunch &p, int64_t seq, int32_t by) {
+// DECIDE: then the decisions d over the same rows with the selection as their subject:
+// wave 0 evaluates d's row rule at each selected position of its 64 (the row's inputs are
+// loaded at the start, beside the selection's) and DV_NONE elsewhere.
+template <bool DECIDE>
+__device__ __forceinline__ void select_rank_block(const SelectLaunch &p, int64_t seq, int32_t by,
+                                                  const DecideLaunch &d) {
   constexpr int kPer = kRankMaxLen / kRankThreads;  // keys built per thread, at most
   __shared__ unsigned long long keys[kRankMaxLen];
   __shared__ float vals[kRankMaxLen];
@@ -369,6 +417,9 @@ __device__ __forceinline__ void select_rank_block(const SelectLaunch &p, int64_t
   // the threshold's key without its index word: a score is kept iff its key's upper word is above it
   const uint32_t thr_ord = static_cast<uint32_t>(select_key(p.thr, 0u, p.largest) >> 32);
   // loads at clamped (always valid) positions, all issued before the first is used
+  const int32_t i = by * 64 + lane;
+  RowVals rv{};
+  if (DECIDE && wave == 0) rv = load_row_vals(d, seq * p.seq_len + min(i, L - 1));
   float v[kPer];
   uint32_t e[kPer];
   if (el) {
@@ -426,7 +477,6 @@ __device__ __forceinline__ void select_rank_block(const SelectLaunch &p, int64_t
   if (lane == 0) wave_kept[wave] = kept;
   __syncthreads();
   const int32_t count = min(p.k, wave_kept[0] + wave_kept[1] + wave_kept[2] + wave_kept[3]);
-  const int32_t i = by * 64 + lane;
   const unsigned long long ki = i < L ? keys[i] : 0ull;
   const int32_t q = (L + 3) / 4, j0 = wave * q, j1 = min(L, j0 + q);
   int32_t r = 0;
@@ -449,10 +499,23 @@ __device__ __forceinline__ void select_rank_block(const SelectLaunch &p, int64_t
     }
     if (lane == 0 && p.out_count) p.out_count[seq] = count;
   }
+  if constexpr (DECIDE) {
+    if (i < L) {
+      const int64_t r = seq * p.seq_len + i;
+      const uint8_t dr = sel ? rule_of_vals(d, r, rv) : DV_NONE;
+      if (d.decision) d.decision[r] = dr;
+      if (d.out_tok) d.out_tok[r] = dr == DV_REPLACE ? rv.tok_v : (dr == DV_REMASK ? d.mask_token : rv.cur);
+    }
+  }
 }
 
 __global__ __launch_bounds__(kRankThreads) void select_rank_kernel(SelectLaunch p) {
-  select_rank_block(p, blockIdx.x, static_cast<int32_t>(blockIdx.y));
+  select_rank_block<false>(p, blockIdx.x, static_cast<int32_t>(blockIdx.y), DecideLaunch{});
+}
+
+// dv_seed_select_decide: the selection, then the decisions over its seeds, in one launch.
+__global__ __launch_bounds__(kRankThreads) void select_decide_kernel(SelectLaunch p, DecideLaunch d) {
+  select_rank_block<true>(p, blockIdx.x, static_cast<int32_t>(blockIdx.y), d);
 }
 
 // Longer sequences: one workgroup per sequence, bitonic sort of pow2 keys in LDS.
@@ -534,7 +597,7 @@ __global__ __launch_bounds__(kRankThreads) void decide_select_kernel(DecideLaunc
       decide_group(d, static_cast<int64_t>(b) * (kRankThreads / 64) + (threadIdx.x >> 6), threadIdx.x & 63);
     return;
   }
-  select_rank_block(s, (b - nd) / ny, static_cast<int32_t>((b - nd) % ny));
+  select_rank_block<false>(s, (b - nd) / ny, static_cast<int32_t>((b - nd) % ny), d);
 }
 
 // ------------------------------------------------------------- noise dump ----
@@ -605,6 +668,21 @@ hipError_t launch_decide_seed_select(const DecideLaunch &d, bool decide, const S
     if (e != hipSuccess) return e;
   }
   return launch_seed_select(s, stream);
+}
+
+hipError_t launch_seed_select_decide(const SelectLaunch &s, const DecideLaunch &d, hipStream_t stream) {
+  if (s.nseq == 0) return hipSuccess;
+  if (s.seq_len <= kRankMaxLen) {
+    const dim3 grid(static_cast<unsigned>(s.nseq), static_cast<unsigned>((s.seq_len + 63) / 64));
+    hipLaunchKernelGGL(select_decide_kernel, grid, dim3(kRankThreads), 0, stream, s, d);
+    return hipGetLastError();
+  }
+  // longer sequences: the selection's own launches, then the decisions with its mask as their subject
+  const hipError_t e = launch_seed_select(s, stream);
+  if (e != hipSuccess) return e;
+  DecideLaunch q = d;
+  q.subject = s.out_mask;
+  return launch_decide(q, stream);
 }
 
 hipError_t launch_select_topk(const SelectLaunch &p, hipStream_t stream) {

@@ -99,6 +99,9 @@ _SIGNATURES = {
     "dv_decide_seed_select": (ctypes.c_int, [ctypes.POINTER(dv_decide_args), ctypes.POINTER(dv_row_stats)] + [_P] * 6 +
                               [ctypes.c_int64, ctypes.c_int64] + [_P] * 6 +
                               [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float] + [_P] * 5),
+    "dv_seed_select_decide": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64] + [_P] * 6 +
+                              [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float] + [_P] * 4 +
+                              [ctypes.POINTER(dv_decide_args), ctypes.POINTER(dv_row_stats)] + [_P] * 4),
     "dv_tree_accept": (ctypes.c_int, [ctypes.POINTER(dv_tree_args)] + [_P] * 15),
     "dv_dual_view_attention": (ctypes.c_int, [ctypes.POINTER(dv_dual_view_args)] + [_P] * 8),
     "dv_influence_drift_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(dv_attention), ctypes.POINTER(ctypes.c_size_t)]),
@@ -515,6 +518,38 @@ def dv_seed_select(u, d_in, d_out, k, **kw):
     cargs, outs, dev = _seed_select_call(u, d_in, d_out, k, **kw)
     _check(load_library().dv_seed_select(*cargs, _stream_handle(dev)), "dv_seed_select")
     return outs
+
+
+def dv_seed_select_decide(seed_select: dict, decide: dict):
+    """COVER's seed step: dv_seed_select, then dv_decide over the same rows with the selected seeds as its
+    subject, in one launch up to 2048 positions per sequence. ``seed_select`` holds dv_seed_select's arguments
+    by name (u, d_in, d_out, k and its keywords; the mask is always produced), ``decide`` dv_decide's (rule,
+    stats, and tau_kl, conf_thr, mask_token, cur_tok, seed, pos, pos_period; no subject, group_len, prefix or
+    best). Returns (dv_seed_select's outputs, (decision, out_tok))."""
+    sargs, souts, dev = _seed_select_call(**{**seed_select, "want_mask": True})
+    for key in ("subject", "group_len", "want_prefix", "want_best"):
+        if decide.get(key):
+            raise ValueError(f"the decisions over the selected seeds take no {key}")
+    dargs, douts, ddev = _decide_call(**decide)
+    if ddev != dev:
+        raise ValueError("the selection and the decisions must be on one device")
+    args, st, _subject, cur, decision, out_tok, _prefix, _best = dargs
+    _check(load_library().dv_seed_select_decide(*sargs, args, st, cur, decision, out_tok, _stream_handle(dev)),
+           "dv_seed_select_decide")
+    return souts, douts[:2]
+
+
+def prepare_seed_select_decide(seed_select: Prepared, decide: Prepared) -> Prepared:
+    """A prepared dv_seed_select (with its mask) and a prepared dv_decide (no subject, prefix or best) as one
+    dv_seed_select_decide call."""
+    if seed_select._name != "dv_seed_select" or decide._name != "dv_decide":
+        raise TypeError("expects a prepared dv_seed_select and a prepared dv_decide")
+    if decide._args[-1] != seed_select._args[-1]:
+        raise ValueError("the two calls must use one stream")
+    a, st, subject, cur, decision, out_tok, prefix, best, stream = decide._args
+    if subject is not None or prefix is not None or best is not None:
+        raise ValueError("the decisions over the selected seeds take no subject, prefix or best")
+    return Prepared("dv_seed_select_decide", *seed_select._args[:-1], a, st, cur, decision, out_tok, stream)
 
 
 def dv_decide_seed_select(decide: dict, seed_select: dict):

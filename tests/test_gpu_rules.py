@@ -432,6 +432,16 @@ def test_workload_cover_chain_full_size():
     gd, go = _oracle_decide(dv.RULES["COVER"], g, 0.0, w.conf_thr, -1, m)
     np.testing.assert_array_equal(d.cpu().numpy(), gd)
     np.testing.assert_array_equal(o.cpu().numpy(), go)
+    # the same step in one launch (the benchmark's): the same selection and decisions
+    (_, fidx, _, _, fmask), (fd, fo) = dv.dv_seed_select_decide(
+        dict(u=got["entropy"].view(w.B, w.L), d_in=_t(d_in, dev).view(w.B, w.L), d_out=_t(d_out, dev).view(w.B, w.L),
+             k=w.topk, seed_eligible=_t(committed, dev).view(w.B, w.L),
+             select_eligible=_t(committed, dev).view(w.B, w.L)),
+        dict(rule="COVER", stats=got, conf_thr=w.conf_thr, mask_token=-1))
+    np.testing.assert_array_equal(fidx.cpu().numpy(), ri)
+    np.testing.assert_array_equal(fmask.cpu().numpy().ravel(), m)
+    np.testing.assert_array_equal(fd.cpu().numpy(), gd)
+    np.testing.assert_array_equal(fo.cpu().numpy(), go)
     # against the oracle's own chain: seed score within tolerance, selection exact unless a near-tie
     ost = _oracle_stats_blocks(a_np, b_np, "bf16")
     np.testing.assert_allclose(g["entropy"], ost["entropy"], rtol=RTOL, atol=ATOL)
@@ -462,6 +472,16 @@ def test_workload_spot_tree_chain_full_size():
     rp = odecide.accepted_prefix(gd, w.group_len)
     np.testing.assert_array_equal(pre.cpu().numpy(), rp)
     assert int(best.cpu()[0]) == odecide.best_group(rp)
+    # the benchmark's one-launch form (decisions beside the seed selection): the same decisions and prefixes
+    d_in, d_out = torch.rand(w.rows, device=dev), torch.rand(w.rows, device=dev)
+    (fd, fo, fpre, fbest), _ = dv.dv_decide_seed_select(
+        dict(rule="COUPLED_ACCEPT", stats=got, mask_token=-1, group_len=w.group_len, want_prefix=True,
+             want_best=True),
+        dict(u=got["entropy"].view(w.B, w.L), d_in=d_in.view(w.B, w.L), d_out=d_out.view(w.B, w.L), k=8))
+    np.testing.assert_array_equal(fd.cpu().numpy(), gd)
+    np.testing.assert_array_equal(fo.cpu().numpy(), go)
+    np.testing.assert_array_equal(fpre.cpu().numpy(), rp)
+    assert int(fbest.cpu()[0]) == odecide.best_group(rp)
     # oracle tokens for three whole candidates give the same prefixes (unless a token is a near-tie)
     for c in (0, 17, 63):
         rows = np.arange(c * w.group_len, (c + 1) * w.group_len)
